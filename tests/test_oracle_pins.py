@@ -1,0 +1,449 @@
+"""Pins of the CPU oracle against facts outside itself (CPU only).
+
+Each test ties one oracle function to something the oracle does not compute
+the same way: brute force over every expert, a closed form (dense SwiGLU FFN,
+full softmax mixture), an exact-rational emulation of the fp32 fma chain,
+library sorts and softmax, permutation invariants, exact power-of-two
+identities, or central finite differences. A dropped term, a wrong sign, a
+swapped gate/up half, a transposed operand or an off-by-one index fails at
+least one of them.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+import workloads
+
+
+def _bf16(a: np.ndarray) -> np.ndarray:
+    """Round float data to bf16 (RNE) and return the bit patterns."""
+    return workloads.bf16_bits(torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16))
+
+
+def _val(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _silu(g):
+    return g / (1.0 + np.exp(-g))
+
+
+def _case(T, emb, mlp, E, k, seed, sigma=0.3):
+    rng = np.random.default_rng(seed)
+    x = _bf16(rng.standard_normal((T, emb)))
+    wr = (rng.standard_normal((emb, E)) * 0.3).astype(np.float32)
+    wi = _bf16(rng.standard_normal((E, emb, 2 * mlp)) * sigma)
+    wo = _bf16(rng.standard_normal((E, mlp, emb)) * sigma)
+    return x, wr, wi, wo
+
+
+def _dense_expert(xv, wiv, wov, e):
+    """Textbook SwiGLU FFN of expert e on all tokens, float64, gate = first half."""
+    mlp = wov.shape[1]
+    h = xv @ wiv[e]
+    return (_silu(h[:, :mlp]) * h[:, mlp:]) @ wov[e]
+
+
+# ---------------------------------------------------------------- full forward
+
+@pytest.mark.parametrize("shape", [(8, 16, 16, 4, 2), (64, 128, 256, 8, 2), (16, 32, 24, 6, 3)])
+def test_forward_matches_brute_force_dense_then_mask(shape):
+    """Every expert computed densely on every token, then masked by the routing."""
+    T, emb, mlp, E, k = shape
+    x, wr, wi, wo = _case(T, emb, mlp, E, k, seed=sum(shape))
+    idx, w, _ = oracle.route(x, wr, None, k)
+    xv, wiv, wov = _val(x), _val(wi), _val(wo)
+    dense = np.stack([_dense_expert(xv, wiv, wov, e) for e in range(E)])  # [E, T, emb]
+    want = np.zeros((T, emb))
+    for t in range(T):
+        for j in range(k):
+            want[t] += float(w[t, j]) * dense[idx[t, j], t]
+    got64 = oracle.ffn_fwd_tokens(x, idx, w, wi, wo, real="f64")
+    np.testing.assert_allclose(got64, want, rtol=1e-10, atol=1e-12)
+    got32 = oracle.ffn_fwd_tokens(x, idx, w, wi, wo, real="f32")
+    assert np.linalg.norm(got32 - want) / np.linalg.norm(want) < 1e-5
+
+
+def test_single_expert_is_dense_swiglu_ffn():
+    """E = 1, k = 1: weight exactly 1 and the layer is the dense FFN (silu(xWg) * xWu) Wo."""
+    x, wr, wi, wo = _case(12, 32, 40, 1, 1, seed=7)
+    idx, w, _ = oracle.route(x, wr, None, 1)
+    assert (idx == 0).all() and (w == 1.0).all()
+    xv, wiv, wov = _val(x), _val(wi), _val(wo)
+    g, u = xv @ wiv[0][:, :40], xv @ wiv[0][:, 40:]
+    want = (g * scipy.special.expit(g) * u) @ wov[0]
+    np.testing.assert_allclose(oracle.ffn_fwd_tokens(x, idx, w, wi, wo, real="f64"), want, rtol=1e-10, atol=1e-12)
+
+
+def test_all_experts_is_full_softmax_mixture():
+    """k = E: the renormalised weights are the full softmax, y = sum_e softmax(l)_e FFN_e(x)."""
+    T, emb, mlp, E = 10, 24, 16, 5
+    x, wr, wi, wo = _case(T, emb, mlp, E, E, seed=11)
+    idx, w, logits = oracle.route(x, wr, None, E)
+    p = scipy.special.softmax(logits.astype(np.float64), axis=1)
+    xv, wiv, wov = _val(x), _val(wi), _val(wo)
+    parts = [_dense_expert(xv, wiv, wov, e) for e in range(E)]
+    want = sum(p[:, e:e + 1] * parts[e] for e in range(E))
+    # the weights are stored as fp32: each carries a relative rounding of at most 2^-24
+    bound = 2.0 ** -24 * sum(p[:, e:e + 1] * np.abs(parts[e]) for e in range(E)) + 1e-12
+    got = oracle.ffn_fwd_tokens(x, idx, w, wi, wo, real="f64")
+    assert (np.abs(got - want) <= bound).all()
+
+
+def test_power_of_two_scaling_is_exact():
+    """y(2 wo) == 2 y(wo) bit for bit (scaling by 2 is exact in every operation)."""
+    x, wr, wi, wo = _case(16, 32, 32, 4, 2, seed=3)
+    idx, w, _ = oracle.route(x, wr, None, 2)
+    wo2 = _bf16(_val(wo) * 2.0)
+    y1 = oracle.ffn_fwd_tokens(x, idx, w, wi, wo)
+    y2 = oracle.ffn_fwd_tokens(x, idx, w, wi, wo2)
+    assert np.array_equal(y2, 2 * y1)
+
+
+def test_token_shuffle_shuffles_rows():
+    x, wr, wi, wo = _case(24, 32, 16, 6, 3, seed=5)
+    idx, w, _ = oracle.route(x, wr, None, 3)
+    y = oracle.ffn_fwd_tokens(x, idx, w, wi, wo)
+    perm = np.random.default_rng(0).permutation(24)
+    idx2, w2, _ = oracle.route(x[perm], wr, None, 3)
+    assert np.array_equal(idx2, idx[perm]) and np.array_equal(w2, w[perm])
+    assert np.array_equal(oracle.ffn_fwd_tokens(x[perm], idx2, w2, wi, wo), y[perm])
+
+
+def test_token_subset_and_thread_count_do_not_change_results():
+    x, wr, wi, wo = _case(40, 32, 16, 6, 2, seed=9)
+    idx, w, _ = oracle.route(x, wr, None, 2)
+    full = oracle.ffn_fwd_tokens(x, idx, w, wi, wo, threads=1)
+    sub = np.array([39, 0, 17, 17, 5])
+    assert np.array_equal(oracle.ffn_fwd_tokens(x, idx, w, wi, wo, tokens=sub, threads=3), full[sub])
+    assert np.array_equal(oracle.router_logits(x, wr, threads=1), oracle.router_logits(x, wr, threads=7))
+
+
+# ---------------------------------------------------------------- router
+
+def _round_f32(q: Fraction) -> float:
+    """Correctly rounded (nearest, ties to even) fp32 value of an exact rational."""
+    if q == 0:
+        return 0.0
+    sign = -1.0 if q < 0 else 1.0
+    q = abs(q)
+    e = q.numerator.bit_length() - q.denominator.bit_length()
+    if Fraction(2) ** e > q:
+        e -= 1
+    ulp = Fraction(2) ** (max(e, -126) - 23)
+    s = q / ulp
+    n = s.numerator // s.denominator
+    rem = s - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return sign * float(n * ulp)
+
+
+def test_router_logits_are_the_exact_fp32_fma_chain():
+    """Each logit equals the chain acc = fl32(x*w + acc) over emb ascending, emulated with exact rationals."""
+    T, emb, E = 3, 40, 5
+    rng = np.random.default_rng(1)
+    x = _bf16(rng.standard_normal((T, emb)))
+    wr = (rng.standard_normal((emb, E)) * 0.3).astype(np.float32)
+    bias = np.array([0.0, 2.0, -1.5, 0.25, 0.0], np.float32)
+    got = oracle.router_logits(x, wr, bias)
+    xv = _val(x)
+    for t in range(T):
+        for e in range(E):
+            acc = 0.0
+            for i in range(emb):
+                acc = _round_f32(Fraction(float(xv[t, i])) * Fraction(float(wr[i, e])) + Fraction(acc))
+            acc = _round_f32(Fraction(acc) + Fraction(float(bias[e])))
+            assert np.float32(acc) == got[t, e], (t, e)
+
+
+def test_router_logits_close_to_float64_matmul():
+    x, wr, _, _ = _case(50, 256, 8, 16, 2, seed=2)
+    got = oracle.router_logits(x, wr).astype(np.float64)
+    ref = _val(x) @ wr.astype(np.float64)
+    bound = 256 * 2.0 ** -24 * (np.abs(_val(x)) @ np.abs(wr.astype(np.float64)))
+    assert (np.abs(got - ref) <= bound + 1e-30).all()
+
+
+def test_topk_matches_stable_sort_and_softmax():
+    rng = np.random.default_rng(4)
+    logits = rng.standard_normal((200, 16)).astype(np.float32)
+    logits[:, 3] = logits[:, 7]  # plant ties
+    logits[::5, 11] = logits[::5, 2]
+    for k in (1, 2, 5, 16):
+        idx, w = oracle.topk(logits, k)
+        want = np.argsort(-logits, axis=1, kind="stable")[:, :k]
+        assert np.array_equal(idx, want)
+        picked = np.take_along_axis(logits, idx, 1).astype(np.float64)
+        np.testing.assert_allclose(w, scipy.special.softmax(picked, axis=1), rtol=0, atol=1e-7)
+        # renormalising the full softmax over the picks gives the same weights
+        full = scipy.special.softmax(logits.astype(np.float64), axis=1)
+        sel = np.take_along_axis(full, idx, 1)
+        np.testing.assert_allclose(w, sel / sel.sum(1, keepdims=True), rtol=0, atol=1e-7)
+
+
+def test_topk_crafted_cases():
+    # all equal -> experts 0..k-1 with weight exactly 1/k
+    idx, w = oracle.topk(np.full((3, 8), 0.7, np.float32), 4)
+    assert (idx == np.arange(4)).all() and (w == 0.25).all()
+    # +0 and -0 are equal: lower id first
+    idx, _ = oracle.topk(np.array([[-0.0, 0.0, -1.0, 0.0]], np.float32), 2)
+    assert idx.tolist() == [[0, 1]]
+    # -inf is never picked while finite logits remain, and is picked last (lowest id first) otherwise
+    l = np.array([[-np.inf, 1.0, -np.inf, 0.5]], np.float32)
+    idx, w = oracle.topk(l, 2)
+    assert idx.tolist() == [[1, 3]]
+    idx, w = oracle.topk(l, 3)
+    assert idx.tolist() == [[1, 3, 0]] and w[0, 2] == 0.0
+    # k = 1 -> weight exactly 1; k = E -> every expert once
+    _, w = oracle.topk(np.random.default_rng(0).standard_normal((5, 6)).astype(np.float32), 1)
+    assert (w == 1.0).all()
+    idx, _ = oracle.topk(np.random.default_rng(1).standard_normal((5, 6)).astype(np.float32), 6)
+    assert (np.sort(idx, 1) == np.arange(6)).all()
+    # known weights: logits 0 and ln 3 -> weights 1/4 and 3/4
+    idx, w = oracle.topk(np.array([[0.0, np.log(3.0), -5.0]], np.float32), 2)
+    assert idx.tolist() == [[1, 0]]
+    np.testing.assert_allclose(w[0], [0.75, 0.25], atol=1e-7)
+    with pytest.raises(oracle.OracleError):
+        oracle.topk(np.array([[0.0, np.nan]], np.float32), 1)
+
+
+def test_skewed_bias_and_empty_expert_workload_routing():
+    """Mid workload: bias -inf on the last expert empties it, +2 on four experts makes them hot."""
+    inp = workloads.make_inputs("mid_skewed", with_weights=False)
+    x = workloads.bf16_bits(inp["x"])[:512]
+    idx, w, logits = oracle.route(x, inp["wr"].numpy(), inp["bias"].numpy(), 4)
+    gs, go, ss, sr = oracle.dispatch(idx, 32)
+    assert gs[31] == 0 and gs[:4].min() > 5 * gs[4:31].max()
+    assert np.isinf(logits[:, 31]).all()
+
+
+# ---------------------------------------------------------------- dispatch / permute
+
+@pytest.mark.parametrize("T,E,k", [(64, 8, 2), (300, 32, 4), (257, 128, 8), (5, 4, 4), (0, 4, 2)])
+def test_dispatch_is_the_expert_then_token_order(T, E, k):
+    rng = np.random.default_rng(T + E)
+    idx = np.array([rng.permutation(E)[:k] for _ in range(T)], np.int32).reshape(T, k)
+    if T >= 3:
+        idx[:3] = np.arange(k)  # several tokens on the same experts
+    gs, go, ss, sr = oracle.dispatch(idx, E)
+    S = T * k
+    assert np.array_equal(gs, np.bincount(idx.reshape(-1), minlength=E))
+    assert go[0] == 0 and np.array_equal(np.diff(go), gs) and go[-1] == S
+    flat_e = idx.reshape(-1)
+    flat_t = np.repeat(np.arange(T), k)
+    order = np.lexsort((flat_t, flat_e))  # library sort by (expert, token)
+    assert np.array_equal(ss, order)
+    assert np.array_equal(sr[ss], np.arange(S))  # bijection
+    assert np.array_equal(ss[sr], np.arange(S))
+    if S:
+        assert np.all(np.diff(flat_e[ss]) >= 0)
+        for e in range(E):
+            assert np.all(flat_e[ss[go[e]:go[e + 1]]] == e)
+
+
+def test_dispatch_rejects_bad_indices():
+    with pytest.raises(oracle.OracleError):
+        oracle.dispatch(np.array([[0, 4]], np.int32), 4)
+    with pytest.raises(oracle.OracleError):
+        oracle.dispatch(np.array([[1, 1]], np.int32), 4)
+
+
+def test_permute_copies_rows_bitwise_and_combine_with_unit_weights_is_k_x():
+    for T, emb, E, k in [(64, 128, 8, 2), (33, 64, 16, 4), (20, 32, 8, 8)]:
+        rng = np.random.default_rng(k)
+        x = _bf16(rng.standard_normal((T, emb)))
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        gs, go, ss, sr = oracle.dispatch(idx, E)
+        xs = oracle.permute(x, ss, k)
+        assert np.array_equal(xs, x[ss // k])
+        y = oracle.combine(xs, sr, None, T, k)  # permute backward = combine with unit weights
+        assert np.array_equal(y, (k * _val(x)).astype(np.float32))
+
+
+# ---------------------------------------------------------------- stage oracles
+
+def _offsets(rng, M, E, empty=(1,)):
+    cuts = np.sort(rng.integers(0, M + 1, E - 1))
+    sizes = np.diff(np.concatenate([[0], cuts, [M]]))
+    for e in empty:
+        if e < E:
+            sizes[e + 1 if e + 1 < E else 0] += sizes[e]
+            sizes[e] = 0
+    return np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+
+
+def test_grouped_gemm_stage_matches_per_group_matmul():
+    rng = np.random.default_rng(6)
+    M, K, N, E = 37, 24, 20, 5
+    off = _offsets(rng, M, E)
+    A = _bf16(rng.standard_normal((M, K)))
+    Bnn = _bf16(rng.standard_normal((E, K, N)))
+    Bnt = _bf16(rng.standard_normal((E, N, K)))
+    Av = _val(A)
+    got = oracle.grouped_gemm(0, 0, A, Bnn, off, real="f64")
+    got_t = oracle.grouped_gemm(1, 0, A, Bnt, off, real="f64")
+    got_s = oracle.grouped_gemm(0, 1, A, Bnn, off, real="f64")
+    for e in range(E):
+        r = slice(off[e], off[e + 1])
+        h = Av[r] @ _val(Bnn)[e]
+        np.testing.assert_allclose(got[r], h, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(got_t[r], Av[r] @ _val(Bnt)[e].T, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(got_s[r], _silu(h[:, :N // 2]) * h[:, N // 2:], rtol=1e-12, atol=1e-12)
+    part = oracle.grouped_gemm(0, 0, A, Bnn, off, rows=(5, 30), real="f64")
+    assert np.array_equal(part, got[5:30])
+
+
+def test_swiglu_backward_epilogue_matches_finite_differences():
+    """epi 2 returns d/d[h] of sum(da * silu(g) * u) for h = [g | u]."""
+    rng = np.random.default_rng(8)
+    M, K, N, E = 6, 5, 4, 2
+    off = np.array([0, 2, 6], np.int32)
+    A = rng.standard_normal((M, K))
+    B = rng.standard_normal((E, N, K))  # NT
+    h = rng.standard_normal((M, 2 * N))
+    dh = oracle.grouped_gemm(1, 2, A, B, off, aux=h, real="f64")
+    da = np.concatenate([A[off[e]:off[e + 1]] @ B[e].T for e in range(E)])
+    f = lambda hh: np.sum(da * _silu(hh[:, :N]) * hh[:, N:])  # noqa: E731
+    eps = 1e-6
+    fd = np.zeros_like(h)
+    for i in np.ndindex(h.shape):
+        hp, hm = h.copy(), h.copy()
+        hp[i] += eps
+        hm[i] -= eps
+        fd[i] = (f(hp) - f(hm)) / (2 * eps)
+    np.testing.assert_allclose(dh, fd, rtol=1e-7, atol=1e-8)
+
+
+def test_wgrad_stage_matches_transposed_matmul():
+    rng = np.random.default_rng(10)
+    M, P, Q, E = 29, 12, 9, 4
+    off = _offsets(rng, M, E, empty=(2,))
+    A = _bf16(rng.standard_normal((M, P)))
+    D = _bf16(rng.standard_normal((M, Q)))
+    for e in range(E):
+        got = oracle.grouped_wgrad(A, D, off, e, real="f64")
+        r = slice(off[e], off[e + 1])
+        want = _val(A)[r].T @ _val(D)[r]
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+        if off[e] == off[e + 1]:
+            assert (got == 0).all()
+
+
+def test_combine_and_combine_backward_stages():
+    rng = np.random.default_rng(12)
+    T, emb, E, k = 21, 16, 6, 3
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    _, _, ss, sr = oracle.dispatch(idx, E)
+    ys = _bf16(rng.standard_normal((T * k, emb)))
+    dy = _bf16(rng.standard_normal((T, emb)))
+    y = oracle.combine(ys, sr, w, T, k, real="f64")
+    want = np.einsum("tj,tjn->tn", w.astype(np.float64), _val(ys)[sr.reshape(T, k)])
+    np.testing.assert_allclose(y, want, rtol=1e-12, atol=1e-12)
+    dys, dw = oracle.combine_bwd(dy, ys, sr, w, k, real="f64")
+    # adjoint identity: <combine(ys), dy> == <ys, dys> and dw = d<combine, dy>/dw
+    assert abs(np.sum(y * _val(dy)) - np.sum(_val(ys) * dys)) < 1e-9 * np.abs(y).sum()
+    want_dw = np.einsum("tjn,tn->tj", _val(ys)[sr.reshape(T, k)], _val(dy))
+    np.testing.assert_allclose(dw, want_dw, rtol=1e-12, atol=1e-12)
+
+
+def test_stage_composition_equals_per_token_forward():
+    """route -> dispatch -> permute -> GEMM1(SwiGLU) -> GEMM2 -> combine == the per-token loop."""
+    T, emb, mlp, E, k = 48, 32, 24, 6, 2
+    x, wr, wi, wo = _case(T, emb, mlp, E, k, seed=13)
+    idx, w, _ = oracle.route(x, wr, None, k)
+    gs, go, ss, sr = oracle.dispatch(idx, E)
+    xs = oracle.permute(x, ss, k)
+    a = oracle.grouped_gemm(0, 1, xs, wi, go, real="f64")
+    o = oracle.grouped_gemm(0, 0, a, _val(wo), go, real="f64")
+    y = oracle.combine(o, sr, w, T, k, real="f64")
+    np.testing.assert_allclose(y, oracle.ffn_fwd_tokens(x, idx, w, wi, wo, real="f64"), rtol=1e-10, atol=1e-13)
+
+
+# ---------------------------------------------------------------- backward
+
+def _fd_case():
+    T, emb, mlp, E, k = 4, 8, 8, 4, 2
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((T, emb))
+    wi = rng.standard_normal((E, emb, 2 * mlp)) * 0.4
+    wo = rng.standard_normal((E, mlp, emb)) * 0.4
+    dy = rng.standard_normal((T, emb))
+    idx = np.array([[0, 2], [1, 3], [2, 0], [0, 1]], np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    return x, wi, wo, dy, idx, w
+
+
+def _loss(x, wi, wo, dy, idx, w):
+    return float(np.sum(oracle.ffn_fwd_tokens(x, idx, w, wi, wo, real="f64") * dy))
+
+
+def _central(f, arr, eps=1e-5):
+    g = np.zeros_like(arr)
+    for i in np.ndindex(arr.shape):
+        old = arr[i]
+        arr[i] = old + eps
+        fp = f()
+        arr[i] = old - eps
+        fm = f()
+        arr[i] = old
+        g[i] = (fp - fm) / (2 * eps)
+    return g
+
+
+def test_backward_matches_central_finite_differences():
+    x, wi, wo, dy, idx, w = _fd_case()
+    dx, dw = oracle.ffn_bwd_tokens(x, idx, w, wi, wo, dy, real="f64")
+    grads = oracle.ffn_wgrad_experts(x, idx, w, wi, wo, dy, range(4), real="f64")
+    dwi = np.stack([grads[e][0] for e in range(4)])
+    dwo = np.stack([grads[e][1] for e in range(4)])
+    f = lambda: _loss(x, wi, wo, dy, idx, w)  # noqa: E731
+    np.testing.assert_allclose(dx, _central(f, x), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dwi, _central(f, wi), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dwo, _central(f, wo), rtol=1e-6, atol=1e-8)
+    wd = w.astype(np.float64)
+    fw = lambda: float(np.sum(oracle.ffn_fwd_tokens(x, idx, wd.astype(np.float32), wi, wo, real="f64") * dy))  # noqa: E731
+    # topk_w is stored fp32, so differentiate by linearity instead: y is linear in each weight
+    y_parts = oracle.ffn_fwd_tokens(x, idx, w, wi, wo, real="f64", want_intermediates=True)[3]  # o [T,k,emb]
+    np.testing.assert_allclose(dw, np.einsum("tjn,tn->tj", y_parts, dy), rtol=1e-12, atol=1e-12)
+    assert np.isfinite(fw())
+
+
+def test_unrouted_expert_gets_zero_weight_gradient():
+    x, wi, wo, dy, idx, w = _fd_case()
+    idx = np.where(idx == 3, 1, idx).astype(np.int32)
+    idx[1] = [1, 2]
+    g = oracle.ffn_wgrad_experts(x, idx, w, wi, wo, dy, [3], real="f64")[3]
+    assert (g[0] == 0).all() and (g[1] == 0).all()
+
+
+def test_backward_stage_composition_equals_per_token_backward():
+    """combine-bwd -> NT GEMM + SwiGLU-bwd -> NT GEMM -> permute-bwd == the per-token backward;
+    wgrad stage on the sorted activations == the per-expert weight gradients."""
+    T, emb, mlp, E, k = 12, 16, 8, 4, 2
+    x, wr, wi, wo = _case(T, emb, mlp, E, k, seed=17)
+    dy = _bf16(np.random.default_rng(3).standard_normal((T, emb)))
+    idx, w, _ = oracle.route(x, wr, None, k)
+    gs, go, ss, sr = oracle.dispatch(idx, E)
+    xs = oracle.permute(x, ss, k)
+    h = oracle.grouped_gemm(0, 0, xs, wi, go, real="f64")
+    a = _silu(h[:, :mlp]) * h[:, mlp:]
+    o = oracle.grouped_gemm(0, 0, a, _val(wo), go, real="f64")
+    do, dwt = oracle.combine_bwd(dy, o, sr, w, k, real="f64")
+    wo_t = np.ascontiguousarray(_val(wo))  # NT: B[e] = wo[e] is [mlp, emb] = [N, K]
+    dh = oracle.grouped_gemm(1, 2, do, wo_t, go, aux=h, real="f64")
+    dxs = oracle.grouped_gemm(1, 0, dh, np.ascontiguousarray(_val(wi)), go, real="f64")  # wi[e] = [emb, 2mlp] = [N, K]
+    dx = oracle.combine(dxs, sr, None, T, k, real="f64")
+    dx_ref, dw_ref = oracle.ffn_bwd_tokens(x, idx, w, wi, wo, dy, real="f64")
+    np.testing.assert_allclose(dx, dx_ref, rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(dwt, dw_ref, rtol=1e-9, atol=1e-12)
+    ref = oracle.ffn_wgrad_experts(x, idx, w, wi, wo, dy, range(E), real="f64")
+    for e in range(E):
+        np.testing.assert_allclose(oracle.grouped_wgrad(a, do, go, e, real="f64"), ref[e][1], rtol=1e-9, atol=1e-12)
+        np.testing.assert_allclose(oracle.grouped_wgrad(_val(xs), dh, go, e, real="f64"), ref[e][0], rtol=1e-9,
+                                   atol=1e-12)
