@@ -1,0 +1,232 @@
+/*
+ * moe_ffn.h -- C ABI of the MI355X (gfx950) sparse-MoE expert-FFN library.
+ *
+ * The forward pipeline follows the flow in "Keep fused MoE weights intact
+ * through FSDP gather" (Description): the prefused expert weight feeds ONE
+ * grouped GEMM and only the GEMM output is split into gate and up for SwiGLU.
+ * Around it sit the router and the permute/combine pair of "MoE: fused
+ * TensorCore Pallas permute/combine kernels and split-expert wi layout for
+ * TPU v6e" (Context item 1; Commits table, commits 1 and 2), and the second
+ * grouped GEMM of "[DRAFT][JAX] Optimize MoE block" (Flowchart).
+ *
+ * Conventions for every call:
+ *  - Tensor arguments are DEVICE pointers to dense row-major buffers unless
+ *    stated. bf16 tensors are passed as raw 16-bit patterns (moe_bf16_t).
+ *    Every pointer must be 16-byte aligned.
+ *  - The caller owns all memory, the workspace included. The library never
+ *    allocates, frees, synchronises or copies between host and device.
+ *  - Calls only enqueue work on `stream` (a hipStream_t; NULL = the null
+ *    stream) and return. Results are ready when the stream reaches them.
+ *  - Arguments are validated before anything is enqueued. A call that
+ *    returns an error has enqueued nothing, except MOE_ERR_HIP, which reports
+ *    a launch failure (the HIP error text is in moe_last_error_detail()).
+ *  - Index data produced on the device (expert ids, offsets, rows) is not
+ *    re-validated on the host. Out-of-range values give unspecified results
+ *    but never an access outside the buffers described here.
+ *  - The library holds no mutable global state apart from the thread-local
+ *    error text. Calls on different streams with separate buffers may run
+ *    concurrently.
+ *
+ * Shapes: T tokens, emb model width, mlp per-expert hidden width, E experts,
+ * k experts per token, S = T * k routed rows.
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t moe_bf16_t; /* raw bf16 bit pattern */
+typedef void* moe_stream_t;  /* hipStream_t */
+
+typedef struct {
+  int64_t T;
+  int32_t emb, mlp, E, k;
+} moe_shape_t;
+
+enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,       /* sizes inconsistent or out of range */
+  MOE_ERR_UNSUPPORTED = 3, /* valid but outside what the kernels support (moe_query_support) */
+  MOE_ERR_WORKSPACE = 4,   /* workspace missing or too small */
+  MOE_ERR_HIP = 5,         /* a kernel launch failed */
+  MOE_ERR_ALIGN = 6        /* a pointer is not 16-byte aligned */
+};
+
+enum { MOE_NN = 0, MOE_NT = 1 };
+enum { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1, MOE_EPI_SWIGLU_BWD = 2 };
+
+/* Text of a status code (static storage). */
+const char* moe_status_str(int status);
+/* Detail of the last error on the calling thread ("" if none). */
+const char* moe_last_error_detail(void);
+/* Library version string. */
+const char* moe_version(void);
+
+/*
+ * moe_query_support: MOE_OK if the layer kernels accept this shape, else the
+ * reason (MOE_ERR_SHAPE / MOE_ERR_UNSUPPORTED, detail text set). Supported:
+ * 0 <= T, T*k < 2^31; emb % 64 == 0; mlp % 64 == 0; 1 <= k <= 64; k <= E <= 256.
+ * The pages' own Pallas kernels guard a similar envelope (a capability check
+ * on dtype, width multiple of 128 lanes, row count = tokens * k and k <= 128;
+ * "MoE: fused TensorCore Pallas permute/combine kernels ...", Code Review).
+ * Here an unsupported shape is an error, never a fallback.
+ */
+int moe_query_support(const moe_shape_t* shape);
+
+/*
+ * Workspace sizes in bytes (host computation, no device access).
+ *  moe_permute_workspace_bytes: scratch of moe_permute (per-block expert
+ *    masks and row bases).
+ *  moe_workspace_bytes: scratch of moe_ffn_fwd (with_backward = 0: routing,
+ *    indices and the xs/a/o activations when no saved set is given) or of
+ *    moe_ffn_bwd (with_backward = 1: the do/dh/dxs activations).
+ */
+size_t moe_permute_workspace_bytes(const moe_shape_t* shape);
+size_t moe_workspace_bytes(const moe_shape_t* shape, int with_backward);
+
+/*
+ * moe_route -- gate and top-k routing ("[DRAFT][JAX] Optimize MoE block",
+ * Flowchart; top-k weights on the main compute units in "Gemma4 26B MoE on
+ * TPU v6e: MaxText layer/model optimizations", Commits table, commit 6).
+ *  x [T, emb] bf16; wr [emb, E] fp32; bias [E] fp32 or NULL (added to the
+ *  logits, may hold -inf to disable an expert).
+ *  logits_in [T, E] fp32 or NULL: when given, these are the logits (x, wr
+ *  and bias must then be NULL).
+ *  Outputs topk_idx [T, k] int32 and topk_w [T, k] fp32.
+ * Logits are the fp32 fused-multiply-add chain over emb in ascending order
+ * starting from 0, then + bias (one fp32 add). Picks are in descending logit
+ * order; equal logits go to the lower expert id (+0 equals -0). The weights
+ * are the softmax over the k picked logits (which equals the full softmax
+ * renormalised over the picks). NaN logits give unspecified picks.
+ */
+int moe_route(const moe_shape_t* shape, const moe_bf16_t* x, const float* wr, const float* bias,
+              const float* logits_in, int32_t* topk_idx, float* topk_w, moe_stream_t stream);
+
+/*
+ * moe_permute -- group_size histogram, then the gather of tokens into
+ * expert-sorted order ("MoE: fused TensorCore Pallas permute/combine
+ * kernels ...", Commits table, commit 2: the histogram moves above the
+ * gather). The unsorted [T*k, emb] copy is never built (same page, Context
+ * item 1): each token row is read once and written to its k sorted rows.
+ *  x [T, emb] bf16, topk_idx [T, k] int32 in [0, E), distinct per token.
+ *  Outputs: group_sizes [E], group_offsets [E + 1] (exclusive prefix,
+ *  group_offsets[E] = S), sorted_slot [S] (row r holds slot t*k + j),
+ *  slot_row [S] (its inverse), xs [S, emb] bf16 (row r = x[sorted_slot[r]/k]).
+ *  Row order: by expert, then by token (stable), so it is unique.
+ *  ws: at least moe_permute_workspace_bytes(shape) bytes of device memory.
+ */
+int moe_permute(const moe_shape_t* shape, const moe_bf16_t* x, const int32_t* topk_idx, int32_t* group_sizes,
+                int32_t* group_offsets, int32_t* sorted_slot, int32_t* slot_row, moe_bf16_t* xs, void* ws,
+                size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * moe_grouped_gemm -- ragged grouped GEMM over expert groups, bf16 in, fp32
+ * accumulate, bf16 out. Row r of A belongs to the expert e with
+ * group_offsets[e] <= r < group_offsets[e + 1] (device array [E + 1]); rows
+ * at or past group_offsets[E] are not written. Groups may be empty.
+ *  op MOE_NN: B is [E, K, N] (B[e] is K x N).  op MOE_NT: B is [E, N, K]
+ *  (C = A B[e]^T, the transposed-RHS backward form of "MoE: fused TensorCore
+ *  Pallas permute/combine kernels ...", Related PRs, part 3).
+ *  A [M, K]. Epilogues:
+ *   MOE_EPI_NONE: C [M, N].
+ *   MOE_EPI_SWIGLU (op NN, N = 2*mlp, the prefused [gate | up] weight of
+ *    "Keep fused MoE weights intact through FSDP gather", Description):
+ *    C [M, mlp] = silu(h[:, :mlp]) * h[:, mlp:] with h = A B[e] kept in fp32;
+ *    aux_out [M, 2*mlp] bf16 receives h when non-NULL (saved for backward).
+ *   MOE_EPI_SWIGLU_BWD (op NT, N = mlp): da = A B[e]^T; aux_in = saved h
+ *    [M, 2*mlp]; C [M, 2*mlp] = [da*u*s*(1 + g*(1 - s)) | da*silu(g)] with
+ *    g = h[:, :mlp], u = h[:, mlp:], s = sigmoid(g) -- one concatenated
+ *    gradient, as in the gate/up split VJP of "Gemma4 26B MoE on TPU v6e",
+ *    Commits table, commit 7.
+ *  Needs K % 64 == 0, N % 8 == 0 (SWIGLU: mlp % 8 == 0), M < 2^31.
+ */
+int moe_grouped_gemm(int op, int epilogue, const moe_bf16_t* A, const moe_bf16_t* B, const moe_bf16_t* aux_in,
+                     moe_bf16_t* aux_out, const int32_t* group_offsets, int32_t E, int64_t M, int32_t K, int32_t N,
+                     moe_bf16_t* C, moe_stream_t stream);
+
+/*
+ * moe_grouped_gemm_wgrad -- weight gradient of a grouped GEMM: for every
+ * expert e, C[e] [P, Q] = sum over rows r of group e of A[r]^T D[r] (the
+ * gradients of the grouped GEMM, "MoE: fused TensorCore Pallas
+ * permute/combine kernels ...", Tests). A [M, P], D [M, Q] bf16;
+ * C [E, P, Q] bf16; an empty group gives exact zeros. fp32 accumulate.
+ * Needs P % 8 == 0, Q % 8 == 0.
+ */
+int moe_grouped_gemm_wgrad(const moe_bf16_t* A, const moe_bf16_t* D, const int32_t* group_offsets, int32_t E,
+                           int64_t M, int32_t P, int32_t Q, moe_bf16_t* C, moe_stream_t stream);
+
+/*
+ * moe_combine -- unpermute plus top-k weighted sum ("MoE: fused TensorCore
+ * Pallas permute/combine kernels ...", Commits table, commit 1):
+ *  y[t] = sum_{j<k} topk_w[t, j] * ys[slot_row[t*k + j]], accumulated in fp32
+ *  by fused multiply-add in j order, rounded once to bf16.
+ *  ys [S, emb] bf16; slot_row [S]; topk_w [T, k] fp32 or NULL for unit
+ *  weights (the permute backward, same table, commit 2); y [T, emb] bf16.
+ */
+int moe_combine(const moe_shape_t* shape, const moe_bf16_t* ys, const int32_t* slot_row, const float* topk_w,
+                moe_bf16_t* y, moe_stream_t stream);
+
+/*
+ * moe_combine_bwd -- backward of moe_combine (same table, commit 1: a
+ * permutation for dx and a reduction for the weight gradient):
+ *  dys[slot_row[t*k + j]] = bf16(topk_w[t, j] * dy[t]);
+ *  dtopk_w[t, j] = sum_n ys[slot_row[t*k + j], n] * dy[t, n] (fp32; skipped
+ *  when ys or dtopk_w is NULL).
+ */
+int moe_combine_bwd(const moe_shape_t* shape, const moe_bf16_t* dy, const moe_bf16_t* ys, const int32_t* slot_row,
+                    const float* topk_w, moe_bf16_t* dys, float* dtopk_w, moe_stream_t stream);
+
+/* Caller-owned activations of one forward pass, kept for the backward. All
+   device pointers: topk_idx [T,k], topk_w [T,k], group_sizes [E],
+   group_offsets [E+1], sorted_slot [S], slot_row [S], xs [S,emb],
+   h [S,2*mlp], a [S,mlp], o [S,emb]. */
+typedef struct {
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* group_sizes;
+  int32_t* group_offsets;
+  int32_t* sorted_slot;
+  int32_t* slot_row;
+  moe_bf16_t* xs;
+  moe_bf16_t* h;
+  moe_bf16_t* a;
+  moe_bf16_t* o;
+} moe_saved_t;
+
+/*
+ * moe_ffn_fwd -- the whole MoE FFN forward: route, permute, grouped GEMM on
+ * the prefused wi [E, emb, 2*mlp] with the SwiGLU epilogue, grouped GEMM on
+ * wo [E, mlp, emb], combine. y [T, emb] bf16.
+ *  Router inputs as in moe_route. saved: NULL for inference (intermediates
+ *  live in the workspace and h is not produced), else every pointer in it
+ *  must be set and receives the intermediates.
+ *  ws: at least moe_workspace_bytes(shape, 0) bytes.
+ */
+int moe_ffn_fwd(const moe_shape_t* shape, const moe_bf16_t* x, const float* wr, const float* bias,
+                const float* logits_in, const moe_bf16_t* wi, const moe_bf16_t* wo, moe_bf16_t* y,
+                const moe_saved_t* saved, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * moe_ffn_bwd -- backward of moe_ffn_fwd with the routing held fixed, for
+ * the loss sum(dy * y): combine backward, NT grouped GEMM on wo with the
+ * SwiGLU-backward epilogue, NT grouped GEMM on wi, permute backward
+ * (combine with unit weights), and the two weight-gradient grouped GEMMs.
+ *  dy [T, emb] bf16; saved from a moe_ffn_fwd call with the same shape and
+ *  weights. Outputs (each may be NULL to skip it): dx [T, emb] bf16,
+ *  dwi [E, emb, 2*mlp] bf16, dwo [E, mlp, emb] bf16, dtopk_w [T, k] fp32.
+ *  ws: at least moe_workspace_bytes(shape, 1) bytes.
+ */
+int moe_ffn_bwd(const moe_shape_t* shape, const moe_bf16_t* dy, const moe_saved_t* saved, const moe_bf16_t* wi,
+                const moe_bf16_t* wo, moe_bf16_t* dx, moe_bf16_t* dwi, moe_bf16_t* dwo, float* dtopk_w, void* ws,
+                size_t ws_bytes, moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_FFN_H */

@@ -1,0 +1,254 @@
+"""MI355X (gfx950) sparse-MoE expert FFN: Python binding of libmoe_ffn.so.
+
+Every step of the layer runs in the library's HIP kernels; this module only
+checks tensor dtypes/devices, allocates outputs with torch on the input's
+device and passes raw pointers and torch's current HIP stream. Names follow
+the C ABI in include/moe_ffn.h:
+
+    route, permute, grouped_gemm, grouped_gemm_wgrad, combine, combine_bwd,
+    ffn_fwd, ffn_bwd
+
+Tensors: bf16 activations/weights, fp32 router weights/logits/top-k weights,
+int32 indices, all contiguous and on one CUDA (HIP) device.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import torch
+
+from . import _lib
+from ._lib import (MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_SWIGLU_BWD, MOE_NN, MOE_NT, MoeError, MoeSaved,  # noqa: F401
+                   MoeShape)
+
+__all__ = ["route", "permute", "grouped_gemm", "grouped_gemm_wgrad", "combine", "combine_bwd", "ffn_fwd", "ffn_bwd",
+           "query_support", "workspace_bytes", "MoeError"]
+
+_EPI = {"none": MOE_EPI_NONE, "swiglu": MOE_EPI_SWIGLU, "swiglu_bwd": MOE_EPI_SWIGLU_BWD}
+_OP = {"nn": MOE_NN, "nt": MOE_NT}
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return C.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t, name, dtype, device=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def query_support(T: int, emb: int, mlp: int, E: int, k: int) -> None:
+    """Raise MoeError if the layer kernels do not support this shape."""
+    s = _lib.shape(T, emb, mlp, E, k)
+    _lib.check(_lib.lib().moe_query_support(C.byref(s)), "moe_query_support")
+
+
+def workspace_bytes(T: int, emb: int, mlp: int, E: int, k: int, backward: bool = False) -> int:
+    s = _lib.shape(T, emb, mlp, E, k)
+    return int(_lib.lib().moe_workspace_bytes(C.byref(s), int(backward)))
+
+
+def route(k: int, x: torch.Tensor | None = None, wr: torch.Tensor | None = None, bias: torch.Tensor | None = None,
+          logits: torch.Tensor | None = None):
+    """(topk_idx [T,k] int32, topk_w [T,k] fp32). Either x [T,emb] bf16 + wr [emb,E] fp32 (+ bias [E]),
+    or logits [T,E] fp32."""
+    if logits is not None:
+        _need(logits, "logits", torch.float32)
+        dev = logits.device
+        T, E = logits.shape
+        emb = 64
+    else:
+        _need(x, "x", torch.bfloat16)
+        dev = x.device
+        _need(wr, "wr", torch.float32, dev)
+        _need(bias, "bias", torch.float32, dev)
+        T, emb = x.shape
+        E = wr.shape[1]
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    s = _lib.shape(T, emb, 64, E, k)
+    _lib.check(_lib.lib().moe_route(C.byref(s), _ptr(x), _ptr(wr), _ptr(bias), _ptr(logits), _ptr(idx), _ptr(w),
+                                    _stream(dev)), "moe_route")
+    return idx, w
+
+
+def permute(x: torch.Tensor, topk_idx: torch.Tensor, E: int) -> dict:
+    """Expert-sorted gather: dict of group_sizes [E], group_offsets [E+1], sorted_slot [S], slot_row [S]
+    (int32) and xs [S, emb] bf16."""
+    _need(x, "x", torch.bfloat16)
+    dev = x.device
+    _need(topk_idx, "topk_idx", torch.int32, dev)
+    T, emb = x.shape
+    k = topk_idx.shape[1]
+    S = T * k
+    s = _lib.shape(T, emb, 64, E, k)
+    ws_n = int(_lib.lib().moe_permute_workspace_bytes(C.byref(s)))
+    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
+    out = dict(group_sizes=torch.empty(E, dtype=torch.int32, device=dev),
+               group_offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+               sorted_slot=torch.empty(S, dtype=torch.int32, device=dev),
+               slot_row=torch.empty(S, dtype=torch.int32, device=dev),
+               xs=torch.empty((S, emb), dtype=torch.bfloat16, device=dev))
+    _lib.check(_lib.lib().moe_permute(C.byref(s), _ptr(x), _ptr(topk_idx), _ptr(out["group_sizes"]),
+                                      _ptr(out["group_offsets"]), _ptr(out["sorted_slot"]), _ptr(out["slot_row"]),
+                                      _ptr(out["xs"]), _ptr(ws), ws.numel(), _stream(dev)), "moe_permute")
+    return out
+
+
+def grouped_gemm(A: torch.Tensor, B: torch.Tensor, group_offsets: torch.Tensor, op: str = "nn",
+                 epilogue: str = "none", aux_in: torch.Tensor | None = None, save_h: bool = False,
+                 out: torch.Tensor | None = None):
+    """Ragged grouped GEMM (see moe_grouped_gemm). Returns C, or (C, h) with save_h (SwiGLU only)."""
+    _need(A, "A", torch.bfloat16)
+    dev = A.device
+    _need(B, "B", torch.bfloat16, dev)
+    _need(group_offsets, "group_offsets", torch.int32, dev)
+    _need(aux_in, "aux_in", torch.bfloat16, dev)
+    M, K = A.shape
+    E = B.shape[0]
+    N = B.shape[2] if op == "nn" else B.shape[1]
+    epi = _EPI[epilogue]
+    width = N if epi == MOE_EPI_NONE else (N // 2 if epi == MOE_EPI_SWIGLU else 2 * N)
+    C_ = out if out is not None else torch.empty((M, width), dtype=torch.bfloat16, device=dev)
+    _need(C_, "out", torch.bfloat16, dev)
+    h = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if (save_h and epi == MOE_EPI_SWIGLU) else None
+    _lib.check(_lib.lib().moe_grouped_gemm(_OP[op], epi, _ptr(A), _ptr(B), _ptr(aux_in), _ptr(h), _ptr(group_offsets),
+                                           E, M, K, N, _ptr(C_), _stream(dev)), "moe_grouped_gemm")
+    return (C_, h) if save_h else C_
+
+
+def grouped_gemm_wgrad(A: torch.Tensor, D: torch.Tensor, group_offsets: torch.Tensor, E: int) -> torch.Tensor:
+    """C [E, P, Q] = per-group A^T D."""
+    _need(A, "A", torch.bfloat16)
+    dev = A.device
+    _need(D, "D", torch.bfloat16, dev)
+    _need(group_offsets, "group_offsets", torch.int32, dev)
+    M, P = A.shape
+    Q = D.shape[1]
+    C_ = torch.empty((E, P, Q), dtype=torch.bfloat16, device=dev)
+    _lib.check(_lib.lib().moe_grouped_gemm_wgrad(_ptr(A), _ptr(D), _ptr(group_offsets), E, M, P, Q, _ptr(C_),
+                                                 _stream(dev)), "moe_grouped_gemm_wgrad")
+    return C_
+
+
+def combine(ys: torch.Tensor, slot_row: torch.Tensor, topk_w: torch.Tensor | None, T: int, k: int) -> torch.Tensor:
+    """y [T, emb] = sum_j topk_w[t,j] ys[slot_row[t*k+j]] (unit weights when topk_w is None)."""
+    _need(ys, "ys", torch.bfloat16)
+    dev = ys.device
+    _need(slot_row, "slot_row", torch.int32, dev)
+    _need(topk_w, "topk_w", torch.float32, dev)
+    emb = ys.shape[1]
+    y = torch.empty((T, emb), dtype=torch.bfloat16, device=dev)
+    s = _lib.shape(T, emb, 64, max(k, 1), k)
+    _lib.check(_lib.lib().moe_combine(C.byref(s), _ptr(ys), _ptr(slot_row), _ptr(topk_w), _ptr(y), _stream(dev)),
+               "moe_combine")
+    return y
+
+
+def combine_bwd(dy: torch.Tensor, ys: torch.Tensor | None, slot_row: torch.Tensor, topk_w: torch.Tensor, k: int):
+    """(dys [S, emb] bf16, dtopk_w [T, k] fp32 or None when ys is None)."""
+    _need(dy, "dy", torch.bfloat16)
+    dev = dy.device
+    _need(ys, "ys", torch.bfloat16, dev)
+    _need(slot_row, "slot_row", torch.int32, dev)
+    _need(topk_w, "topk_w", torch.float32, dev)
+    T, emb = dy.shape
+    dys = torch.empty((T * k, emb), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((T, k), dtype=torch.float32, device=dev) if ys is not None else None
+    s = _lib.shape(T, emb, 64, max(k, 1), k)
+    _lib.check(_lib.lib().moe_combine_bwd(C.byref(s), _ptr(dy), _ptr(ys), _ptr(slot_row), _ptr(topk_w), _ptr(dys),
+                                          _ptr(dw), _stream(dev)), "moe_combine_bwd")
+    return dys, dw
+
+
+_SAVED_NAMES = ("topk_idx", "topk_w", "group_sizes", "group_offsets", "sorted_slot", "slot_row", "xs", "h", "a", "o")
+
+
+def alloc_saved(T: int, emb: int, mlp: int, E: int, k: int, device) -> dict:
+    S = T * k
+    i32, f32, bf = torch.int32, torch.float32, torch.bfloat16
+    return dict(topk_idx=torch.empty((T, k), dtype=i32, device=device),
+                topk_w=torch.empty((T, k), dtype=f32, device=device),
+                group_sizes=torch.empty(E, dtype=i32, device=device),
+                group_offsets=torch.empty(E + 1, dtype=i32, device=device),
+                sorted_slot=torch.empty(S, dtype=i32, device=device),
+                slot_row=torch.empty(S, dtype=i32, device=device),
+                xs=torch.empty((S, emb), dtype=bf, device=device),
+                h=torch.empty((S, 2 * mlp), dtype=bf, device=device),
+                a=torch.empty((S, mlp), dtype=bf, device=device),
+                o=torch.empty((S, emb), dtype=bf, device=device))
+
+
+def _saved_struct(saved: dict) -> MoeSaved:
+    return MoeSaved(*[saved[n].data_ptr() for n in _SAVED_NAMES])
+
+
+def ffn_fwd(x: torch.Tensor, wi: torch.Tensor, wo: torch.Tensor, k: int, wr: torch.Tensor | None = None,
+            bias: torch.Tensor | None = None, logits: torch.Tensor | None = None, save: bool = False,
+            workspace: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """MoE FFN forward. Returns (y [T, emb] bf16, saved dict or None)."""
+    _need(x, "x", torch.bfloat16)
+    dev = x.device
+    for t, n, d in ((wi, "wi", torch.bfloat16), (wo, "wo", torch.bfloat16), (wr, "wr", torch.float32),
+                    (bias, "bias", torch.float32), (logits, "logits", torch.float32)):
+        _need(t, n, d, dev)
+    T, emb = x.shape
+    E, _, n2 = wi.shape
+    mlp = n2 // 2
+    s = _lib.shape(T, emb, mlp, E, k)
+    ws_n = int(_lib.lib().moe_workspace_bytes(C.byref(s), 0))
+    if ws_n == 0:
+        _lib.check(_lib.lib().moe_query_support(C.byref(s)), "ffn_fwd")
+    ws = workspace if workspace is not None and workspace.numel() >= ws_n else \
+        torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    y = out if out is not None else torch.empty((T, emb), dtype=torch.bfloat16, device=dev)
+    saved = alloc_saved(T, emb, mlp, E, k, dev) if save else None
+    sv = C.byref(_saved_struct(saved)) if save else None
+    _lib.check(_lib.lib().moe_ffn_fwd(C.byref(s), _ptr(x), _ptr(wr), _ptr(bias), _ptr(logits), _ptr(wi), _ptr(wo),
+                                      _ptr(y), sv, _ptr(ws), ws.numel(), _stream(dev)), "moe_ffn_fwd")
+    return y, saved
+
+
+def ffn_bwd(dy: torch.Tensor, saved: dict, wi: torch.Tensor, wo: torch.Tensor, k: int,
+            need=("dx", "dwi", "dwo", "dtopk_w"), workspace: torch.Tensor | None = None) -> dict:
+    """MoE FFN backward with the routing held fixed; returns the requested gradients."""
+    _need(dy, "dy", torch.bfloat16)
+    dev = dy.device
+    _need(wi, "wi", torch.bfloat16, dev)
+    _need(wo, "wo", torch.bfloat16, dev)
+    T, emb = dy.shape
+    E, _, n2 = wi.shape
+    mlp = n2 // 2
+    s = _lib.shape(T, emb, mlp, E, k)
+    ws_n = int(_lib.lib().moe_workspace_bytes(C.byref(s), 1))
+    if ws_n == 0:
+        _lib.check(_lib.lib().moe_query_support(C.byref(s)), "ffn_bwd")
+    ws = workspace if workspace is not None and workspace.numel() >= ws_n else \
+        torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    g = {}
+    if "dx" in need:
+        g["dx"] = torch.empty((T, emb), dtype=torch.bfloat16, device=dev)
+    if "dwi" in need:
+        g["dwi"] = torch.empty((E, emb, 2 * mlp), dtype=torch.bfloat16, device=dev)
+    if "dwo" in need:
+        g["dwo"] = torch.empty((E, mlp, emb), dtype=torch.bfloat16, device=dev)
+    if "dtopk_w" in need:
+        g["dtopk_w"] = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _lib.check(_lib.lib().moe_ffn_bwd(C.byref(s), _ptr(dy), C.byref(_saved_struct(saved)), _ptr(wi), _ptr(wo),
+                                      _ptr(g.get("dx")), _ptr(g.get("dwi")), _ptr(g.get("dwo")),
+                                      _ptr(g.get("dtopk_w")), _ptr(ws), ws.numel(), _stream(dev)), "moe_ffn_bwd")
+    return g

@@ -1,0 +1,38 @@
+// Launch entry points of the gfx950 kernels (host side). Shapes and buffers
+// are validated by the C-ABI layer before any of these is called; each
+// returns the HIP status of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kPermuteBlock = 64;  // tokens per histogram block
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+hipError_t launch_route(int64_t T, int emb, int E, int k, const uint16_t* x, const float* wr, const float* bias,
+                        const float* logits_in, int32_t* topk_idx, float* topk_w, hipStream_t stream);
+
+// masks: [nblk, E] uint64, base: [nblk, E] int32, nblk = ceil(T / 64).
+hipError_t launch_permute(int64_t T, int emb, int E, int k, const uint16_t* x, const int32_t* topk_idx,
+                          int32_t* group_sizes, int32_t* group_offsets, int32_t* sorted_slot, int32_t* slot_row,
+                          uint16_t* xs, uint64_t* masks, int32_t* base, hipStream_t stream);
+
+hipError_t launch_grouped_gemm(int op, int epi, const uint16_t* A, const uint16_t* B, const uint16_t* aux_in,
+                               uint16_t* aux_out, const int32_t* group_offsets, int E, int64_t M, int K, int N,
+                               uint16_t* C, hipStream_t stream);
+
+hipError_t launch_wgrad(const uint16_t* A, const uint16_t* D, const int32_t* group_offsets, int E, int64_t M, int P,
+                        int Q, uint16_t* C, hipStream_t stream);
+
+hipError_t launch_combine(int64_t T, int emb, int k, const uint16_t* ys, const int32_t* slot_row, const float* w,
+                          uint16_t* y, hipStream_t stream);
+
+hipError_t launch_combine_bwd(int64_t T, int emb, int k, const uint16_t* dy, const uint16_t* ys,
+                              const int32_t* slot_row, const float* w, uint16_t* dys, float* dw, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,411 @@
+// C ABI of the MoE FFN library: argument validation, workspace layout and the
+// launch sequence of each entry point (declared in include/moe_ffn.h).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.h"
+#include "moe_ffn.h"
+
+namespace moe {
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+}  // namespace moe
+
+namespace {
+
+thread_local char g_detail[512];
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define NEED(p)                                                       \
+  do {                                                                \
+    if (!(p)) return fail(MOE_ERR_NULL, "argument %s is NULL", #p);   \
+    if (!aligned16(p)) return fail(MOE_ERR_ALIGN, "argument %s is not 16-byte aligned", #p); \
+  } while (0)
+#define MAYBE(p)                                                      \
+  do {                                                                \
+    if ((p) && !aligned16(p)) return fail(MOE_ERR_ALIGN, "argument %s is not 16-byte aligned", #p); \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int check_shape(const moe_shape_t* s) {
+  if (!s) return fail(MOE_ERR_NULL, "shape is NULL");
+  if (s->T < 0 || s->emb <= 0 || s->mlp <= 0 || s->E <= 0 || s->k <= 0)
+    return fail(MOE_ERR_SHAPE, "need T >= 0 and emb, mlp, E, k > 0");
+  if (s->k > s->E) return fail(MOE_ERR_SHAPE, "k (%d) > E (%d)", s->k, s->E);
+  if (s->E > 256) return fail(MOE_ERR_UNSUPPORTED, "E (%d) > 256", s->E);
+  if (s->k > 64) return fail(MOE_ERR_UNSUPPORTED, "k (%d) > 64", s->k);
+  if (s->emb % 64) return fail(MOE_ERR_UNSUPPORTED, "emb (%d) is not a multiple of 64", s->emb);
+  if (s->mlp % 64) return fail(MOE_ERR_UNSUPPORTED, "mlp (%d) is not a multiple of 64", s->mlp);
+  if (s->T * (int64_t)s->k >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "T*k >= 2^31");
+  if ((int64_t)s->emb * 2 * s->mlp >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "emb*2*mlp >= 2^31 (per-expert weight too large)");
+  if (s->T * (int64_t)s->k * 2 * s->mlp >= (int64_t(1) << 40))
+    return fail(MOE_ERR_UNSUPPORTED, "activation too large");
+  return MOE_OK;
+}
+
+// Region sizes of the permute workspace.
+size_t masks_bytes(const moe_shape_t* s) {
+  const int64_t nblk = (s->T + moe::kPermuteBlock - 1) / moe::kPermuteBlock;
+  return round_up((size_t)nblk * s->E * sizeof(uint64_t));
+}
+size_t base_bytes(const moe_shape_t* s) {
+  const int64_t nblk = (s->T + moe::kPermuteBlock - 1) / moe::kPermuteBlock;
+  return round_up((size_t)nblk * s->E * sizeof(int32_t));
+}
+size_t permute_ws(const moe_shape_t* s) { return masks_bytes(s) + base_bytes(s); }
+
+struct Carver {
+  char* p;
+  size_t used = 0;
+  template <class T>
+  T* take(size_t count) {
+    T* r = reinterpret_cast<T*>(p + used);
+    used += round_up(count * sizeof(T));
+    return r;
+  }
+};
+
+// Forward workspace: permute scratch, then routing and activations (used when no saved set is given).
+size_t fwd_ws(const moe_shape_t* s) {
+  const size_t S = (size_t)s->T * s->k;
+  return permute_ws(s) + round_up(S * 4) * 2 /*topk idx, w*/ + round_up(s->E * 4) + round_up((s->E + 1) * 4) +
+         round_up(S * 4) * 2 /*sorted_slot, slot_row*/ + round_up(S * s->emb * 2) /*xs*/ +
+         round_up(S * s->mlp * 2) /*a*/ + round_up(S * s->emb * 2) /*o*/;
+}
+size_t bwd_ws(const moe_shape_t* s) {
+  const size_t S = (size_t)s->T * s->k;
+  return round_up(S * s->emb * 2) /*do*/ + round_up(S * 2 * s->mlp * 2) /*dh*/ + round_up(S * s->emb * 2) /*dxs*/;
+}
+
+int check_gemm(int op, int epi, int64_t M, int K, int N, int E) {
+  if (op != MOE_NN && op != MOE_NT) return fail(MOE_ERR_SHAPE, "op must be MOE_NN or MOE_NT");
+  if (epi == MOE_EPI_SWIGLU && op != MOE_NN) return fail(MOE_ERR_UNSUPPORTED, "SWIGLU epilogue needs op NN");
+  if (epi == MOE_EPI_SWIGLU_BWD && op != MOE_NT) return fail(MOE_ERR_UNSUPPORTED, "SWIGLU_BWD epilogue needs op NT");
+  if (epi < MOE_EPI_NONE || epi > MOE_EPI_SWIGLU_BWD) return fail(MOE_ERR_SHAPE, "unknown epilogue %d", epi);
+  if (M < 0 || K <= 0 || N <= 0 || E <= 0) return fail(MOE_ERR_SHAPE, "need M >= 0 and K, N, E > 0");
+  if (E > 256) return fail(MOE_ERR_UNSUPPORTED, "E (%d) > 256", E);
+  if (M >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "M >= 2^31");
+  if (K % 64) return fail(MOE_ERR_UNSUPPORTED, "K (%d) is not a multiple of 64", K);
+  if (N % 8) return fail(MOE_ERR_UNSUPPORTED, "N (%d) is not a multiple of 8", N);
+  if (epi == MOE_EPI_SWIGLU && (N % 16)) return fail(MOE_ERR_UNSUPPORTED, "SWIGLU needs (N/2) %% 8 == 0");
+  if ((int64_t)K * N >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "K*N >= 2^31");
+  if ((int64_t)255 * K >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "K too large");
+  // upper bound of the ragged tile count must fit an int
+  const int64_t ntn = epi == MOE_EPI_SWIGLU ? (N / 2 + 127) / 128 : (N + 255) / 256;
+  if ((M / 256 + E) * ntn >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "tile count too large");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "null pointer";
+    case MOE_ERR_SHAPE: return "invalid shape";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch error";
+    case MOE_ERR_ALIGN: return "pointer not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error_detail(void) { return g_detail; }
+
+const char* moe_version(void) { return "moe_ffn 0.1 gfx950"; }
+
+int moe_query_support(const moe_shape_t* shape) {
+  g_detail[0] = 0;
+  return check_shape(shape);
+}
+
+size_t moe_permute_workspace_bytes(const moe_shape_t* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  return permute_ws(shape);
+}
+
+size_t moe_workspace_bytes(const moe_shape_t* shape, int with_backward) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  return with_backward ? bwd_ws(shape) : fwd_ws(shape);
+}
+
+int moe_route(const moe_shape_t* s, const moe_bf16_t* x, const float* wr, const float* bias, const float* logits_in,
+              int32_t* topk_idx, float* topk_w, moe_stream_t stream) {
+  g_detail[0] = 0;
+  if (int rc = check_shape(s)) return rc;
+  if (s->T == 0) return MOE_OK;  // no tokens: nothing to route
+  if (logits_in) {
+    if (x || wr || bias) return fail(MOE_ERR_SHAPE, "with logits_in, x, wr and bias must be NULL");
+    MAYBE(logits_in);
+  } else {
+    NEED(x);
+    NEED(wr);
+    MAYBE(bias);
+  }
+  NEED(topk_idx);
+  NEED(topk_w);
+  return hip_status(moe::launch_route(s->T, s->emb, s->E, s->k, x, wr, bias, logits_in, topk_idx, topk_w,
+                                      (hipStream_t)stream),
+                    "moe_route");
+}
+
+int moe_permute(const moe_shape_t* s, const moe_bf16_t* x, const int32_t* topk_idx, int32_t* group_sizes,
+                int32_t* group_offsets, int32_t* sorted_slot, int32_t* slot_row, moe_bf16_t* xs, void* ws,
+                size_t ws_bytes, moe_stream_t stream) {
+  g_detail[0] = 0;
+  if (int rc = check_shape(s)) return rc;
+  NEED(group_sizes);
+  NEED(group_offsets);
+  if (s->T > 0) {
+    NEED(x);
+    NEED(topk_idx);
+    NEED(sorted_slot);
+    NEED(slot_row);
+    NEED(xs);
+  }
+  NEED(ws);
+  if (ws_bytes < permute_ws(s)) return fail(MOE_ERR_WORKSPACE, "need %zu workspace bytes", permute_ws(s));
+  char* w = static_cast<char*>(ws);
+  uint64_t* masks = reinterpret_cast<uint64_t*>(w);
+  int32_t* base = reinterpret_cast<int32_t*>(w + masks_bytes(s));
+  return hip_status(moe::launch_permute(s->T, s->emb, s->E, s->k, x, topk_idx, group_sizes, group_offsets,
+                                        sorted_slot, slot_row, xs, masks, base, (hipStream_t)stream),
+                    "moe_permute");
+}
+
+int moe_grouped_gemm(int op, int epilogue, const moe_bf16_t* A, const moe_bf16_t* B, const moe_bf16_t* aux_in,
+                     moe_bf16_t* aux_out, const int32_t* group_offsets, int32_t E, int64_t M, int32_t K, int32_t N,
+                     moe_bf16_t* C, moe_stream_t stream) {
+  g_detail[0] = 0;
+  if (int rc = check_gemm(op, epilogue, M, K, N, E)) return rc;
+  NEED(B);
+  NEED(group_offsets);
+  if (M > 0) {
+    NEED(A);
+    NEED(C);
+  }
+  if (epilogue == MOE_EPI_SWIGLU_BWD) NEED(aux_in);
+  if (epilogue == MOE_EPI_SWIGLU) MAYBE(aux_out);
+  return hip_status(moe::launch_grouped_gemm(op, epilogue, A, B, aux_in, epilogue == MOE_EPI_SWIGLU ? aux_out : nullptr,
+                                             group_offsets, E, M, K, N, C, (hipStream_t)stream),
+                    "moe_grouped_gemm");
+}
+
+int moe_grouped_gemm_wgrad(const moe_bf16_t* A, const moe_bf16_t* D, const int32_t* group_offsets, int32_t E,
+                           int64_t M, int32_t P, int32_t Q, moe_bf16_t* C, moe_stream_t stream) {
+  g_detail[0] = 0;
+  if (M < 0 || P <= 0 || Q <= 0 || E <= 0) return fail(MOE_ERR_SHAPE, "need M >= 0 and P, Q, E > 0");
+  if (E > 256) return fail(MOE_ERR_UNSUPPORTED, "E (%d) > 256", E);
+  if (M >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "M >= 2^31");
+  if (P % 8 || Q % 8) return fail(MOE_ERR_UNSUPPORTED, "P and Q must be multiples of 8");
+  if ((int64_t)E * ((P + 255) / 256) * ((Q + 255) / 256) >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "tile count too large");
+  NEED(group_offsets);
+  NEED(C);
+  if (M > 0) {
+    NEED(A);
+    NEED(D);
+  }
+  return hip_status(moe::launch_wgrad(A, D, group_offsets, E, M, P, Q, C, (hipStream_t)stream),
+                    "moe_grouped_gemm_wgrad");
+}
+
+int moe_combine(const moe_shape_t* s, const moe_bf16_t* ys, const int32_t* slot_row, const float* topk_w,
+                moe_bf16_t* y, moe_stream_t stream) {
+  g_detail[0] = 0;
+  if (int rc = check_shape(s)) return rc;
+  if (s->T > 0) {
+    NEED(ys);
+    NEED(slot_row);
+    NEED(y);
+    MAYBE(topk_w);
+  }
+  return hip_status(moe::launch_combine(s->T, s->emb, s->k, ys, slot_row, topk_w, y, (hipStream_t)stream),
+                    "moe_combine");
+}
+
+int moe_combine_bwd(const moe_shape_t* s, const moe_bf16_t* dy, const moe_bf16_t* ys, const int32_t* slot_row,
+                    const float* topk_w, moe_bf16_t* dys, float* dtopk_w, moe_stream_t stream) {
+  g_detail[0] = 0;
+  if (int rc = check_shape(s)) return rc;
+  if (s->T > 0) {
+    NEED(dy);
+    NEED(slot_row);
+    NEED(topk_w);
+    NEED(dys);
+    MAYBE(ys);
+    MAYBE(dtopk_w);
+  }
+  return hip_status(moe::launch_combine_bwd(s->T, s->emb, s->k, dy, ys, slot_row, topk_w, dys, dtopk_w,
+                                            (hipStream_t)stream),
+                    "moe_combine_bwd");
+}
+
+int moe_ffn_fwd(const moe_shape_t* s, const moe_bf16_t* x, const float* wr, const float* bias, const float* logits_in,
+                const moe_bf16_t* wi, const moe_bf16_t* wo, moe_bf16_t* y, const moe_saved_t* saved, void* ws,
+                size_t ws_bytes, moe_stream_t stream) {
+  g_detail[0] = 0;
+  if (int rc = check_shape(s)) return rc;
+  const bool any = s->T > 0;  // with no tokens, per-token buffers may be empty (NULL)
+  if (any) {
+    NEED(x);
+    NEED(y);
+  }
+  NEED(wi);
+  NEED(wo);
+  if (logits_in) {
+    if (wr || bias) return fail(MOE_ERR_SHAPE, "with logits_in, wr and bias must be NULL");
+    MAYBE(logits_in);
+  } else {
+    NEED(wr);
+    MAYBE(bias);
+  }
+  NEED(ws);
+  if (ws_bytes < fwd_ws(s)) return fail(MOE_ERR_WORKSPACE, "need %zu workspace bytes", fwd_ws(s));
+  if (saved) {
+    NEED(saved->group_sizes);
+    NEED(saved->group_offsets);
+    if (any) {
+      NEED(saved->topk_idx);
+      NEED(saved->topk_w);
+      NEED(saved->sorted_slot);
+      NEED(saved->slot_row);
+      NEED(saved->xs);
+      NEED(saved->h);
+      NEED(saved->a);
+      NEED(saved->o);
+    }
+  }
+  const int64_t T = s->T, S = T * s->k;
+  Carver c{static_cast<char*>(ws)};
+  uint64_t* masks = c.take<uint64_t>(((T + moe::kPermuteBlock - 1) / moe::kPermuteBlock) * s->E);
+  int32_t* base = c.take<int32_t>(((T + moe::kPermuteBlock - 1) / moe::kPermuteBlock) * s->E);
+  moe_saved_t v;
+  v.topk_idx = c.take<int32_t>(S);
+  v.topk_w = c.take<float>(S);
+  v.group_sizes = c.take<int32_t>(s->E);
+  v.group_offsets = c.take<int32_t>(s->E + 1);
+  v.sorted_slot = c.take<int32_t>(S);
+  v.slot_row = c.take<int32_t>(S);
+  v.xs = c.take<moe_bf16_t>(S * s->emb);
+  v.a = c.take<moe_bf16_t>(S * s->mlp);
+  v.o = c.take<moe_bf16_t>(S * s->emb);
+  v.h = nullptr;
+  if (saved) v = *saved;
+  const hipStream_t st = (hipStream_t)stream;
+  const int emb = s->emb, mlp = s->mlp, E = s->E, k = s->k;
+  if (int rc = hip_status(moe::launch_route(T, emb, E, k, logits_in ? nullptr : x, wr, bias, logits_in, v.topk_idx,
+                                            v.topk_w, st),
+                          "route"))
+    return rc;
+  if (int rc = hip_status(moe::launch_permute(T, emb, E, k, x, v.topk_idx, v.group_sizes, v.group_offsets,
+                                              v.sorted_slot, v.slot_row, v.xs, masks, base, st),
+                          "permute"))
+    return rc;
+  if (int rc = hip_status(moe::launch_grouped_gemm(MOE_NN, MOE_EPI_SWIGLU, v.xs, wi, nullptr, v.h, v.group_offsets, E,
+                                                   S, emb, 2 * mlp, v.a, st),
+                          "gemm1"))
+    return rc;
+  if (int rc = hip_status(moe::launch_grouped_gemm(MOE_NN, MOE_EPI_NONE, v.a, wo, nullptr, nullptr, v.group_offsets,
+                                                   E, S, mlp, emb, v.o, st),
+                          "gemm2"))
+    return rc;
+  return hip_status(moe::launch_combine(T, emb, k, v.o, v.slot_row, v.topk_w, y, st), "combine");
+}
+
+int moe_ffn_bwd(const moe_shape_t* s, const moe_bf16_t* dy, const moe_saved_t* saved, const moe_bf16_t* wi,
+                const moe_bf16_t* wo, moe_bf16_t* dx, moe_bf16_t* dwi, moe_bf16_t* dwo, float* dtopk_w, void* ws,
+                size_t ws_bytes, moe_stream_t stream) {
+  g_detail[0] = 0;
+  if (int rc = check_shape(s)) return rc;
+  if (!saved) return fail(MOE_ERR_NULL, "saved is NULL");
+  NEED(saved->group_offsets);
+  if (s->T > 0) {  // with no tokens, per-token buffers may be empty (NULL)
+    NEED(dy);
+    NEED(saved->topk_w);
+    NEED(saved->slot_row);
+    NEED(saved->xs);
+    NEED(saved->h);
+    NEED(saved->a);
+    NEED(saved->o);
+  }
+  NEED(wi);
+  NEED(wo);
+  MAYBE(dx);
+  MAYBE(dwi);
+  MAYBE(dwo);
+  MAYBE(dtopk_w);
+  NEED(ws);
+  if (ws_bytes < bwd_ws(s)) return fail(MOE_ERR_WORKSPACE, "need %zu workspace bytes", bwd_ws(s));
+  const int64_t T = s->T, S = T * s->k;
+  const int emb = s->emb, mlp = s->mlp, E = s->E, k = s->k;
+  const hipStream_t st = (hipStream_t)stream;
+  Carver c{static_cast<char*>(ws)};
+  moe_bf16_t* d_o = c.take<moe_bf16_t>(S * emb);
+  moe_bf16_t* dh = c.take<moe_bf16_t>(S * 2 * mlp);
+  moe_bf16_t* dxs = c.take<moe_bf16_t>(S * emb);
+  // combine backward: do (the permutation part) and dtopk_w (the reduction part)
+  if (int rc = hip_status(moe::launch_combine_bwd(T, emb, k, dy, dtopk_w ? saved->o : nullptr, saved->slot_row,
+                                                  saved->topk_w, d_o, dtopk_w, st),
+                          "combine_bwd"))
+    return rc;
+  if (dwo) {
+    if (int rc = hip_status(moe::launch_wgrad(saved->a, d_o, saved->group_offsets, E, S, mlp, emb, dwo, st), "dwo"))
+      return rc;
+  }
+  if (!dx && !dwi) return MOE_OK;
+  if (int rc = hip_status(moe::launch_grouped_gemm(MOE_NT, MOE_EPI_SWIGLU_BWD, d_o, wo, saved->h, nullptr,
+                                                   saved->group_offsets, E, S, emb, mlp, dh, st),
+                          "dh"))
+    return rc;
+  if (dwi) {
+    if (int rc = hip_status(moe::launch_wgrad(saved->xs, dh, saved->group_offsets, E, S, emb, 2 * mlp, dwi, st),
+                            "dwi"))
+      return rc;
+  }
+  if (dx) {
+    if (int rc = hip_status(moe::launch_grouped_gemm(MOE_NT, MOE_EPI_NONE, dh, wi, nullptr, nullptr,
+                                                     saved->group_offsets, E, S, 2 * mlp, emb, dxs, st),
+                            "dxs"))
+      return rc;
+    if (int rc = hip_status(moe::launch_combine(T, emb, k, dxs, saved->slot_row, nullptr, dx, st), "dx")) return rc;
+  }
+  return MOE_OK;
+}
+
+}  // extern "C"

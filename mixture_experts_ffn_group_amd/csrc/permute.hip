@@ -1,0 +1,168 @@
+// Permute into expert-sorted order: histogram, scan, row scatter.
+//
+// The group_size histogram sits above the gather ("MoE: fused TensorCore
+// Pallas permute/combine kernels and split-expert wi layout for TPU v6e",
+// Commits table, commit 2), and the gather never builds the unsorted
+// [tokens * top_k, emb] copy (same page, Context item 1): each token row is
+// read once and written straight to its k sorted rows.
+//
+// Sorted order is by (expert, token). Tokens are cut into blocks of 64; for
+// block b and expert e a 64-bit mask holds which of the block's tokens picked
+// e (a token picks an expert at most once). Then
+//   group_sizes[e] = sum_b popcount(mask[b][e]),
+//   base[b][e]     = group_offsets[e] + sum_{b' < b} popcount(mask[b'][e]),
+//   row(t, j)      = base[b][e] + popcount(mask[b][e] & lanes below t),
+// which is the rank of token t among the tokens of expert e: the stable order.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+// One wave per 64-token block: LDS 64-bit OR per (token, pick).
+__global__ __launch_bounds__(256) void hist_kernel(int64_t T, int E, int k, int64_t nblk,
+                                                   const int32_t* __restrict__ topk_idx, uint64_t* __restrict__ masks) {
+  __shared__ unsigned long long s_m[4][kMaxExperts];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t blk = (int64_t)blockIdx.x * 4 + wave;
+  for (int e = lane; e < E; e += 64) s_m[wave][e] = 0ull;
+  __syncthreads();
+  const int64_t t = blk * kPermuteBlock + lane;
+  if (blk < nblk && t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = topk_idx[t * k + j];
+      if ((unsigned)e < (unsigned)E) atomicOr(&s_m[wave][e], 1ull << lane);
+    }
+  }
+  __syncthreads();
+  if (blk < nblk)
+    for (int e = lane; e < E; e += 64) masks[blk * E + e] = s_m[wave][e];
+}
+
+// Single workgroup. Thread (e, p) owns a contiguous chunk of blocks of expert e.
+__global__ __launch_bounds__(1024) void scan_kernel(int64_t nblk, int E, const uint64_t* __restrict__ masks,
+                                                    int32_t* __restrict__ group_sizes,
+                                                    int32_t* __restrict__ group_offsets, int32_t* __restrict__ base) {
+  __shared__ int32_t s_part[1024];
+  __shared__ int32_t s_size[kMaxExperts];
+  __shared__ int32_t s_excl[kMaxExperts + 1];
+  const int tid = threadIdx.x;
+  const int P = 1024 / E;
+  const int e = tid % E, p = tid / E;
+  const bool active = p < P;
+  const int64_t chunk = (nblk + P - 1) / P;
+  const int64_t b0 = (int64_t)p * chunk;
+  const int64_t b1 = b0 + chunk < nblk ? b0 + chunk : nblk;
+  int32_t s = 0;
+  if (active)
+    for (int64_t b = b0; b < b1; ++b) s += __popcll(masks[b * E + e]);
+  s_part[tid] = s;
+  __syncthreads();
+  if (tid < E) {  // exclusive scan over the chunks of expert tid
+    int32_t run = 0;
+    for (int q = 0; q < P; ++q) {
+      const int32_t v = s_part[q * E + tid];
+      s_part[q * E + tid] = run;
+      run += v;
+    }
+    s_size[tid] = run;
+    group_sizes[tid] = run;
+  }
+  __syncthreads();
+  if (tid < 64) {  // exclusive scan over experts: 4 per lane, then a wave scan
+    int32_t v[4], tot = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e2 = tid * 4 + u;
+      v[u] = e2 < E ? s_size[e2] : 0;
+      tot += v[u];
+    }
+    int32_t incl = tot;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int32_t n = __shfl_up(incl, d);
+      if (tid >= d) incl += n;
+    }
+    int32_t ex = incl - tot;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e2 = tid * 4 + u;
+      if (e2 < E) s_excl[e2] = ex;
+      ex += v[u];
+    }
+    if (tid == 63) s_excl[E] = incl;
+  }
+  __syncthreads();
+  if (tid <= E) group_offsets[tid] = s_excl[tid];
+  if (active) {
+    int32_t run = s_excl[e] + s_part[p * E + e];
+    for (int64_t b = b0; b < b1; ++b) {
+      base[b * E + e] = run;
+      run += __popcll(masks[b * E + e]);
+    }
+  }
+}
+
+// One wave per token: read the row once (16 bytes per lane per chunk), write it to its k rows.
+__global__ __launch_bounds__(256) void scatter_kernel(int64_t T, int emb, int E, int k, const uint16_t* __restrict__ x,
+                                                      const int32_t* __restrict__ topk_idx,
+                                                      const uint64_t* __restrict__ masks,
+                                                      const int32_t* __restrict__ base,
+                                                      int32_t* __restrict__ sorted_slot,
+                                                      int32_t* __restrict__ slot_row, uint16_t* __restrict__ xs) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  const int64_t b = t / kPermuteBlock;
+  const int tl = (int)(t % kPermuteBlock);
+  const uint64_t below = (1ull << tl) - 1ull;
+  int32_t my_r = -1;
+  if (lane < k) {
+    const int e = topk_idx[t * k + lane];
+    if ((unsigned)e < (unsigned)E) {
+      my_r = base[b * E + e] + __popcll(masks[b * E + e] & below);
+      sorted_slot[my_r] = (int32_t)(t * k + lane);
+      slot_row[t * k + lane] = my_r;
+    }
+  }
+  const int nch = emb >> 3;  // 16-byte chunks per row
+  const uint16_t* src = x + t * emb;
+  for (int c0 = 0; c0 < nch; c0 += 64 * 8) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = c0 + lane + 64 * u;
+      if (c < nch) v[u] = ld16(src + c * 8);
+    }
+    for (int j = 0; j < k; ++j) {
+      const int32_t r = __shfl(my_r, j);
+      if (r < 0) continue;
+      uint16_t* dst = xs + (int64_t)r * emb;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = c0 + lane + 64 * u;
+        if (c < nch) st16(dst + c * 8, v[u]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_permute(int64_t T, int emb, int E, int k, const uint16_t* x, const int32_t* topk_idx,
+                          int32_t* group_sizes, int32_t* group_offsets, int32_t* sorted_slot, int32_t* slot_row,
+                          uint16_t* xs, uint64_t* masks, int32_t* base, hipStream_t stream) {
+  const int64_t nblk = (T + kPermuteBlock - 1) / kPermuteBlock;
+  if (nblk > 0) {
+    hist_kernel<<<dim3((unsigned)((nblk + 3) / 4)), dim3(256), 0, stream>>>(T, E, k, nblk, topk_idx, masks);
+  }
+  // The scan also runs for T == 0 so that group_sizes / group_offsets are written (all zero).
+  scan_kernel<<<dim3(1), dim3(1024), 0, stream>>>(nblk, E, masks, group_sizes, group_offsets, base);
+  if (T > 0) {
+    scatter_kernel<<<dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream>>>(T, emb, E, k, x, topk_idx, masks, base,
+                                                                           sorted_slot, slot_row, xs);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,186 @@
+// Router: logits, top-k and renormalised weights, one workgroup per 64 tokens.
+//
+// Gate and top-k routing come first in the MoE block ("[DRAFT][JAX] Optimize
+// MoE block", Flowchart), and the top-k weights are computed on the main
+// compute units ("Gemma4 26B MoE on TPU v6e: MaxText layer/model
+// optimizations", Commits table, commit 6).
+//
+// Logit contract (an integer decision hangs on it, so it is fixed exactly):
+// logits[t, e] = fp32 fma chain over i = 0..emb-1 of x[t, i] * wr[i, e],
+// starting from +0, then one fp32 add of bias[e]. Each (t, e) chain is one
+// lane's register; lanes run experts, the wave runs 16 tokens, so x values are
+// LDS broadcasts and wr values are conflict-free LDS reads. The chain is on
+// the fp32 vector ALU: its bound is 2*T*emb*E flop at the non-packed fp32 rate.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kTPW = 16;            // tokens per wave
+constexpr int kWaves = 4;
+constexpr int kTB = kTPW * kWaves;  // tokens per workgroup
+constexpr int kBK = 32;             // emb slice staged in LDS per step
+
+// Order-preserving key of a logit: larger logit -> larger key. -0 maps like +0;
+// NaN maps to 0, below every number.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  if (f != f) return 0u;
+  uint32_t u = __float_as_uint(f);
+  if ((u << 1) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) {
+    uint32_t lo = __shfl_xor((unsigned int)(uint32_t)v, s);
+    uint32_t hi = __shfl_xor((unsigned int)(uint32_t)(v >> 32), s);
+    uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s);
+  return v;
+}
+
+// EQ = experts per lane: lane L holds experts L, L + 64, ..., L + 64 (EQ - 1).
+template <int EQ>
+__global__ __launch_bounds__(256) void route_kernel(int64_t T, int emb, int E, int k, const uint16_t* __restrict__ x,
+                                                    const float* __restrict__ wr, const float* __restrict__ bias,
+                                                    const float* __restrict__ logits_in, int32_t* __restrict__ topk_idx,
+                                                    float* __restrict__ topk_w) {
+  __shared__ __attribute__((aligned(16))) float s_x[kBK][kTB];
+  __shared__ float s_w[kBK][64 * EQ];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * kTB;
+  const int64_t tw = t0 + wave * kTPW;
+
+  float acc[kTPW][EQ];
+  if (logits_in) {
+#pragma unroll
+    for (int tt = 0; tt < kTPW; ++tt)
+#pragma unroll
+      for (int q = 0; q < EQ; ++q) {
+        const int e = lane + 64 * q;
+        const int64_t t = tw + tt;
+        acc[tt][q] = (t < T && e < E) ? logits_in[t * E + e] : 0.0f;
+      }
+  } else {
+#pragma unroll
+    for (int tt = 0; tt < kTPW; ++tt)
+#pragma unroll
+      for (int q = 0; q < EQ; ++q) acc[tt][q] = 0.0f;
+    for (int i0 = 0; i0 < emb; i0 += kBK) {
+      {  // x slice: 64 tokens x 32 values, 16 bytes per thread, widened to fp32 [i][token]
+        const int tk = tid >> 2, seg = tid & 3;
+        const int64_t t = t0 + tk;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (t < T) v = ld16(x + t * emb + i0 + seg * 8);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          s_x[seg * 8 + 2 * u][tk] = bf16_lo(v[u]);
+          s_x[seg * 8 + 2 * u + 1][tk] = bf16_hi(v[u]);
+        }
+      }
+      for (int idx = tid; idx < kBK * 64 * EQ; idx += 256) {  // wr slice [32][64*EQ], zero past E
+        const int ii = idx / (64 * EQ), e = idx % (64 * EQ);
+        s_w[ii][e] = e < E ? wr[(int64_t)(i0 + ii) * E + e] : 0.0f;
+      }
+      __syncthreads();
+#pragma unroll 2
+      for (int ii = 0; ii < kBK; ++ii) {
+        float xv[kTPW];
+        const f32x4_t* px = reinterpret_cast<const f32x4_t*>(&s_x[ii][wave * kTPW]);
+#pragma unroll
+        for (int c = 0; c < kTPW / 4; ++c) {
+          const f32x4_t v = px[c];
+          xv[4 * c + 0] = v[0];
+          xv[4 * c + 1] = v[1];
+          xv[4 * c + 2] = v[2];
+          xv[4 * c + 3] = v[3];
+        }
+        float wv[EQ];
+#pragma unroll
+        for (int q = 0; q < EQ; ++q) wv[q] = s_w[ii][lane + 64 * q];
+#pragma unroll
+        for (int tt = 0; tt < kTPW; ++tt)
+#pragma unroll
+          for (int q = 0; q < EQ; ++q) acc[tt][q] = __builtin_fmaf(xv[tt], wv[q], acc[tt][q]);
+      }
+      __syncthreads();
+    }
+    if (bias) {
+#pragma unroll
+      for (int q = 0; q < EQ; ++q) {
+        const int e = lane + 64 * q;
+        const float b = e < E ? bias[e] : 0.0f;
+#pragma unroll
+        for (int tt = 0; tt < kTPW; ++tt) acc[tt][q] = acc[tt][q] + b;
+      }
+    }
+  }
+
+  // Top-k per token: k rounds of a wave-wide max over (key(logit), -expert).
+  // Picked and padding experts hold candidate 0, which no real expert reaches.
+#pragma unroll 1
+  for (int tt = 0; tt < kTPW; ++tt) {
+    const int64_t t = tw + tt;
+    if (t >= T) break;  // wave-uniform
+    uint64_t cand[EQ];
+#pragma unroll
+    for (int q = 0; q < EQ; ++q) {
+      const int e = lane + 64 * q;
+      cand[q] = e < E ? (((uint64_t)order_key(acc[tt][q]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e)) : 0ull;
+    }
+    int my_e = 0;
+    float my_l = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      uint64_t best = 0ull;
+#pragma unroll
+      for (int q = 0; q < EQ; ++q) best = cand[q] > best ? cand[q] : best;
+      best = wave_max_u64(best);
+      const int e = (int)(0xffffffffu - (uint32_t)best);
+      const float l = key_value((uint32_t)(best >> 32));
+#pragma unroll
+      for (int q = 0; q < EQ; ++q)
+        if (e == lane + 64 * q) cand[q] = 0ull;
+      if (lane == j) {
+        my_e = e;
+        my_l = l;
+      }
+    }
+    const float l0 = __shfl(my_l, 0);
+    const float ex = lane < k ? expf(my_l - l0) : 0.0f;
+    const float s = wave_sum(ex);
+    if (lane < k) {
+      topk_idx[t * k + lane] = my_e;
+      topk_w[t * k + lane] = ex / s;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_route(int64_t T, int emb, int E, int k, const uint16_t* x, const float* wr, const float* bias,
+                        const float* logits_in, int32_t* topk_idx, float* topk_w, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const dim3 grid((unsigned)((T + kTB - 1) / kTB)), block(256);
+  const int eq = (E + 63) / 64;
+  switch (eq) {
+    case 1: route_kernel<1><<<grid, block, 0, stream>>>(T, emb, E, k, x, wr, bias, logits_in, topk_idx, topk_w); break;
+    case 2: route_kernel<2><<<grid, block, 0, stream>>>(T, emb, E, k, x, wr, bias, logits_in, topk_idx, topk_w); break;
+    case 3: route_kernel<3><<<grid, block, 0, stream>>>(T, emb, E, k, x, wr, bias, logits_in, topk_idx, topk_w); break;
+    default: route_kernel<4><<<grid, block, 0, stream>>>(T, emb, E, k, x, wr, bias, logits_in, topk_idx, topk_w); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,185 @@
+"""GPU parity of the whole MoE FFN layer (moe_ffn_fwd / moe_ffn_bwd) against the oracle.
+
+Small workloads are compared element by element on every token. Full-size
+workloads (the Gemma4-class layer, the Zipf token sweep, the DeepSeek-V3-shaped
+forward+backward) are generated on the device; routing, group sizes, sort
+order and the permuted rows are compared bit for bit on every token, and the
+FFN outputs and gradients on sampled tokens and experts that the oracle
+computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_ffn_group_amd as moe
+import oracle
+import workloads
+from parity_util import W_ABS, assert_close, bits, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _dev(inp, device=DEV):
+    return {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+def _fwd(d, save=True, out=None):
+    wl = d["workload"]
+    return moe.ffn_fwd(d["x"], d["wi"], d["wo"], wl.k, wr=d["wr"], bias=d["bias"], logits=d["logits_in"], save=save,
+                       out=out)
+
+
+def _np32(t):
+    return None if t is None else t.detach().cpu().numpy()
+
+
+def _oracle_route(h):
+    wl = h["workload"]
+    return oracle.route(bits(h["x"]), _np32(h["wr"]), _np32(h["bias"]), wl.k, logits_in=_np32(h["logits_in"]))
+
+
+def _check_routing_and_permute(saved, h, check_xs_rows=None):
+    wl = h["workload"]
+    r_idx, r_w, _ = _oracle_route(h)
+    assert np.array_equal(saved["topk_idx"].cpu().numpy(), r_idx), "topk_idx differs"
+    assert np.abs(saved["topk_w"].cpu().numpy() - r_w).max() <= W_ABS
+    gs, go, ss, sr = oracle.dispatch(r_idx, wl.E)
+    assert np.array_equal(saved["group_sizes"].cpu().numpy(), gs)
+    assert np.array_equal(saved["group_offsets"].cpu().numpy(), go)
+    assert np.array_equal(saved["sorted_slot"].cpu().numpy(), ss)
+    assert np.array_equal(saved["slot_row"].cpu().numpy(), sr)
+    xs = bits(saved["xs"])
+    xb = bits(h["x"])
+    rows = np.arange(wl.S) if check_xs_rows is None else check_xs_rows
+    assert np.array_equal(xs[rows], xb[ss[rows] // wl.k])
+    return r_idx, r_w, gs, go, ss, sr
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid_skewed"])
+def test_layer_forward_every_token(name):
+    h = workloads.make_inputs(name)
+    d = _dev(h)
+    y, saved = _fwd(d)
+    r_idx, r_w, gs, *_ = _check_routing_and_permute(saved, h)
+    if name == "mid_skewed":
+        assert gs[-1] == 0 and gs[:4].min() > 1000
+    ref = oracle.ffn_fwd_tokens(bits(h["x"]), r_idx, r_w, bits(h["wi"]), bits(h["wo"]))
+    assert_close(to_np(y), ref, f"{name} y")
+
+
+@pytest.mark.parametrize("T,emb,mlp,E,k", [(1, 64, 64, 4, 2), (300, 192, 320, 12, 3), (257, 256, 128, 64, 8),
+                                           (100, 128, 64, 2, 2), (0, 128, 128, 8, 2)])
+def test_layer_forward_edge_shapes(T, emb, mlp, E, k):
+    wl = workloads.custom(T, emb, mlp, E, k, seed=T + E, sigma_w=0.05)
+    h = workloads.make_inputs(wl)
+    y, saved = _fwd(_dev(h))
+    assert y.shape == (T, emb)
+    if T == 0:
+        assert saved["group_sizes"].sum().item() == 0
+        return
+    r_idx, r_w, *_ = _check_routing_and_permute(saved, h)
+    ref = oracle.ffn_fwd_tokens(bits(h["x"]), r_idx, r_w, bits(h["wi"]), bits(h["wo"]))
+    assert_close(to_np(y), ref, "y")
+
+
+def test_layer_forward_is_deterministic_and_writes_every_output():
+    h = workloads.make_inputs("mid_skewed")
+    d = _dev(h)
+    canary = torch.full((h["workload"].T, h["workload"].emb), float("nan"), dtype=torch.bfloat16, device=DEV)
+    y1, _ = _fwd(d, save=False, out=canary)
+    assert torch.isfinite(y1).all()
+    y2, _ = _fwd(d, save=False)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_layer_forward_wo_times_two_doubles_y_exactly():
+    h = workloads.make_inputs("tiny")
+    d = _dev(h)
+    y1, _ = _fwd(d, save=False)
+    d["wo"] = (d["wo"].float() * 2).to(torch.bfloat16)
+    y2, _ = _fwd(d, save=False)
+    assert torch.equal((y1.float() * 2).to(torch.bfloat16).view(torch.int16), y2.view(torch.int16))
+
+
+def test_layer_forward_token_shuffle_shuffles_rows():
+    h = workloads.make_inputs("tiny")
+    d = _dev(h)
+    y, _ = _fwd(d, save=False)
+    perm = torch.randperm(h["workload"].T, generator=torch.Generator().manual_seed(0)).to(DEV)
+    d2 = dict(d)
+    d2["x"] = d["x"][perm].contiguous()
+    y2, _ = _fwd(d2, save=False)
+    assert torch.equal(y[perm].view(torch.int16), y2.view(torch.int16))
+
+
+def _small_bwd_case():
+    wl = workloads.custom(384, 256, 128, 8, 2, seed=77, sigma_w=0.05, backward=True)
+    return workloads.make_inputs(wl)
+
+
+def test_layer_backward_every_token_and_expert():
+    h = _small_bwd_case()
+    wl = h["workload"]
+    d = _dev(h)
+    y, saved = _fwd(d)
+    g = moe.ffn_bwd(d["dy"], saved, d["wi"], d["wo"], wl.k)
+    r_idx, r_w, *_ = _check_routing_and_permute(saved, h)
+    x, wi, wo, dy = bits(h["x"]), bits(h["wi"]), bits(h["wo"]), bits(h["dy"])
+    dx, dtw = oracle.ffn_bwd_tokens(x, r_idx, r_w, wi, wo, dy)
+    assert_close(to_np(g["dx"]), dx, "dx")
+    assert_close(g["dtopk_w"].cpu().numpy(), dtw, "dtopk_w")
+    ref = oracle.ffn_wgrad_experts(x, r_idx, r_w, wi, wo, dy, range(wl.E))
+    assert_close(to_np(g["dwi"]), np.stack([ref[e][0] for e in range(wl.E)]), "dwi")
+    assert_close(to_np(g["dwo"]), np.stack([ref[e][1] for e in range(wl.E)]), "dwo")
+    # skipping outputs leaves the others unchanged
+    g2 = moe.ffn_bwd(d["dy"], saved, d["wi"], d["wo"], wl.k, need=("dx",))
+    assert torch.equal(g2["dx"].view(torch.int16), g["dx"].view(torch.int16))
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+def _sample_tokens(T, n, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, T - 1], rng.choice(T, n - 2, replace=False)])).astype(np.int64)
+
+
+def _host(d):
+    return {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["gemma4_class"] + [f"sweep_zipf_T{t}" for t in workloads.SWEEP_T])
+def test_full_size_forward_sampled(name):
+    d = workloads.make_inputs(name, device=DEV)
+    wl = d["workload"]
+    y, saved = _fwd(d)
+    torch.cuda.synchronize()
+    h = _host(d)
+    r_idx, r_w, gs, go, ss, sr = _check_routing_and_permute(saved, h)
+    toks = _sample_tokens(wl.T, 40, wl.seed)
+    ref = oracle.ffn_fwd_tokens(bits(h["x"]), r_idx, r_w, bits(h["wi"]), bits(h["wo"]), tokens=toks)
+    assert_close(to_np(y)[toks], ref, f"{name} y[sampled]")
+
+
+@pytest.mark.slow
+def test_full_size_deepseek_v3_shape_forward_backward_sampled():
+    d = workloads.make_inputs("deepseek_v3_shape", device=DEV)
+    wl = d["workload"]
+    y, saved = _fwd(d)
+    g = moe.ffn_bwd(d["dy"], saved, d["wi"], d["wo"], wl.k)
+    torch.cuda.synchronize()
+    h = _host(d)
+    r_idx, r_w, gs, go, ss, sr = _check_routing_and_permute(saved, h)
+    x, wi, wo, dy = bits(h["x"]), bits(h["wi"]), bits(h["wo"]), bits(h["dy"])
+    toks = _sample_tokens(wl.T, 16, 5)
+    ref_y = oracle.ffn_fwd_tokens(x, r_idx, r_w, wi, wo, tokens=toks)
+    assert_close(to_np(y)[toks], ref_y, "y[sampled]")
+    dx, dtw = oracle.ffn_bwd_tokens(x, r_idx, r_w, wi, wo, dy, tokens=toks)
+    assert_close(to_np(g["dx"])[toks], dx, "dx[sampled]")
+    assert_close(g["dtopk_w"].cpu().numpy()[toks], dtw, "dtopk_w[sampled]")
+    experts = [int(e) for e in np.argsort(gs, kind="stable")[:2]]
+    ref = oracle.ffn_wgrad_experts(x, r_idx, r_w, wi, wo, dy, experts)
+    for e in experts:
+        assert_close(to_np(g["dwi"][e]), ref[e][0], f"dwi[{e}]")
+        assert_close(to_np(g["dwo"][e]), ref[e][1], f"dwo[{e}]")

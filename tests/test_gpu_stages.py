@@ -1,0 +1,261 @@
+"""GPU parity of each hot-path stage against the CPU oracle, through the C ABI.
+
+Integer and byte outputs (routing indices, group sizes/offsets, sort order,
+the permuted rows) must match bit for bit; fp32 top-k weights within 1e-6;
+bf16 outputs within relative Frobenius 1e-2 and max-abs 2e-2 (combine: at
+most 1 bf16 ulp from the oracle's fp32 result).
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_ffn_group_amd as moe
+import oracle
+import workloads
+from parity_util import W_ABS, assert_close, bf16_ulp_diff, bf16_values, bits, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _bf16_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).to(DEV)
+
+
+def _route_case(T, emb, E, k, seed, bias=None):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((T, emb), generator=g).to(torch.bfloat16)
+    wr = torch.randn((emb, E), generator=g) * 0.02
+    return x, wr, bias
+
+
+# ---------------------------------------------------------------- route
+
+@pytest.mark.parametrize("T,emb,E,k,seed", [(64, 128, 8, 2, 1), (1000, 256, 32, 4, 2), (333, 512, 128, 8, 3),
+                                            (130, 64, 256, 8, 4), (70, 128, 5, 5, 5), (17, 64, 64, 1, 6),
+                                            (0, 64, 8, 2, 7)])
+def test_route_bit_exact(T, emb, E, k, seed):
+    x, wr, _ = _route_case(T, emb, E, k, seed)
+    idx, w = moe.route(k, x=x.to(DEV), wr=wr.to(DEV))
+    r_idx, r_w, _ = oracle.route(bits(x), wr.numpy(), None, k)
+    assert np.array_equal(idx.cpu().numpy(), r_idx)
+    assert np.abs(w.cpu().numpy() - r_w).max(initial=0) <= W_ABS
+
+
+def test_route_with_bias_empty_and_hot_experts():
+    inp = workloads.make_inputs("mid_skewed", with_weights=False)
+    k = inp["workload"].k
+    idx, w = moe.route(k, x=inp["x"].to(DEV), wr=inp["wr"].to(DEV), bias=inp["bias"].to(DEV))
+    r_idx, r_w, _ = oracle.route(bits(inp["x"]), inp["wr"].numpy(), inp["bias"].numpy(), k)
+    assert np.array_equal(idx.cpu().numpy(), r_idx)
+    assert np.abs(w.cpu().numpy() - r_w).max() <= W_ABS
+    assert not (r_idx == 31).any()
+
+
+def test_route_logits_in_with_ties_zero_signs_and_minus_inf():
+    rng = np.random.default_rng(11)
+    T, E, k = 300, 40, 6
+    l = rng.standard_normal((T, E)).astype(np.float32)
+    l[:, 5] = l[:, 9]                      # exact ties -> lower id first
+    l[::3, 1] = 0.0
+    l[::3, 2] = -0.0                       # +0 == -0
+    l[::3, 3:8] = 0.0
+    l[::7, 0] = -np.inf                    # never picked while finite logits remain
+    l[5] = 0.25                            # all equal -> experts 0..k-1
+    idx, w = moe.route(k, logits=torch.from_numpy(l).to(DEV))
+    r_idx, r_w = oracle.topk(l, k)
+    assert np.array_equal(idx.cpu().numpy(), r_idx)
+    assert np.abs(w.cpu().numpy() - r_w).max() <= W_ABS
+    assert (w[5].cpu().numpy() == np.float32(1.0 / 6)).all() or np.abs(w[5].cpu().numpy() - 1 / 6).max() < 1e-7
+
+
+def test_route_zipf_logits_workload():
+    inp = workloads.make_inputs("sweep_zipf_T1024", with_weights=False)
+    idx, w = moe.route(8, logits=inp["logits_in"].to(DEV))
+    r_idx, r_w = oracle.topk(inp["logits_in"].numpy(), 8)
+    assert np.array_equal(idx.cpu().numpy(), r_idx)
+    assert np.abs(w.cpu().numpy() - r_w).max() <= W_ABS
+    loads = np.bincount(r_idx.reshape(-1), minlength=128)
+    assert loads[0] > 5 * np.median(loads)  # skewed head
+
+
+# ---------------------------------------------------------------- permute
+
+def _random_idx(T, E, k, seed, skew=False):
+    rng = np.random.default_rng(seed)
+    if skew:
+        p = 1.0 / np.arange(1, E + 1) ** 1.5
+        return np.array([rng.choice(E, k, replace=False, p=p / p.sum()) for _ in range(T)], np.int32).reshape(T, k)
+    return np.array([rng.permutation(E)[:k] for _ in range(T)], np.int32).reshape(T, k)
+
+
+@pytest.mark.parametrize("T,emb,E,k,skew", [(64, 128, 8, 2, False), (1000, 256, 16, 4, True), (129, 64, 256, 8, False),
+                                            (4096, 1024, 32, 4, True), (1, 64, 4, 4, False), (0, 64, 8, 2, False)])
+def test_permute_bit_exact(T, emb, E, k, skew):
+    rng = np.random.default_rng(T + E)
+    x = torch.from_numpy(rng.standard_normal((T, emb)).astype(np.float32)).to(torch.bfloat16)
+    idx = _random_idx(T, E, k, T, skew)
+    out = moe.permute(x.to(DEV), torch.from_numpy(idx).to(DEV), E)
+    gs, go, ss, sr = oracle.dispatch(idx, E)
+    assert np.array_equal(out["group_sizes"].cpu().numpy(), gs)
+    assert np.array_equal(out["group_offsets"].cpu().numpy(), go)
+    assert np.array_equal(out["sorted_slot"].cpu().numpy(), ss)
+    assert np.array_equal(out["slot_row"].cpu().numpy(), sr)
+    assert np.array_equal(bits(out["xs"]), oracle.permute(bits(x), ss, k))
+
+
+def test_permute_empty_expert_and_single_hot_expert():
+    T, emb, E, k = 500, 128, 8, 2
+    idx = np.zeros((T, k), np.int32)
+    idx[:, 0] = 3
+    idx[:, 1] = np.where(np.arange(T) % 2 == 0, 5, 6)  # experts 0,1,2,4,7 empty
+    x = torch.randn((T, emb)).to(torch.bfloat16)
+    out = moe.permute(x.to(DEV), torch.from_numpy(idx).to(DEV), E)
+    gs, go, ss, sr = oracle.dispatch(idx, E)
+    assert np.array_equal(out["group_sizes"].cpu().numpy(), gs)
+    assert np.array_equal(out["sorted_slot"].cpu().numpy(), ss)
+    assert np.array_equal(bits(out["xs"]), oracle.permute(bits(x), ss, k))
+
+
+# ---------------------------------------------------------------- combine
+
+@pytest.mark.parametrize("T,emb,k", [(64, 128, 2), (777, 1024, 4), (300, 2048, 8), (5, 7168, 8)])
+def test_combine_within_one_ulp(T, emb, k):
+    E = max(8, k)
+    rng = np.random.default_rng(T)
+    idx = _random_idx(T, E, k, T)
+    _, _, ss, sr = oracle.dispatch(idx, E)
+    ys = torch.from_numpy(rng.standard_normal((T * k, emb)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy(rng.random((T, k)).astype(np.float32))
+    y = moe.combine(ys.to(DEV), torch.from_numpy(sr).to(DEV), w.to(DEV), T, k)
+    ref = oracle.combine(bits(ys), sr, w.numpy(), T, k)
+    ref_bits = bits(torch.from_numpy(ref).to(torch.bfloat16))
+    assert bf16_ulp_diff(bits(y), ref_bits) <= 1
+
+
+@pytest.mark.parametrize("k", [2, 3, 4, 8])
+def test_combine_of_permute_with_unit_weights_is_k_x(k):
+    """permute then combine with unit weights: y == bf16(k * x) exactly (exact for k a power of two)."""
+    T, emb, E = 513, 256, 16
+    x = torch.randn((T, emb)).to(torch.bfloat16)
+    idx = torch.from_numpy(_random_idx(T, E, k, k)).to(DEV)
+    out = moe.permute(x.to(DEV), idx, E)
+    y = moe.combine(out["xs"], out["slot_row"], None, T, k)
+    want = (x.float() * k).to(torch.bfloat16)
+    assert np.array_equal(bits(y), bits(want))
+    if k in (2, 4, 8):
+        assert np.array_equal(bf16_values(bits(y)), k * bf16_values(bits(x)))
+
+
+def test_combine_bwd_matches_oracle():
+    T, emb, E, k = 400, 512, 16, 4
+    rng = np.random.default_rng(3)
+    idx = _random_idx(T, E, k, 3)
+    _, _, ss, sr = oracle.dispatch(idx, E)
+    dy = torch.from_numpy(rng.standard_normal((T, emb)).astype(np.float32)).to(torch.bfloat16)
+    ys = torch.from_numpy(rng.standard_normal((T * k, emb)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy(rng.random((T, k)).astype(np.float32))
+    dys, dw = moe.combine_bwd(dy.to(DEV), ys.to(DEV), torch.from_numpy(sr).to(DEV), w.to(DEV), k)
+    r_dys, r_dw = oracle.combine_bwd(bits(dy), bits(ys), sr, w.numpy(), k)
+    # do = bf16(w * dy): one rounding of the same fp32 product
+    assert bf16_ulp_diff(bits(dys), bits(torch.from_numpy(r_dys).to(torch.bfloat16))) <= 1
+    np.testing.assert_allclose(dw.cpu().numpy(), r_dw, rtol=1e-4, atol=1e-3)
+
+
+# ---------------------------------------------------------------- grouped GEMM
+
+def _offsets(M, E, seed, empty=()):
+    rng = np.random.default_rng(seed)
+    sizes = rng.multinomial(M, rng.dirichlet(np.ones(E) * 2)).astype(np.int64)
+    for e in empty:
+        j = (e + 1) % E
+        sizes[j] += sizes[e]
+        sizes[e] = 0
+    return np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+
+
+GEMM_CASES = [  # (M, K, N, E, empty groups)
+    (700, 128, 512, 4, (2,)),
+    (1500, 256, 1536, 6, (0, 5)),
+    (300, 1024, 200, 3, ()),
+    (64, 64, 64, 8, (1, 3, 6)),
+    (2600, 512, 768, 2, ()),
+]
+
+
+@pytest.mark.parametrize("M,K,N,E,empty", GEMM_CASES)
+def test_grouped_gemm_nn_none(M, K, N, E, empty):
+    rng = np.random.default_rng(M)
+    off = _offsets(M, E, M, empty)
+    A = _bf16_dev(rng.standard_normal((M, K)))
+    B = _bf16_dev(rng.standard_normal((E, K, N)) * (0.5 / np.sqrt(K)))
+    C_ = moe.grouped_gemm(A, B, torch.from_numpy(off).to(DEV), op="nn")
+    ref = oracle.grouped_gemm(0, 0, bits(A), bits(B), off)
+    assert_close(to_np(C_), ref, "C")
+
+
+@pytest.mark.parametrize("M,K,N,E,empty", GEMM_CASES)
+def test_grouped_gemm_nn_swiglu_on_prefused_weight(M, K, N, E, empty):
+    N2 = 2 * N
+    rng = np.random.default_rng(M + 1)
+    off = _offsets(M, E, M + 1, empty)
+    A = _bf16_dev(rng.standard_normal((M, K)))
+    B = _bf16_dev(rng.standard_normal((E, K, N2)) * (1.0 / np.sqrt(K)))
+    a, h = moe.grouped_gemm(A, B, torch.from_numpy(off).to(DEV), op="nn", epilogue="swiglu", save_h=True)
+    ref_a = oracle.grouped_gemm(0, 1, bits(A), bits(B), off)
+    ref_h = oracle.grouped_gemm(0, 0, bits(A), bits(B), off)
+    assert_close(to_np(a), ref_a, "a")
+    assert_close(to_np(h), ref_h, "h")
+
+
+@pytest.mark.parametrize("M,K,N,E,empty", GEMM_CASES)
+def test_grouped_gemm_nt_none(M, K, N, E, empty):
+    rng = np.random.default_rng(M + 2)
+    off = _offsets(M, E, M + 2, empty)
+    A = _bf16_dev(rng.standard_normal((M, K)))
+    B = _bf16_dev(rng.standard_normal((E, N, K)) * (0.5 / np.sqrt(K)))
+    C_ = moe.grouped_gemm(A, B, torch.from_numpy(off).to(DEV), op="nt")
+    ref = oracle.grouped_gemm(1, 0, bits(A), bits(B), off)
+    assert_close(to_np(C_), ref, "C")
+
+
+@pytest.mark.parametrize("M,K,N,E,empty", GEMM_CASES)
+def test_grouped_gemm_nt_swiglu_bwd(M, K, N, E, empty):
+    rng = np.random.default_rng(M + 3)
+    off = _offsets(M, E, M + 3, empty)
+    A = _bf16_dev(rng.standard_normal((M, K)))
+    B = _bf16_dev(rng.standard_normal((E, N, K)) * (0.5 / np.sqrt(K)))
+    h = _bf16_dev(rng.standard_normal((M, 2 * N)))
+    dh = moe.grouped_gemm(A, B, torch.from_numpy(off).to(DEV), op="nt", epilogue="swiglu_bwd", aux_in=h)
+    ref = oracle.grouped_gemm(1, 2, bits(A), bits(B), off, aux=bits(h))
+    assert_close(to_np(dh), ref, "dh")
+
+
+def test_grouped_gemm_rows_past_last_group_untouched():
+    M, K, N, E = 600, 128, 256, 3
+    off = np.array([0, 100, 100, 450], np.int32)  # rows 450.. belong to no group
+    A = _bf16_dev(np.random.default_rng(0).standard_normal((M, K)))
+    B = _bf16_dev(np.random.default_rng(1).standard_normal((E, K, N)) * (0.5 / np.sqrt(K)))
+    out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    moe.grouped_gemm(A, B, torch.from_numpy(off).to(DEV), op="nn", out=out)
+    got = to_np(out)
+    assert np.isnan(got[450:]).all() and np.isfinite(got[:450]).all()
+    assert_close(got[:450], oracle.grouped_gemm(0, 0, bits(A), bits(B), off)[:450], "C")
+
+
+@pytest.mark.parametrize("M,P,Q,E,empty", [(700, 128, 512, 4, (2,)), (1000, 256, 200, 5, (0,)),
+                                           (90, 64, 64, 8, (1, 2, 3)), (3000, 768, 256, 3, ())])
+def test_wgrad_matches_oracle_and_zeros_empty_groups(M, P, Q, E, empty):
+    rng = np.random.default_rng(P + Q)
+    off = _offsets(M, E, P + Q, empty)
+    # scaled so that |dW| stays O(1) for groups of up to ~1000 rows
+    A = _bf16_dev(rng.standard_normal((M, P)) * 0.03)
+    D = _bf16_dev(rng.standard_normal((M, Q)) * 0.5)
+    C_ = moe.grouped_gemm_wgrad(A, D, torch.from_numpy(off).to(DEV), E)
+    Cn = to_np(C_)
+    for e in range(E):
+        ref = oracle.grouped_wgrad(bits(A), bits(D), off, e)
+        if off[e] == off[e + 1]:
+            assert (Cn[e] == 0).all()
+        else:
+            assert_close(Cn[e], ref, f"dW[{e}]")
