@@ -1,0 +1,283 @@
+"""Benchmark of the MoE FFN layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gemma4_class]
+                    [--no-cpu-baseline] [--stage-json PATH]
+
+One step = one pass of the whole forward hot path over one batch: route,
+permute, grouped GEMM 1 (prefused wi, SwiGLU epilogue), grouped GEMM 2 (wo),
+combine. The timed loop calls the library's stage entry points in exactly
+the order moe_ffn_fwd does, with HIP events between launches on the stream
+the kernels run on, so every kernel's duration is measured inside the timed
+region. Inputs are resident in HBM before timing starts. Prints ONE JSON line.
+
+With --backward (DeepSeek-V3-shaped workload) the step also runs the layer
+backward (combine-bwd, NT GEMM + SwiGLU-bwd, NT GEMM, permute-bwd, wgrad x2).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_FP32_FMA_TFLOPS = 78.6    # non-packed fp32 FMA: 256 CU x 64 lanes x 2 flop x 2.4 GHz
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+GEMM_SRC = os.path.join(ROOT, "mixture_experts_ffn_group_amd", "csrc", "gemm.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gemma4_class")
+    ap.add_argument("--backward", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--stage-json", default=None, help="also write per-stage details to this file")
+    return ap.parse_args()
+
+
+def source_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this MoE FFN build has no multi-GPU path "
+              "(collectives and sharding are out of scope); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_ffn_group_amd as moe
+    import workloads
+    from mixture_experts_ffn_group_amd import _lib
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = workloads.WORKLOADS[args.workload]
+    T, emb, mlp, E, k, S = wl.T, wl.emb, wl.mlp, wl.E, wl.k, wl.S
+    inp = workloads.make_inputs(wl, device=dev)
+    x, wi, wo, wr, bias, logits = inp["x"], inp["wi"], inp["wo"], inp["wr"], inp["bias"], inp["logits_in"]
+    moe.query_support(T, emb, mlp, E, k)
+    stream = torch.cuda.current_stream(dev)
+
+    # buffers (allocated once, outside the timed region)
+    saved = moe.alloc_saved(T, emb, mlp, E, k, dev)
+    y = torch.empty((T, emb), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(moe.workspace_bytes(T, emb, mlp, E, k), dtype=torch.uint8, device=dev)
+    pws = torch.empty(max(16, int(_lib.lib().moe_permute_workspace_bytes(
+        __import__("ctypes").byref(_lib.shape(T, emb, mlp, E, k))))), dtype=torch.uint8, device=dev)
+    bwd = args.backward
+    if bwd:
+        dy = inp["dy"]
+        bws = torch.empty(moe.workspace_bytes(T, emb, mlp, E, k, backward=True), dtype=torch.uint8, device=dev)
+        grads = dict(dx=torch.empty((T, emb), dtype=torch.bfloat16, device=dev),
+                     dwi=torch.empty_like(wi), dwo=torch.empty_like(wo),
+                     dtopk_w=torch.empty((T, k), dtype=torch.float32, device=dev))
+
+    import ctypes as C
+    L = _lib.lib()
+    shp = _lib.shape(T, emb, mlp, E, k)
+    P = lambda t: None if t is None else C.c_void_p(t.data_ptr())  # noqa: E731
+    st = C.c_void_p(stream.cuda_stream)
+    sv = saved
+
+    def stage_calls():
+        """The forward (and optional backward) as separate library calls, in moe_ffn_fwd order."""
+        calls = [
+            ("route", lambda: L.moe_route(C.byref(shp), None if logits is not None else P(x), P(wr), P(bias),
+                                          P(logits), P(sv["topk_idx"]), P(sv["topk_w"]), st)),
+            ("permute", lambda: L.moe_permute(C.byref(shp), P(x), P(sv["topk_idx"]), P(sv["group_sizes"]),
+                                              P(sv["group_offsets"]), P(sv["sorted_slot"]), P(sv["slot_row"]),
+                                              P(sv["xs"]), P(pws), pws.numel(), st)),
+            ("gemm1_swiglu", lambda: L.moe_grouped_gemm(0, 1, P(sv["xs"]), P(wi), None, P(sv["h"]) if bwd else None,
+                                                        P(sv["group_offsets"]), E, S, emb, 2 * mlp, P(sv["a"]), st)),
+            ("gemm2", lambda: L.moe_grouped_gemm(0, 0, P(sv["a"]), P(wo), None, None, P(sv["group_offsets"]), E, S,
+                                                 mlp, emb, P(sv["o"]), st)),
+            ("combine", lambda: L.moe_combine(C.byref(shp), P(sv["o"]), P(sv["slot_row"]), P(sv["topk_w"]), P(y),
+                                              st)),
+        ]
+        if bwd:
+            calls.append(("backward", lambda: L.moe_ffn_bwd(C.byref(shp), P(dy), C.byref(moe._saved_struct(sv)),
+                                                            P(wi), P(wo), P(grads["dx"]), P(grads["dwi"]),
+                                                            P(grads["dwo"]), P(grads["dtopk_w"]), P(bws), bws.numel(),
+                                                            st)))
+        return calls
+
+    calls = stage_calls()
+
+    def run_step(events=None):
+        for i, (name, f) in enumerate(calls):
+            if events is not None:
+                events[i].record(stream)
+            rc = f()
+            if rc != 0:
+                raise _lib.MoeError(rc, name, L.moe_last_error_detail().decode())
+        if events is not None:
+            events[len(calls)].record(stream)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        run_step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = {name: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+                for i, (name, _) in enumerate(calls)}
+
+    # the fused entry point over the same buffers, as a cross-check of the staged timing
+    fused_ms = None
+    if not bwd:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(2):
+            moe.ffn_fwd(x, wi, wo, k, wr=wr, bias=bias, logits=logits, workspace=ws, out=y)
+        e0.record(stream)
+        for _ in range(args.steps):
+            moe.ffn_fwd(x, wi, wo, k, wr=wr, bias=bias, logits=logits, workspace=ws, out=y)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fused_ms = e0.elapsed_time(e1) / args.steps
+
+    gs = saved["group_sizes"].cpu().numpy()
+    e_nz = int((gs > 0).sum())
+    ms_step = wall * 1e3 / args.steps
+    tokens_per_s = T / (ms_step * 1e-3)
+    fwd_flop = 6.0 * S * emb * mlp              # active-expert FLOPs of the two GEMMs
+    g1_flop, g2_flop = 4.0 * S * emb * mlp, 2.0 * S * mlp * emb
+    g1_bytes = S * emb * 2 + e_nz * emb * 2 * mlp * 2 + S * mlp * 2 * (2 if bwd else 1)
+    g2_bytes = S * mlp * 2 + e_nz * mlp * emb * 2 + S * emb * 2
+    perm_bytes = T * emb * 2 + S * emb * 2 + 12 * S
+    comb_bytes = S * emb * 2 + 8 * S + T * emb * 2
+    route_flop = 0.0 if logits is not None else 2.0 * T * emb * E
+    route_bytes = (T * E * 4 if logits is not None else T * emb * 2 + emb * E * 4) + 8 * S
+
+    def tf(flop, ms):
+        return flop / (ms * 1e-3) / 1e12
+
+    def gb(b, ms):
+        return b / (ms * 1e-3) / 1e9
+
+    stages = {
+        "route": dict(ms=stage_ms["route"], bound="alu" if route_flop else "hbm",
+                      achieved=tf(route_flop, stage_ms["route"]) if route_flop else gb(route_bytes, stage_ms["route"]),
+                      peak=PEAK_FP32_FMA_TFLOPS if route_flop else PEAK_HBM_GBS,
+                      unit="TFLOP/s" if route_flop else "GB/s"),
+        "permute": dict(ms=stage_ms["permute"], bound="hbm", achieved=gb(perm_bytes, stage_ms["permute"]),
+                        peak=PEAK_HBM_GBS, unit="GB/s", bytes=perm_bytes),
+        "gemm1_swiglu": dict(ms=stage_ms["gemm1_swiglu"], bound="mfma",
+                             achieved=tf(g1_flop, stage_ms["gemm1_swiglu"]), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                             flop=g1_flop, bytes=g1_bytes, hbm_gbs=gb(g1_bytes, stage_ms["gemm1_swiglu"])),
+        "gemm2": dict(ms=stage_ms["gemm2"], bound="mfma", achieved=tf(g2_flop, stage_ms["gemm2"]),
+                      peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", flop=g2_flop, bytes=g2_bytes,
+                      hbm_gbs=gb(g2_bytes, stage_ms["gemm2"])),
+        "combine": dict(ms=stage_ms["combine"], bound="hbm", achieved=gb(comb_bytes, stage_ms["combine"]),
+                        peak=PEAK_HBM_GBS, unit="GB/s", bytes=comb_bytes),
+    }
+    if bwd:
+        stages["backward"] = dict(ms=stage_ms["backward"], bound="mfma",
+                                  achieved=tf(12.0 * S * emb * mlp, stage_ms["backward"]), peak=PEAK_BF16_TFLOPS,
+                                  unit="TFLOP/s")
+    for v in stages.values():
+        v["frac"] = v["achieved"] / v["peak"]
+    gemm_ms = stage_ms["gemm1_swiglu"] + stage_ms["gemm2"]
+
+    # dominant kernel: grouped GEMM 1 (prefused wi + SwiGLU epilogue)
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tr = json.load(open(TRAFFIC_FILE))
+            ent = tr.get(args.workload, {}).get("gemm1_swiglu")
+            if ent and ent.get("source_sha") == source_hash(GEMM_SRC):
+                traffic = ent["bytes_per_launch"]
+        except Exception:
+            traffic = None
+    g1 = stages["gemm1_swiglu"]
+    roofline = {"bound": "mfma", "kernel": "gemm_kernel<NN,SWIGLU> (grouped GEMM 1 on prefused wi)",
+                "achieved": round(g1["achieved"], 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(g1["frac"], 4), "traffic": traffic,
+                "per_launch_flop": g1_flop, "avg_launch_ms": round(g1["ms"], 5)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, wl, args.cpu_seconds)
+
+    line = {
+        "metric": "MoE FFN layer tokens/s + achieved bf16 MFMA TFLOP/s, 128 experts top-8",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": T, "emb": emb, "mlp": mlp, "E": E, "k": k,
+                   "pass": "forward+backward" if bwd else "forward", "parallelism": "none (1 GPU)"},
+        "layer_tflops": round(tf(fwd_flop * (3 if bwd else 1), ms_step), 2),
+        "gemm_stage_tflops": round(tf(fwd_flop, gemm_ms), 2),
+        "gemm_stage_frac": round(tf(fwd_flop, gemm_ms) / PEAK_BF16_TFLOPS, 4),
+        "fused_entry_ms": None if fused_ms is None else round(fused_ms, 4),
+        "stages": {k_: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                   for k_, v in stages.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if args.stage_json:
+        json.dump(line, open(args.stage_json, "w"), indent=1)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(inp, wl, target_s: float):
+    """The oracle as it stands, on a bounded token sample of the same workload, on the host cores."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    threads = oracle.default_threads()
+    xb = workloads.bf16_bits(inp["x"])
+    wib = workloads.bf16_bits(inp["wi"])
+    wob = workloads.bf16_bits(inp["wo"])
+    wr = None if inp["wr"] is None else inp["wr"].cpu().numpy()
+    bias = None if inp["bias"] is None else inp["bias"].cpu().numpy()
+    logits = None if inp["logits_in"] is None else inp["logits_in"].cpu().numpy()
+    rng = np.random.default_rng(0)
+
+    def run(n):
+        toks = np.sort(rng.choice(wl.T, n, replace=False))
+        t0 = time.perf_counter()
+        idx, w, _ = oracle.route(xb[toks], wr, bias, wl.k, logits_in=None if logits is None else logits[toks],
+                                 threads=threads)
+        oracle.ffn_fwd_tokens(xb[toks], idx, w, wib, wob, threads=threads)
+        return time.perf_counter() - t0
+
+    n = threads
+    dt = run(n)
+    n = int(max(threads, min(wl.T, n * target_s / max(dt, 1e-3))))
+    dt = run(n)
+    return {"value": round(n / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {wl.T} tokens of {wl.name}: fp32 router + top-k + per-token FFN forward "
+                      f"(fp32 accumulate), {dt:.1f} s on {threads} threads"}
+
+
+if __name__ == "__main__":
+    main()
