@@ -102,9 +102,10 @@ def main():
                                               P(sv["group_offsets"]), P(sv["sorted_slot"]), P(sv["slot_row"]),
                                               P(sv["xs"]), P(pws), pws.numel(), st)),
             ("gemm1_swiglu", lambda: L.moe_grouped_gemm(0, 1, P(sv["xs"]), P(wi), None, P(sv["h"]) if bwd else None,
-                                                        P(sv["group_offsets"]), E, S, emb, 2 * mlp, P(sv["a"]), st)),
+                                                        P(sv["group_offsets"]), E, S, emb, 2 * mlp, None, P(sv["a"]),
+                                                        st)),
             ("gemm2", lambda: L.moe_grouped_gemm(0, 0, P(sv["a"]), P(wo), None, None, P(sv["group_offsets"]), E, S,
-                                                 mlp, emb, P(sv["o"]), st)),
+                                                 mlp, emb, None, P(sv["o"]), st)),
             ("combine", lambda: L.moe_combine(C.byref(shp), P(sv["o"]), P(sv["slot_row"]), P(sv["topk_w"]), P(y),
                                               st)),
         ]
@@ -160,7 +161,7 @@ def main():
     tokens_per_s = T / (ms_step * 1e-3)
     fwd_flop = 6.0 * S * emb * mlp              # active-expert FLOPs of the two GEMMs
     g1_flop, g2_flop = 4.0 * S * emb * mlp, 2.0 * S * mlp * emb
-    g1_bytes = S * emb * 2 + e_nz * emb * 2 * mlp * 2 + S * mlp * 2 * (2 if bwd else 1)
+    g1_bytes = S * emb * 2 + e_nz * emb * 2 * mlp * 2 + S * mlp * 2 + (S * 2 * mlp * 4 if bwd else 0)
     g2_bytes = S * mlp * 2 + e_nz * mlp * emb * 2 + S * emb * 2
     perm_bytes = T * emb * 2 + S * emb * 2 + 12 * S
     comb_bytes = S * emb * 2 + 8 * S + T * emb * 2

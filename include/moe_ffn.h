@@ -125,30 +125,42 @@ int moe_permute(const moe_shape_t* shape, const moe_bf16_t* x, const int32_t* to
                 int32_t* group_offsets, int32_t* sorted_slot, int32_t* slot_row, moe_bf16_t* xs, void* ws,
                 size_t ws_bytes, moe_stream_t stream);
 
+/* Optional row mapping of a grouped GEMM (see moe_grouped_gemm). */
+typedef struct {
+  const int32_t* row_slot;  /* [M] device, or NULL: output row r reads A row row_slot[r] / slot_div */
+  int32_t n_slots;          /* row_slot values lie in [0, n_slots); A then has n_slots / slot_div rows */
+  int32_t slot_div;         /* >= 1 (k when row_slot holds slots t*k + j and A is [T, K]) */
+  const float* slot_scale;  /* device or NULL: output row r is scaled, in fp32 before the epilogue, by
+                               slot_scale[row_slot[r]] ([n_slots]), or by slot_scale[r] ([M]) without row_slot */
+} moe_gemm_rows_t;
+
 /*
  * moe_grouped_gemm -- ragged grouped GEMM over expert groups, bf16 in, fp32
- * accumulate, bf16 out. Row r of A belongs to the expert e with
+ * accumulate, bf16 out. Row r of the output belongs to the expert e with
  * group_offsets[e] <= r < group_offsets[e + 1] (device array [E + 1]); rows
  * at or past group_offsets[E] are not written. Groups may be empty.
  *  op MOE_NN: B is [E, K, N] (B[e] is K x N).  op MOE_NT: B is [E, N, K]
  *  (C = A B[e]^T, the transposed-RHS backward form of "MoE: fused TensorCore
  *  Pallas permute/combine kernels ...", Related PRs, part 3).
- *  A [M, K]. Epilogues:
+ *  A [M, K] bf16, or with rows->row_slot the rows are gathered in place from
+ *  A [n_slots / slot_div, K] (no permuted copy is made).
+ *  Epilogues:
  *   MOE_EPI_NONE: C [M, N].
  *   MOE_EPI_SWIGLU (op NN, N = 2*mlp, the prefused [gate | up] weight of
  *    "Keep fused MoE weights intact through FSDP gather", Description):
  *    C [M, mlp] = silu(h[:, :mlp]) * h[:, mlp:] with h = A B[e] kept in fp32;
- *    aux_out [M, 2*mlp] bf16 receives h when non-NULL (saved for backward).
+ *    aux_out [M, 2*mlp] fp32 receives h when non-NULL (saved for backward).
  *   MOE_EPI_SWIGLU_BWD (op NT, N = mlp): da = A B[e]^T; aux_in = saved h
- *    [M, 2*mlp]; C [M, 2*mlp] = [da*u*s*(1 + g*(1 - s)) | da*silu(g)] with
- *    g = h[:, :mlp], u = h[:, mlp:], s = sigmoid(g) -- one concatenated
+ *    [M, 2*mlp] fp32; C [M, 2*mlp] = [da*u*s*(1 + g*(1 - s)) | da*silu(g)]
+ *    with g = h[:, :mlp], u = h[:, mlp:], s = sigmoid(g) -- one concatenated
  *    gradient, as in the gate/up split VJP of "Gemma4 26B MoE on TPU v6e",
  *    Commits table, commit 7.
+ *  rows: NULL, or a row gather and/or per-row fp32 scale (moe_gemm_rows_t).
  *  Needs K % 64 == 0, N % 8 == 0 (SWIGLU: mlp % 8 == 0), M < 2^31.
  */
-int moe_grouped_gemm(int op, int epilogue, const moe_bf16_t* A, const moe_bf16_t* B, const moe_bf16_t* aux_in,
-                     moe_bf16_t* aux_out, const int32_t* group_offsets, int32_t E, int64_t M, int32_t K, int32_t N,
-                     moe_bf16_t* C, moe_stream_t stream);
+int moe_grouped_gemm(int op, int epilogue, const moe_bf16_t* A, const moe_bf16_t* B, const float* aux_in,
+                     float* aux_out, const int32_t* group_offsets, int32_t E, int64_t M, int32_t K, int32_t N,
+                     const moe_gemm_rows_t* rows, moe_bf16_t* C, moe_stream_t stream);
 
 /*
  * moe_grouped_gemm_wgrad -- weight gradient of a grouped GEMM: for every
@@ -184,8 +196,9 @@ int moe_combine_bwd(const moe_shape_t* shape, const moe_bf16_t* dy, const moe_bf
 
 /* Caller-owned activations of one forward pass, kept for the backward. All
    device pointers: topk_idx [T,k], topk_w [T,k], group_sizes [E],
-   group_offsets [E+1], sorted_slot [S], slot_row [S], xs [S,emb],
-   h [S,2*mlp], a [S,mlp], o [S,emb]. */
+   group_offsets [E+1], sorted_slot [S], slot_row [S], xs [S,emb] bf16,
+   h [S,2*mlp] fp32 (the gate/up pre-activations, unrounded), a [S,mlp] bf16,
+   o [S,emb] bf16. */
 typedef struct {
   int32_t* topk_idx;
   float* topk_w;
@@ -194,7 +207,7 @@ typedef struct {
   int32_t* sorted_slot;
   int32_t* slot_row;
   moe_bf16_t* xs;
-  moe_bf16_t* h;
+  float* h;
   moe_bf16_t* a;
   moe_bf16_t* o;
 } moe_saved_t;
@@ -217,6 +230,8 @@ int moe_ffn_fwd(const moe_shape_t* shape, const moe_bf16_t* x, const float* wr, 
  * the loss sum(dy * y): combine backward, NT grouped GEMM on wo with the
  * SwiGLU-backward epilogue, NT grouped GEMM on wi, permute backward
  * (combine with unit weights), and the two weight-gradient grouped GEMMs.
+ * The wo GEMM reads dy rows in place through sorted_slot and applies each
+ * row's top-k weight in fp32, so its input is never rounded after scaling.
  *  dy [T, emb] bf16; saved from a moe_ffn_fwd call with the same shape and
  *  weights. Outputs (each may be NULL to skip it): dx [T, emb] bf16,
  *  dwi [E, emb, 2*mlp] bf16, dwo [E, mlp, emb] bf16, dtopk_w [T, k] fp32.

@@ -18,8 +18,8 @@ import ctypes as C
 import torch
 
 from . import _lib
-from ._lib import (MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_SWIGLU_BWD, MOE_NN, MOE_NT, MoeError, MoeSaved,  # noqa: F401
-                   MoeShape)
+from ._lib import (MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_SWIGLU_BWD, MOE_NN, MOE_NT, MoeError,  # noqa: F401
+                   MoeGemmRows, MoeSaved, MoeShape)
 
 __all__ = ["route", "permute", "grouped_gemm", "grouped_gemm_wgrad", "combine", "combine_bwd", "ffn_fwd", "ffn_bwd",
            "query_support", "workspace_bytes", "MoeError"]
@@ -111,23 +111,36 @@ def permute(x: torch.Tensor, topk_idx: torch.Tensor, E: int) -> dict:
 
 def grouped_gemm(A: torch.Tensor, B: torch.Tensor, group_offsets: torch.Tensor, op: str = "nn",
                  epilogue: str = "none", aux_in: torch.Tensor | None = None, save_h: bool = False,
-                 out: torch.Tensor | None = None):
-    """Ragged grouped GEMM (see moe_grouped_gemm). Returns C, or (C, h) with save_h (SwiGLU only)."""
+                 out: torch.Tensor | None = None, row_slot: torch.Tensor | None = None, slot_div: int = 1,
+                 slot_scale: torch.Tensor | None = None, M: int | None = None):
+    """Ragged grouped GEMM (see moe_grouped_gemm). Returns C, or (C, h) with save_h (SwiGLU, h in fp32).
+
+    row_slot [M] int32 (optional): output row r reads A row row_slot[r] // slot_div (A is not permuted).
+    slot_scale (optional, fp32): per-row scale, indexed by row_slot[r] (or r)."""
     _need(A, "A", torch.bfloat16)
     dev = A.device
     _need(B, "B", torch.bfloat16, dev)
     _need(group_offsets, "group_offsets", torch.int32, dev)
-    _need(aux_in, "aux_in", torch.bfloat16, dev)
-    M, K = A.shape
+    _need(aux_in, "aux_in", torch.float32, dev)
+    _need(row_slot, "row_slot", torch.int32, dev)
+    _need(slot_scale, "slot_scale", torch.float32, dev)
+    K = A.shape[1]
+    if M is None:
+        M = row_slot.numel() if row_slot is not None else A.shape[0]
     E = B.shape[0]
     N = B.shape[2] if op == "nn" else B.shape[1]
     epi = _EPI[epilogue]
     width = N if epi == MOE_EPI_NONE else (N // 2 if epi == MOE_EPI_SWIGLU else 2 * N)
     C_ = out if out is not None else torch.empty((M, width), dtype=torch.bfloat16, device=dev)
     _need(C_, "out", torch.bfloat16, dev)
-    h = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if (save_h and epi == MOE_EPI_SWIGLU) else None
+    h = torch.empty((M, N), dtype=torch.float32, device=dev) if (save_h and epi == MOE_EPI_SWIGLU) else None
+    rows = None
+    if row_slot is not None or slot_scale is not None:
+        n_slots = A.shape[0] * slot_div if row_slot is not None else 0
+        rows = C.byref(MoeGemmRows(None if row_slot is None else row_slot.data_ptr(), n_slots, slot_div,
+                                   None if slot_scale is None else slot_scale.data_ptr()))
     _lib.check(_lib.lib().moe_grouped_gemm(_OP[op], epi, _ptr(A), _ptr(B), _ptr(aux_in), _ptr(h), _ptr(group_offsets),
-                                           E, M, K, N, _ptr(C_), _stream(dev)), "moe_grouped_gemm")
+                                           E, M, K, N, rows, _ptr(C_), _stream(dev)), "moe_grouped_gemm")
     return (C_, h) if save_h else C_
 
 
@@ -188,7 +201,7 @@ def alloc_saved(T: int, emb: int, mlp: int, E: int, k: int, device) -> dict:
                 sorted_slot=torch.empty(S, dtype=i32, device=device),
                 slot_row=torch.empty(S, dtype=i32, device=device),
                 xs=torch.empty((S, emb), dtype=bf, device=device),
-                h=torch.empty((S, 2 * mlp), dtype=bf, device=device),
+                h=torch.empty((S, 2 * mlp), dtype=f32, device=device),
                 a=torch.empty((S, mlp), dtype=bf, device=device),
                 o=torch.empty((S, emb), dtype=bf, device=device))
 

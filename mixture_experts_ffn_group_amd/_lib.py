@@ -33,6 +33,11 @@ class MoeSaved(C.Structure):
                                            "slot_row", "xs", "h", "a", "o")]
 
 
+class MoeGemmRows(C.Structure):
+    _fields_ = [("row_slot", C.c_void_p), ("n_slots", C.c_int32), ("slot_div", C.c_int32),
+                ("slot_scale", C.c_void_p)]
+
+
 _SHP = C.POINTER(MoeShape)
 SIGNATURES = {
     "moe_status_str": ([C.c_int], C.c_char_p),
@@ -43,7 +48,8 @@ SIGNATURES = {
     "moe_workspace_bytes": ([_SHP, C.c_int], _sz),
     "moe_route": ([_SHP, _p, _p, _p, _p, _p, _p, _p], C.c_int),
     "moe_permute": ([_SHP, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p], C.c_int),
-    "moe_grouped_gemm": ([C.c_int, C.c_int, _p, _p, _p, _p, _p, _i32, _i64, _i32, _i32, _p, _p], C.c_int),
+    "moe_grouped_gemm": ([C.c_int, C.c_int, _p, _p, _p, _p, _p, _i32, _i64, _i32, _i32, C.POINTER(MoeGemmRows), _p,
+                          _p], C.c_int),
     "moe_grouped_gemm_wgrad": ([_p, _p, _p, _i32, _i64, _i32, _i32, _p, _p], C.c_int),
     "moe_combine": ([_SHP, _p, _p, _p, _p, _p], C.c_int),
     "moe_combine_bwd": ([_SHP, _p, _p, _p, _p, _p, _p, _p], C.c_int),

@@ -47,11 +47,14 @@ enum { EPI_NONE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_BWD = 2 };
 struct GemmP {
   const uint16_t* A;
   const uint16_t* B;
-  const uint16_t* aux_in;
-  uint16_t* aux_out;
+  const float* aux_in;   // SWIGLU_BWD: saved h [M, 2N] fp32
+  float* aux_out;        // SWIGLU: h [M, N] fp32 (optional)
   uint16_t* C;
   const int32_t* off;
+  const int32_t* row_slot;  // optional: A row of output row r is row_slot[r] / slot_div
+  const float* slot_scale;  // optional: output row r is scaled by slot_scale[row_slot[r]] (or [r])
   int E, M, K, N;
+  int n_slots, slot_div;
 };
 
 struct WgradP {
@@ -179,11 +182,22 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmP p) {
 
     // Per-tile operand bases with 32-bit offsets. Rows past the group end are
     // clamped to its last row and columns past N to a valid column: both only
-    // feed outputs that are never stored.
-    const uint16_t* Ab = p.A + (int64_t)m0 * p.K;
+    // feed outputs that are never stored. With a row gather, A rows are read in
+    // place through the slot index (no permuted copy of A).
+    const uint16_t* Ab;
     int a_off[8];
+    if (p.row_slot) {
+      Ab = p.A;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a_off[i] = (min(m0 + ra + 32 * i, m_end - 1) - m0) * p.K + ca * 8;
+      for (int i = 0; i < 8; ++i) {
+        const int s = min(max(p.row_slot[min(m0 + ra + 32 * i, m_end - 1)], 0), p.n_slots - 1);
+        a_off[i] = (s / p.slot_div) * p.K + ca * 8;
+      }
+    } else {
+      Ab = p.A + (int64_t)m0 * p.K;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a_off[i] = (min(m0 + ra + 32 * i, m_end - 1) - m0) * p.K + ca * 8;
+    }
     int b_off[8];
     if (OP == OP_NT) {
 #pragma unroll
@@ -265,6 +279,14 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmP p) {
     for (int i = 0; i < 4; ++i) {
       const int m = m0 + wm * 128 + i * 32 + (lane & 31);
       if (m >= m_end) continue;
+      if (p.slot_scale) {  // per-row scale in fp32 (e.g. the top-k weight of the row's slot)
+        const int s = p.row_slot ? min(max(p.row_slot[m], 0), p.n_slots - 1) : m;
+        const float sc = p.slot_scale[s];
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][f][r] *= sc;
+      }
       if (EPI == EPI_NONE) {
         uint16_t* crow = p.C + (int64_t)m * p.N;
 #pragma unroll
@@ -277,7 +299,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmP p) {
           }
       } else if (EPI == EPI_SWIGLU) {
         uint16_t* arow = p.C + (int64_t)m * mlp;
-        uint16_t* hrow = p.aux_out ? p.aux_out + (int64_t)m * 2 * mlp : nullptr;
+        float* hrow = p.aux_out ? p.aux_out + (int64_t)m * 2 * mlp : nullptr;
 #pragma unroll
         for (int f = 0; f < 2; ++f)
 #pragma unroll
@@ -288,14 +310,19 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmP p) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) a[u] = silu_f(acc[i][f][4 * q + u]) * acc[i][f + 2][4 * q + u];
             st8(arow + col, pack4(a[0], a[1], a[2], a[3]));
-            if (hrow) {
-              st8(hrow + col, pack4(acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]));
-              st8(hrow + mlp + col, pack4(acc[i][f + 2][4 * q], acc[i][f + 2][4 * q + 1], acc[i][f + 2][4 * q + 2],
-                                          acc[i][f + 2][4 * q + 3]));
+            if (hrow) {  // h kept in fp32 for the backward: the gate/up values the SwiGLU used, unrounded
+              f32x4_t gv, uv;
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                gv[u] = acc[i][f][4 * q + u];
+                uv[u] = acc[i][f + 2][4 * q + u];
+              }
+              *reinterpret_cast<f32x4_t*>(hrow + col) = gv;
+              *reinterpret_cast<f32x4_t*>(hrow + mlp + col) = uv;
             }
           }
       } else {  // EPI_SWIGLU_BWD: N = mlp, aux = saved h [M, 2N], C = dh [M, 2N]
-        const uint16_t* hrow = p.aux_in + (int64_t)m * 2 * p.N;
+        const float* hrow = p.aux_in + (int64_t)m * 2 * p.N;
         uint16_t* drow = p.C + (int64_t)m * 2 * p.N;
 #pragma unroll
         for (int f = 0; f < 4; ++f)
@@ -303,10 +330,8 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmP p) {
           for (int q = 0; q < 4; ++q) {
             const int n = n0 + wn * 128 + f * 32 + 8 * q + 4 * hh;
             if (n >= p.N) continue;
-            const u32x2_t gv = *reinterpret_cast<const u32x2_t*>(hrow + n);
-            const u32x2_t uv = *reinterpret_cast<const u32x2_t*>(hrow + p.N + n);
-            const float g[4] = {bf16_lo(gv[0]), bf16_hi(gv[0]), bf16_lo(gv[1]), bf16_hi(gv[1])};
-            const float u[4] = {bf16_lo(uv[0]), bf16_hi(uv[0]), bf16_lo(uv[1]), bf16_hi(uv[1])};
+            const f32x4_t g = *reinterpret_cast<const f32x4_t*>(hrow + n);
+            const f32x4_t u = *reinterpret_cast<const f32x4_t*>(hrow + p.N + n);
             float dg[4], du[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -432,11 +457,13 @@ int persistent_grid() {
 
 }  // namespace
 
-hipError_t launch_grouped_gemm(int op, int epi, const uint16_t* A, const uint16_t* B, const uint16_t* aux_in,
-                               uint16_t* aux_out, const int32_t* group_offsets, int E, int64_t M, int K, int N,
+hipError_t launch_grouped_gemm(int op, int epi, const uint16_t* A, const uint16_t* B, const float* aux_in,
+                               float* aux_out, const int32_t* group_offsets, int E, int64_t M, int K, int N,
+                               const int32_t* row_slot, int n_slots, int slot_div, const float* slot_scale,
                                uint16_t* C, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  GemmP p{A, B, aux_in, aux_out, C, group_offsets, E, (int)M, K, N};
+  GemmP p{A, B, aux_in, aux_out, C, group_offsets, row_slot, slot_scale, E, (int)M, K, N,
+          row_slot ? n_slots : (int)M, slot_div > 0 ? slot_div : 1};
   const dim3 grid(persistent_grid()), block(NTHR);
   if (op == OP_NN && epi == EPI_NONE) gemm_kernel<OP_NN, EPI_NONE><<<grid, block, 0, stream>>>(p);
   else if (op == OP_NN && epi == EPI_SWIGLU) gemm_kernel<OP_NN, EPI_SWIGLU><<<grid, block, 0, stream>>>(p);

@@ -208,9 +208,9 @@ int moe_permute(const moe_shape_t* s, const moe_bf16_t* x, const int32_t* topk_i
                     "moe_permute");
 }
 
-int moe_grouped_gemm(int op, int epilogue, const moe_bf16_t* A, const moe_bf16_t* B, const moe_bf16_t* aux_in,
-                     moe_bf16_t* aux_out, const int32_t* group_offsets, int32_t E, int64_t M, int32_t K, int32_t N,
-                     moe_bf16_t* C, moe_stream_t stream) {
+int moe_grouped_gemm(int op, int epilogue, const moe_bf16_t* A, const moe_bf16_t* B, const float* aux_in,
+                     float* aux_out, const int32_t* group_offsets, int32_t E, int64_t M, int32_t K, int32_t N,
+                     const moe_gemm_rows_t* rows, moe_bf16_t* C, moe_stream_t stream) {
   g_detail[0] = 0;
   if (int rc = check_gemm(op, epilogue, M, K, N, E)) return rc;
   NEED(B);
@@ -221,8 +221,24 @@ int moe_grouped_gemm(int op, int epilogue, const moe_bf16_t* A, const moe_bf16_t
   }
   if (epilogue == MOE_EPI_SWIGLU_BWD) NEED(aux_in);
   if (epilogue == MOE_EPI_SWIGLU) MAYBE(aux_out);
+  const int32_t* row_slot = nullptr;
+  const float* slot_scale = nullptr;
+  int n_slots = 0, slot_div = 1;
+  if (rows) {
+    row_slot = rows->row_slot;
+    slot_scale = rows->slot_scale;
+    n_slots = rows->n_slots;
+    slot_div = rows->slot_div;
+    MAYBE(slot_scale);
+    if (row_slot) {
+      if (n_slots <= 0 || slot_div <= 0) return fail(MOE_ERR_SHAPE, "row gather needs n_slots > 0 and slot_div > 0");
+      if ((int64_t)(n_slots / slot_div) * K >= (int64_t(1) << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "gathered A too large (rows*K >= 2^31)");
+    }
+  }
   return hip_status(moe::launch_grouped_gemm(op, epilogue, A, B, aux_in, epilogue == MOE_EPI_SWIGLU ? aux_out : nullptr,
-                                             group_offsets, E, M, K, N, C, (hipStream_t)stream),
+                                             group_offsets, E, M, K, N, row_slot, n_slots, slot_div, slot_scale, C,
+                                             (hipStream_t)stream),
                     "moe_grouped_gemm");
 }
 
@@ -338,11 +354,11 @@ int moe_ffn_fwd(const moe_shape_t* s, const moe_bf16_t* x, const float* wr, cons
                           "permute"))
     return rc;
   if (int rc = hip_status(moe::launch_grouped_gemm(MOE_NN, MOE_EPI_SWIGLU, v.xs, wi, nullptr, v.h, v.group_offsets, E,
-                                                   S, emb, 2 * mlp, v.a, st),
+                                                   S, emb, 2 * mlp, nullptr, 0, 1, nullptr, v.a, st),
                           "gemm1"))
     return rc;
   if (int rc = hip_status(moe::launch_grouped_gemm(MOE_NN, MOE_EPI_NONE, v.a, wo, nullptr, nullptr, v.group_offsets,
-                                                   E, S, mlp, emb, v.o, st),
+                                                   E, S, mlp, emb, nullptr, 0, 1, nullptr, v.o, st),
                           "gemm2"))
     return rc;
   return hip_status(moe::launch_combine(T, emb, k, v.o, v.slot_row, v.topk_w, y, st), "combine");
@@ -358,6 +374,7 @@ int moe_ffn_bwd(const moe_shape_t* s, const moe_bf16_t* dy, const moe_saved_t* s
   if (s->T > 0) {  // with no tokens, per-token buffers may be empty (NULL)
     NEED(dy);
     NEED(saved->topk_w);
+    NEED(saved->sorted_slot);
     NEED(saved->slot_row);
     NEED(saved->xs);
     NEED(saved->h);
@@ -389,8 +406,10 @@ int moe_ffn_bwd(const moe_shape_t* s, const moe_bf16_t* dy, const moe_saved_t* s
       return rc;
   }
   if (!dx && !dwi) return MOE_OK;
-  if (int rc = hip_status(moe::launch_grouped_gemm(MOE_NT, MOE_EPI_SWIGLU_BWD, d_o, wo, saved->h, nullptr,
-                                                   saved->group_offsets, E, S, emb, mlp, dh, st),
+  // da = w * (dy . wo[e]^T): dy rows read in place through sorted_slot, the top-k weight applied in fp32
+  if (int rc = hip_status(moe::launch_grouped_gemm(MOE_NT, MOE_EPI_SWIGLU_BWD, dy, wo, saved->h, nullptr,
+                                                   saved->group_offsets, E, S, emb, mlp, saved->sorted_slot, (int)S, k,
+                                                   saved->topk_w, dh, st),
                           "dh"))
     return rc;
   if (dwi) {
@@ -400,7 +419,8 @@ int moe_ffn_bwd(const moe_shape_t* s, const moe_bf16_t* dy, const moe_saved_t* s
   }
   if (dx) {
     if (int rc = hip_status(moe::launch_grouped_gemm(MOE_NT, MOE_EPI_NONE, dh, wi, nullptr, nullptr,
-                                                     saved->group_offsets, E, S, 2 * mlp, emb, dxs, st),
+                                                     saved->group_offsets, E, S, 2 * mlp, emb, nullptr, 0, 1, nullptr,
+                                                     dxs, st),
                             "dxs"))
       return rc;
     if (int rc = hip_status(moe::launch_combine(T, emb, k, dxs, saved->slot_row, nullptr, dx, st), "dx")) return rc;

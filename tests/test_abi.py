@@ -97,17 +97,17 @@ def test_validation_precedes_any_launch(lib):
     assert lib.moe_permute(C.byref(s), fake, fake, fake, fake, fake, fake, fake, nul, 1 << 20, nul) == \
         _lib.MOE_ERR_NULL
     # grouped GEMM: bad op, wrong epilogue/op pairs, K not a multiple of 64, N not a multiple of 8
-    assert lib.moe_grouped_gemm(7, 0, fake, fake, nul, nul, fake, 4, 128, 64, 64, fake, nul) == _lib.MOE_ERR_SHAPE
-    assert lib.moe_grouped_gemm(1, 1, fake, fake, nul, nul, fake, 4, 128, 64, 64, fake, nul) == \
+    assert lib.moe_grouped_gemm(7, 0, fake, fake, nul, nul, fake, 4, 128, 64, 64, None, fake, nul) == _lib.MOE_ERR_SHAPE
+    assert lib.moe_grouped_gemm(1, 1, fake, fake, nul, nul, fake, 4, 128, 64, 64, None, fake, nul) == \
         _lib.MOE_ERR_UNSUPPORTED
-    assert lib.moe_grouped_gemm(0, 2, fake, fake, fake, nul, fake, 4, 128, 64, 64, fake, nul) == \
+    assert lib.moe_grouped_gemm(0, 2, fake, fake, fake, nul, fake, 4, 128, 64, 64, None, fake, nul) == \
         _lib.MOE_ERR_UNSUPPORTED
-    assert lib.moe_grouped_gemm(0, 0, fake, fake, nul, nul, fake, 4, 128, 96, 64, fake, nul) == \
+    assert lib.moe_grouped_gemm(0, 0, fake, fake, nul, nul, fake, 4, 128, 96, 64, None, fake, nul) == \
         _lib.MOE_ERR_UNSUPPORTED
-    assert lib.moe_grouped_gemm(0, 0, fake, fake, nul, nul, fake, 4, 128, 64, 60, fake, nul) == \
+    assert lib.moe_grouped_gemm(0, 0, fake, fake, nul, nul, fake, 4, 128, 64, 60, None, fake, nul) == \
         _lib.MOE_ERR_UNSUPPORTED
-    assert lib.moe_grouped_gemm(1, 2, fake, fake, nul, nul, fake, 4, 128, 64, 64, fake, nul) == _lib.MOE_ERR_NULL
-    assert lib.moe_grouped_gemm(0, 0, fake, fake, nul, nul, fake, 300, 128, 64, 64, fake, nul) == \
+    assert lib.moe_grouped_gemm(1, 2, fake, fake, nul, nul, fake, 4, 128, 64, 64, None, fake, nul) == _lib.MOE_ERR_NULL
+    assert lib.moe_grouped_gemm(0, 0, fake, fake, nul, nul, fake, 300, 128, 64, 64, None, fake, nul) == \
         _lib.MOE_ERR_UNSUPPORTED
     assert lib.moe_grouped_gemm_wgrad(fake, fake, fake, 4, 128, 12, 64, fake, nul) == _lib.MOE_ERR_UNSUPPORTED
     assert lib.moe_grouped_gemm_wgrad(fake, fake, nul, 4, 128, 64, 64, fake, nul) == _lib.MOE_ERR_NULL

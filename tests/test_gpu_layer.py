@@ -14,7 +14,7 @@ import torch
 import mixture_experts_ffn_group_amd as moe
 import oracle
 import workloads
-from parity_util import W_ABS, assert_close, bits, to_np
+from parity_util import W_ABS, assert_close, assert_close_wgrad, bits, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -130,8 +130,8 @@ def test_layer_backward_every_token_and_expert():
     assert_close(to_np(g["dx"]), dx, "dx")
     assert_close(g["dtopk_w"].cpu().numpy(), dtw, "dtopk_w")
     ref = oracle.ffn_wgrad_experts(x, r_idx, r_w, wi, wo, dy, range(wl.E))
-    assert_close(to_np(g["dwi"]), np.stack([ref[e][0] for e in range(wl.E)]), "dwi")
-    assert_close(to_np(g["dwo"]), np.stack([ref[e][1] for e in range(wl.E)]), "dwo")
+    assert_close_wgrad(to_np(g["dwi"]), np.stack([ref[e][0] for e in range(wl.E)]), "dwi")
+    assert_close_wgrad(to_np(g["dwo"]), np.stack([ref[e][1] for e in range(wl.E)]), "dwo")
     # skipping outputs leaves the others unchanged
     g2 = moe.ffn_bwd(d["dy"], saved, d["wi"], d["wo"], wl.k, need=("dx",))
     assert torch.equal(g2["dx"].view(torch.int16), g["dx"].view(torch.int16))
@@ -181,5 +181,5 @@ def test_full_size_deepseek_v3_shape_forward_backward_sampled():
     experts = [int(e) for e in np.argsort(gs, kind="stable")[:2]]
     ref = oracle.ffn_wgrad_experts(x, r_idx, r_w, wi, wo, dy, experts)
     for e in experts:
-        assert_close(to_np(g["dwi"][e]), ref[e][0], f"dwi[{e}]")
-        assert_close(to_np(g["dwo"][e]), ref[e][1], f"dwo[{e}]")
+        assert_close_wgrad(to_np(g["dwi"][e]), ref[e][0], f"dwi[{e}]")
+        assert_close_wgrad(to_np(g["dwo"][e]), ref[e][1], f"dwo[{e}]")

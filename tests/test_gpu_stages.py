@@ -237,10 +237,34 @@ def test_grouped_gemm_nt_swiglu_bwd(M, K, N, E, empty):
     off = _offsets(M, E, M + 3, empty)
     A = _bf16_dev(rng.standard_normal((M, K)))
     B = _bf16_dev(rng.standard_normal((E, N, K)) * (0.5 / np.sqrt(K)))
-    h = _bf16_dev(rng.standard_normal((M, 2 * N)) * 0.5)
-    dh = moe.grouped_gemm(A, B, torch.from_numpy(off).to(DEV), op="nt", epilogue="swiglu_bwd", aux_in=h)
-    ref = oracle.grouped_gemm(1, 2, bits(A), bits(B), off, aux=bits(h))
+    h = (rng.standard_normal((M, 2 * N)) * 0.5).astype(np.float32)  # saved h is fp32
+    dh = moe.grouped_gemm(A, B, torch.from_numpy(off).to(DEV), op="nt", epilogue="swiglu_bwd",
+                          aux_in=torch.from_numpy(h).to(DEV))
+    ref = oracle.grouped_gemm(1, 2, bits(A), bits(B), off, aux=h)
     assert_close(to_np(dh), ref, "dh")
+
+
+@pytest.mark.parametrize("op,epi", [("nn", "none"), ("nn", "swiglu"), ("nt", "none"), ("nt", "swiglu_bwd")])
+def test_grouped_gemm_row_gather_and_row_scale(op, epi):
+    """Rows read in place from A [T, K] through slots t*k + j, each output row scaled by w[slot] in fp32:
+    equal to the oracle GEMM on the gathered, scaled rows (scaling a bf16 value is exact in fp64)."""
+    T, K, N, E, k = 400, 256, 320, 6, 3
+    rng = np.random.default_rng(21)
+    idx = _random_idx(T, E, k, 21)
+    gs, off, ss, sr = oracle.dispatch(idx, E)
+    A = _bf16_dev(rng.standard_normal((T, K)))
+    Nb = 2 * N if epi == "swiglu" else N
+    B = _bf16_dev(rng.standard_normal((E, K, Nb) if op == "nn" else (E, Nb, K)) * (0.5 / np.sqrt(K)))
+    w = rng.random(T * k).astype(np.float32)
+    h = (rng.standard_normal((T * k, 2 * N)) * 0.5).astype(np.float32)
+    got = moe.grouped_gemm(A, B, torch.from_numpy(off).to(DEV), op=op, epilogue=epi,
+                           aux_in=torch.from_numpy(h).to(DEV) if epi == "swiglu_bwd" else None,
+                           row_slot=torch.from_numpy(ss).to(DEV), slot_div=k, slot_scale=torch.from_numpy(w).to(DEV))
+    A_rows = bf16_values(bits(A))[ss // k] * w[ss].astype(np.float64)[:, None]
+    ref = oracle.grouped_gemm(0 if op == "nn" else 1, {"none": 0, "swiglu": 1, "swiglu_bwd": 2}[epi],
+                              np.ascontiguousarray(A_rows), bits(B), off, aux=h if epi == "swiglu_bwd" else None,
+                              real="f64")
+    assert_close(to_np(got), ref, f"{op}/{epi}")
 
 
 def test_grouped_gemm_rows_past_last_group_untouched():
