@@ -17,27 +17,38 @@
 // permute/combine kernels ...", Tests: boundary-tile masking).
 //
 // Design (gfx950):
-//  - Workgroup tile 256 x 256 x 64, 4 waves in 2 x 2, each wave 128 x 128 =
-//    4 x 4 MFMA 32x32x16 bf16 blocks (256 fp32 accumulators per lane).
-//  - A and B stages double-buffered in LDS (128 KB). Global loads of the next
-//    k-slice are in flight while the current slice feeds the MFMAs.
+//  - Workgroup tile 256 x 256, k-slice 32, 8 waves in 2 (M) x 4 (N); each wave
+//    owns 128 x 64 outputs = 4 x 2 MFMA 32x32x16 bf16 blocks (128 fp32
+//    accumulators per lane), which leaves room for two waves per SIMD.
+//  - Operands go global -> LDS with direct loads (global_load_lds_dwordx4,
+//    1 KB per instruction) into a ring of four LDS stages, so three k-slices
+//    are in flight ahead of the one being multiplied.
+//  - [k][n]-major tiles (the NN weight, both wgrad operands) are read with the
+//    gfx950 transposed LDS read ds_read_b64_tr_b16, [row][k]-major tiles with
+//    ds_read_b128. Both layouts are XOR-swizzled on 16-byte chunks for the
+//    64-bank LDS. The swizzle is applied to the global address each lane
+//    copies, since a direct load writes 1 KB of LDS contiguously.
+//  - LDS reads of the next 16-wide sub-slice are issued one per MFMA.
 //  - The weight side is the MFMA's first operand, so each lane ends with four
-//    consecutive output columns per register group (8-byte stores).
-//  - [k][n]-major B tiles (the NN weight, both wgrad operands) are read with
-//    the gfx950 transposed LDS read ds_read_b64_tr_b16; [n][k]-major tiles with
-//    ds_read_b128. Both layouts are XOR-swizzled on 16-byte chunks so the
-//    reads are bank-conflict free.
+//    consecutive output columns per register group. The epilogue stages each
+//    32 x 32 block through LDS and stores whole 64-byte row segments.
 //  - Persistent grid of one workgroup per CU. Each workgroup derives the
 //    ragged tile list from the device-side group offsets itself (no host
 //    sync). Tiles are numbered expert-major and dealt so that each XCD works
-//    on a contiguous run of tiles that share A and B panels in its L2.
+//    on a contiguous run of tiles that share A and B panels in its L2; the
+//    first k-slices of a workgroup's next tile are loaded during the epilogue
+//    of the current one.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64, NTHR = 256;
+constexpr int BM = 256, BN = 256;
+// weight-gradient kernel: k-slice of 64 rows, 4 waves, two register-staged LDS stages
+constexpr int BK = 64, NTHR = 256;
 constexpr int kStageBytes = BM * BK * 2;  // one operand, one stage: 32 KB
 constexpr int kLdsBytes = 4 * kStageBytes;
 
@@ -65,10 +76,11 @@ struct WgradP {
   int E, M, P, Q;
 };
 
-// Tiles whose rows hold 8 16-byte chunks (64 bf16 along k): A [BM][BK], NT-B [BN][BK].
-__device__ __forceinline__ int off_k8(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
-// Tiles whose rows hold 32 chunks (256 bf16 along n): NN-B [BK][BN], wgrad [BK][256].
-__device__ __forceinline__ int off_n32(int krow, int c) { return krow * 512 + ((c ^ ((krow & 3) << 1)) << 4); }
+// LDS swizzle of [k][n] tiles, 512-byte rows of 32 16-byte chunks (NN weight
+// [32][256], wgrad [64][256]): a transposed read covers 4 k-rows x 64 bytes
+// per 16 lanes, and physical chunk = c ^ ((k & 3) << 2) moves each of those
+// k-rows to its own quarter of the 256-byte bank window.
+__device__ __forceinline__ int off_n32(int krow, int c) { return krow * 512 + ((c ^ ((krow & 3) << 2)) << 4); }
 
 __device__ __forceinline__ bf16x8_t lds_rd16(const uint8_t* base, int off) {
   return *reinterpret_cast<const bf16x8_t*>(base + off);
@@ -91,9 +103,31 @@ __device__ __forceinline__ bf16x8_t frag_tr(const uint8_t* tile, int lane, int k
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// MFMA operand from a [row][k] tile: lane l gets row rbase + l%32, k values k0 + 8*(l/32) + 0..7.
-__device__ __forceinline__ bf16x8_t frag_k(const uint8_t* tile, int lane, int k0, int rbase) {
-  return lds_rd16(tile, off_k8(rbase + (lane & 31), (k0 >> 3) + (lane >> 5)));
+// Direct global->LDS copy, 16 bytes per lane: lane L's 16 bytes at sbase + voff
+// land at LDS byte address lds + 16 L (global_load_lds_dwordx4, M0 = lds).
+// Issued from inline asm, so the compiler's wait-count tracking does not order
+// later LDS reads behind it; the kernel waits on vmcnt itself before the
+// barrier that publishes a stage.
+__device__ __forceinline__ void g2lds16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_vm_8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// Opaque copy of a value: stops the compiler hoisting per-lane values computed
+// from it out of the persistent tile loop (they would stay live, and spill,
+// across every tile); they are recomputed per tile instead.
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+template <class T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const T*)(((uint64_t)hi << 32) | lo);
 }
 
 __device__ __forceinline__ f32x16_t mfma(bf16x8_t w, bf16x8_t x, f32x16_t c) {
@@ -107,8 +141,17 @@ __device__ __forceinline__ u32x2_t pack4(float a, float b, float c, float d) {
   return v;
 }
 
-// Block-wide inclusive scan of one int per thread (256 threads); s_wsum holds 4 ints.
-__device__ __forceinline__ int block_incl_scan(int v, int* s_wsum) {
+// Column base (within the 256-wide B tile) of N-fragment f (0, 1) of wave column wn (0..3).
+// SwiGLU: fragment 0 holds 32 gate columns and fragment 1 the matching 32 up columns.
+template <int EPI>
+__device__ __forceinline__ int frag_col8(int wn, int f) {
+  if (EPI == EPI_SWIGLU) return f == 0 ? wn * 32 : 128 + wn * 32;
+  return wn * 64 + f * 32;
+}
+
+// Block-wide inclusive scan of one int per thread (NW waves); s_wsum holds NW ints.
+template <int NW>
+__device__ __forceinline__ int block_incl_scan_n(int v, int* s_wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -121,50 +164,76 @@ __device__ __forceinline__ int block_incl_scan(int v, int* s_wsum) {
   return v;
 }
 
-// Column base (within the 256-wide B tile) of N-fragment f of wave column wn.
-template <int EPI>
-__device__ __forceinline__ int frag_col(int wn, int f) {
-  if (EPI == EPI_SWIGLU) return f < 2 ? wn * 64 + f * 32 : 128 + wn * 64 + (f - 2) * 32;
-  return wn * 128 + f * 32;
-}
+constexpr int GTHR = 512;  // 8 waves: 2 along M x 4 along N, each wave 128 x 64
+constexpr int GBK = 32;    // k-slice
+constexpr int NST = 4;     // LDS stages (three k-slices in flight ahead of the one in use)
+constexpr int kOpStage = 256 * GBK * 2;      // one operand, one stage: 16 KB
+constexpr int kGemmLds = 2 * NST * kOpStage;  // 128 KB
 
-template <int OP, int EPI>
-__global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmP p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
-  __shared__ int s_lo[kMaxExperts], s_n[kMaxExperts], s_pref[kMaxExperts + 1], s_wsum[4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+// [row][k] tiles of 64-byte rows (A [BM][32], NT-B [BN][32]): four 16-byte chunks
+// per row; a ds_read_b128 of 16 lanes covers 16 consecutive rows at one chunk,
+// and c ^ ((row >> 2) & 3) spreads the four rows that share a 64-byte bank
+// quarter over the four chunks.
+__device__ __forceinline__ int off_k4(int row, int c) { return row * 64 + ((c ^ ((row >> 2) & 3)) << 4); }
+// MFMA operand from a [row][k] tile: lane l gets row rbase + l%32, k values k0 + 8*(l/32) + 0..7.
+__device__ __forceinline__ bf16x8_t frag_k4(const uint8_t* tile, int lane, int k0, int rbase) {
+  return lds_rd16(tile, off_k4(rbase + (lane & 31), (k0 >> 3) + (lane >> 5)));
+}
+__device__ __forceinline__ void wait_vm_4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
+
+template <int OP, int EPI, bool GATHER>
+__global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kGemmLds];
+  // Output staging: 2 KB per wave, 32 rows x 64 bytes of the wave's output at a time.
+  __shared__ __attribute__((aligned(16))) uint8_t s_stage[GTHR / 64][2048];
+  __shared__ int s_lo[kMaxExperts + 1], s_pref[kMaxExperts + 1], s_wsum[8];
   const int mlp = EPI == EPI_SWIGLU ? p.N / 2 : p.N;
   const int tile_n = EPI == EPI_SWIGLU ? 128 : BN;
   const int ntn = (mlp + tile_n - 1) / tile_n;
 
   {  // ragged tile list: tiles of expert e = ceil(rows_e / BM) * ntn, prefix over experts
+    const int tid = threadIdx.x;
     int tiles = 0;
+    if (tid <= p.E) s_lo[tid] = min(max(p.off[tid], 0), p.M);
     if (tid < p.E) {
       int lo = p.off[tid], hi = p.off[tid + 1];
       lo = min(max(lo, 0), p.M);
       hi = min(max(hi, 0), p.M);
       const int n = hi > lo ? hi - lo : 0;
-      s_lo[tid] = lo;
-      s_n[tid] = n;
       tiles = ((n + BM - 1) / BM) * ntn;
     }
-    const int incl = block_incl_scan(tiles, s_wsum);
+    const int incl = block_incl_scan_n<GTHR / 64>(tiles, s_wsum);
     if (tid < p.E) s_pref[tid + 1] = incl;
     if (tid == 0) s_pref[0] = 0;
     __syncthreads();
   }
   const int total = s_pref[p.E];
   uint8_t* const As0 = smem;
-  uint8_t* const Bs0 = smem + 2 * kStageBytes;
+  uint8_t* const Bs0 = smem + NST * kOpStage;
 
-  // loader lanes
-  const int ca = tid & 7, ra = tid >> 3;   // [row][k] tiles: chunk, first row (+32 per step)
-  const int cb = tid & 31, kb = tid >> 5;  // [k][n] tiles: chunk, first k-row (+8 per step)
-
-  for (int64_t it = 0;; ++it) {
+  // Loader: direct global->LDS copies, 1 KB per instruction (64 lanes x 16 B,
+  // lane L at LDS base + 16 L); the swizzle is applied to the global address
+  // each lane reads. Per wave 2 instructions per operand per k-slice; block
+  // b = 2*wave + j of 1 KB:
+  //  [row][k] tiles: rows 16b .. 16b+15; lane L -> row 16b + L/4, physical chunk
+  //    L%4, logical chunk (L%4) ^ ((row >> 2) & 3).
+  //  [k][n] tiles: k-rows 2b, 2b+1; lane L -> k-row 2b + L/32, physical chunk
+  //    L%32, logical chunk (L%32) ^ ((k-row & 3) << 2).
+  // Rows past the group end are clamped to its last row and columns past N to a
+  // valid column: both only feed outputs that are never stored. With a row
+  // gather, A rows are read in place through the slot index.
+  const int tid = opaque((int)threadIdx.x), lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t lds_a = lds_addr(As0) + wave_u * 2 * 1024, lds_b = lds_addr(Bs0) + wave_u * 2 * 1024;
+  const int nk = p.K / GBK;
+  int m0, m_end, n0;
+  const uint16_t *Ab, *Bexp;
+  uint32_t a_off[2], b_off[2];
+  // Tile `it` of this workgroup -> m0, m_end, n0, operand bases and per-lane offsets.
+  auto decode = [&](int64_t it) -> bool {
     const int64_t tl = xcd_tile(it, blockIdx.x, gridDim.x);
-    if (tl >= total) break;
+    if (tl >= total) return false;
     const int tile = (int)tl;
     int lo = 0, hi = p.E;
     while (hi - lo > 1) {
@@ -175,167 +244,233 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmP p) {
     const int e = lo;
     const int local = tile - s_pref[e];
     const int mt = local / ntn, nt = local % ntn;
-    const int m0 = s_lo[e] + mt * BM;
-    const int m_end = s_lo[e] + s_n[e];
-    const int n0 = nt * tile_n;
-    const uint16_t* Bexp = p.B + (int64_t)e * p.K * p.N;
-
-    // Per-tile operand bases with 32-bit offsets. Rows past the group end are
-    // clamped to its last row and columns past N to a valid column: both only
-    // feed outputs that are never stored. With a row gather, A rows are read in
-    // place through the slot index (no permuted copy of A).
-    const uint16_t* Ab;
-    int a_off[8];
-    if (p.row_slot) {
-      Ab = p.A;
+    m0 = __builtin_amdgcn_readfirstlane(s_lo[e] + mt * BM);
+    m_end = __builtin_amdgcn_readfirstlane(max(s_lo[e + 1], s_lo[e]));
+    n0 = __builtin_amdgcn_readfirstlane(nt * tile_n);
+    Bexp = uniform_ptr(p.B + (int64_t)__builtin_amdgcn_readfirstlane(e) * p.K * p.N);
+    Ab = GATHER ? p.A : uniform_ptr(p.A + (int64_t)m0 * p.K);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int s = min(max(p.row_slot[min(m0 + ra + 32 * i, m_end - 1)], 0), p.n_slots - 1);
-        a_off[i] = (s / p.slot_div) * p.K + ca * 8;
-      }
-    } else {
-      Ab = p.A + (int64_t)m0 * p.K;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) a_off[i] = (min(m0 + ra + 32 * i, m_end - 1) - m0) * p.K + ca * 8;
-    }
-    int b_off[8];
-    if (OP == OP_NT) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) b_off[i] = min(n0 + ra + 32 * i, p.N - 1) * p.K + ca * 8;
-    } else {
-      int col;
-      if (EPI == EPI_SWIGLU) {
-        const int c = cb < 16 ? n0 + cb * 8 : n0 + (cb - 16) * 8;
-        col = c < mlp ? (cb < 16 ? c : mlp + c) : 0;
+    for (int j = 0; j < 2; ++j) {
+      const int row = (wave_u * 2 + j) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      const int r = min(m0 + row, m_end - 1);
+      if (GATHER) {
+        const int s = min(max(p.row_slot[r], 0), p.n_slots - 1);
+        a_off[j] = (uint32_t)((s / p.slot_div) * p.K + c * 8) * 2u;
       } else {
-        col = n0 + cb * 8;
-        col = col < p.N ? col : 0;
+        a_off[j] = (uint32_t)((r - m0) * p.K + c * 8) * 2u;
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) b_off[i] = (kb + 8 * i) * p.N + col;
     }
-
-    u32x4_t ar[8], br[8];
-    auto load = [&](int k0) {
-      const uint16_t* Ak = Ab + k0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ar[i] = ld16(Ak + a_off[i]);
-      const uint16_t* Bk = OP == OP_NT ? Bexp + k0 : Bexp + (int64_t)k0 * p.N;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) br[i] = ld16(Bk + b_off[i]);
-    };
-    auto store = [&](int stage) {
-      uint8_t* As = As0 + stage * kStageBytes;
-      uint8_t* Bs = Bs0 + stage * kStageBytes;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4_t*>(As + off_k8(ra + 32 * i, ca)) = ar[i];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (OP == OP_NT) *reinterpret_cast<u32x4_t*>(Bs + off_k8(ra + 32 * i, ca)) = br[i];
-        else *reinterpret_cast<u32x4_t*>(Bs + off_n32(kb + 8 * i, cb)) = br[i];
+    for (int j = 0; j < 2; ++j) {
+      if (OP == OP_NT) {
+        const int row = (wave_u * 2 + j) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ ((row >> 2) & 3);
+        b_off[j] = (uint32_t)(min(n0 + row, p.N - 1) * p.K + c * 8) * 2u;
+      } else {
+        const int krow = (wave_u * 2 + j) * 2 + (lane >> 5);
+        const int c = (lane & 31) ^ ((krow & 3) << 2);
+        int col;
+        if (EPI == EPI_SWIGLU) {
+          const int cc = c < 16 ? n0 + c * 8 : n0 + (c - 16) * 8;
+          col = cc < mlp ? (c < 16 ? cc : mlp + cc) : 0;
+        } else {
+          col = n0 + c * 8;
+          col = col < p.N ? col : 0;
+        }
+        b_off[j] = (uint32_t)(krow * p.N + col) * 2u;
       }
-    };
+    }
+    return true;
+  };
+  auto issue_loads = [&](int kt) {
+    const int k0 = kt * GBK;
+    const uint16_t* Ak = Ab + k0;
+    const uint16_t* Bk = OP == OP_NT ? Bexp + k0 : Bexp + (int64_t)k0 * p.N;
+    const uint32_t st = (uint32_t)(kt & (NST - 1)) * kOpStage;
+    g2lds16(Ak, a_off[0], lds_a + st);
+    g2lds16(Ak, a_off[1], lds_a + st + 1024);
+    g2lds16(Bk, b_off[0], lds_b + st);
+    g2lds16(Bk, b_off[1], lds_b + st + 1024);
+  };
 
-    f32x16_t acc[4][4];
+  // The first NST k-slices of a tile are issued before the previous tile's
+  // epilogue (every stage is free once its last barrier has passed), so their
+  // latency overlaps the epilogue's math and stores.
+  if (!decode(0)) return;
+  for (int s = 0; s < NST; ++s)
+    if (s < nk) issue_loads(s);
+  for (int64_t it = 0;; ++it) {
+    f32x16_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int f = 0; f < 4; ++f)
+      for (int f = 0; f < 2; ++f)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
 
-    const int nk = p.K / BK;
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) load((kt + 1) * BK);
-      const uint8_t* As = As0 + cur * kStageBytes;
-      const uint8_t* Bs = Bs0 + cur * kStageBytes;
+    bf16x8_t af[2][4], bf[2][2];
+    auto read_frags = [&](int stage, int ks, int set) {
+      const uint8_t* As = As0 + stage * kOpStage;
+      const uint8_t* Bs = Bs0 + stage * kOpStage;
 #pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        bf16x8_t af[4], bf[4];
+      for (int i = 0; i < 4; ++i) af[set][i] = frag_k4(As, lane, ks * 16, wm * 128 + i * 32);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = frag_k(As, lane, ks * 16, wm * 128 + i * 32);
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          if (OP == OP_NT) bf[f] = frag_k(Bs, lane, ks * 16, frag_col<EPI>(wn, f));
-          else bf[f] = frag_tr(Bs, lane, ks * 16, frag_col<EPI>(wn, f));
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int f = 0; f < 4; ++f) acc[i][f] = mfma(bf[f], af[i], acc[i][f]);
+      for (int f = 0; f < 2; ++f) {
+        if (OP == OP_NT) bf[set][f] = frag_k4(Bs, lane, ks * 16, frag_col8<EPI>(wn, f));
+        else bf[set][f] = frag_tr(Bs, lane, ks * 16, frag_col8<EPI>(wn, f));
       }
-      if (kt + 1 < nk) store(cur ^ 1);
+    };
+    auto mfmas = [&](int set) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int f = 0; f < 2; ++f) acc[i][f] = mfma(bf[set][f], af[set][i], acc[i][f]);
+    };
+    // Issue order inside a 16-wide sub-slice: one MFMA, then one LDS read of the
+    // next sub-slice's fragments.
+    auto interleave = [&]() {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    };
+
+    wait_vm_all();    // this wave's loads of the first k-slices (and the last tile's stores) are done
+    __syncthreads();
+    read_frags(0, 0, 0);
+    // k-slice kt on stage kt % NST. On entry its first 16-wide sub-slice is in
+    // fragment set 0. The barrier sits before the second sub-slice: every wave
+    // then holds all of stage kt % NST in registers, so the loads of k-slice
+    // kt + NST go into it at once, and k-slice kt+1 (issued NST-1 k-slices
+    // ago) must have landed. The next stage's first fragments are read under
+    // the second sub-slice's MFMAs (also on the last k-slice, where they go
+    // unused: it keeps the body one basic block).
+    for (int kt = 0; kt < nk; ++kt) {
+      const int st = kt & (NST - 1);
+      read_frags(st, 1, 1);
+      mfmas(0);
+      interleave();
+      // loads issued after those of k-slice kt+1: k-slices kt+2 and kt+3, where they exist
+      if (kt + 3 < nk) wait_vm_8();
+      else if (kt + 2 < nk) wait_vm_4();
+      else wait_vm_all();
       __syncthreads();
+      if (kt + NST < nk) issue_loads(kt + NST);
+      read_frags((kt + 1) & (NST - 1), 0, 0);
+      mfmas(1);
+      interleave();
     }
 
+    // Next tile's first loads go out now; this tile's rows and columns are kept for the epilogue.
+    const int cm0 = m0, cm_end = m_end, cn0 = n0;
+    // optional per-row fp32 scale (the top-k weight of the row's slot), applied as values are read;
+    // fetched before the prefetch so that its wait does not cover the next tile's loads
+    float sc4[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    if (GATHER && p.slot_scale) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = min(cm0 + wm * 128 + i * 32 + (lane & 31), cm_end - 1);
+        sc4[i] = p.slot_scale[p.row_slot ? min(max(p.row_slot[m], 0), p.n_slots - 1) : m];
+      }
+    }
+    const bool more = decode(it + 1);
+    if (more)
+      for (int s = 0; s < NST; ++s)
+        if (s < nk) issue_loads(s);
     // Epilogue. Lane holds rows m = tile row + lane%32 and, per register group q,
     // four consecutive columns 8q + 4*(lane/32) + 0..3 of each 32-wide fragment.
+    // NONE and SWIGLU pass their output through this wave's LDS staging area,
+    // 32 rows x 64 bytes at a time, and store whole 64-byte row segments:
+    // stores straight from the MFMA layout would write 8 bytes into each of 32
+    // rows per instruction.
     const int hh = lane >> 5;
+    uint8_t* const stg = s_stage[wave];
+    // [32 rows][64 B] block, 16-byte chunk c of row r at r*64 + ((c ^ ((r >> 2) & 3)) << 4)
+    auto stg64 = [&](int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); };
+    const int r = lane & 31;
+    // Read the staged block back, four lanes per row, and store rows m0r + 0..31,
+    // 16 bytes at column byte offset 16 * (lane % 4) from row_ptr(m).
+    auto drain = [&](int m0r, auto row_ptr, int valid_chunks) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int rr = 16 * k + (lane >> 2), c = lane & 3;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + stg64(rr, c));
+        const int m = m0r + rr;
+        if (m < cm_end && c < valid_chunks) st16(reinterpret_cast<uint16_t*>(row_ptr(m)) + c * 8, v);
+      }
+    };
+    if (EPI == EPI_NONE) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sc = sc4[i];
+        const int m0r = cm0 + wm * 128 + i * 32;
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<u32x2_t*>(stg + stg64(r, q) + hh * 8) =
+                pack4(sc * acc[i][f][4 * q], sc * acc[i][f][4 * q + 1], sc * acc[i][f][4 * q + 2],
+                      sc * acc[i][f][4 * q + 3]);
+          const int n0f = cn0 + wn * 64 + f * 32;
+          drain(m0r, [&](int m) { return (void*)(p.C + (int64_t)m * p.N + n0f); }, min(4, (p.N - n0f) >> 3));
+        }
+      }
+    } else if (EPI == EPI_SWIGLU) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sc = sc4[i];
+        const int m0r = cm0 + wm * 128 + i * 32;
+        const int c0 = cn0 + wn * 32;
+        f32x4_t gv[4], uv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float a[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            gv[q][u] = sc * acc[i][0][4 * q + u];
+            uv[q][u] = sc * acc[i][1][4 * q + u];
+            a[u] = silu_f(gv[q][u]) * uv[q][u];
+          }
+          *reinterpret_cast<u32x2_t*>(stg + stg64(r, q) + hh * 8) = pack4(a[0], a[1], a[2], a[3]);
+        }
+        drain(m0r, [&](int m) { return (void*)(p.C + (int64_t)m * mlp + c0); }, min(4, (mlp - c0) >> 3));
+        if (p.aux_out) {  // h kept in fp32 for the backward: the gate/up values the SwiGLU used, unrounded
+#pragma unroll
+          for (int part = 0; part < 4; ++part) {  // gate cols 0-15, 16-31, then up cols 0-15, 16-31
+            const int half = part >> 1, qq = part & 1;
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2)
+              *reinterpret_cast<f32x4_t*>(stg + stg64(r, 2 * q2 + hh)) = half == 0 ? gv[2 * qq + q2] : uv[2 * qq + q2];
+            const int cb = c0 + 16 * qq;
+            // 16 fp32 columns = 64 bytes per row; valid 16-byte chunks of 4 columns
+            drain(m0r, [&](int m) { return (void*)(p.aux_out + (int64_t)m * 2 * mlp + half * mlp + cb); },
+                  min(4, (mlp - cb) >> 2));
+          }
+        }
+      }
+    } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = m0 + wm * 128 + i * 32 + (lane & 31);
-      if (m >= m_end) continue;
-      if (p.slot_scale) {  // per-row scale in fp32 (e.g. the top-k weight of the row's slot)
-        const int s = p.row_slot ? min(max(p.row_slot[m], 0), p.n_slots - 1) : m;
-        const float sc = p.slot_scale[s];
-#pragma unroll
-        for (int f = 0; f < 4; ++f)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][f][r] *= sc;
-      }
-      if (EPI == EPI_NONE) {
-        uint16_t* crow = p.C + (int64_t)m * p.N;
-#pragma unroll
-        for (int f = 0; f < 4; ++f)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int n = n0 + wn * 128 + f * 32 + 8 * q + 4 * hh;
-            if (n < p.N)
-              st8(crow + n, pack4(acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]));
-          }
-      } else if (EPI == EPI_SWIGLU) {
-        uint16_t* arow = p.C + (int64_t)m * mlp;
-        float* hrow = p.aux_out ? p.aux_out + (int64_t)m * 2 * mlp : nullptr;
+      const int m = cm0 + wm * 128 + i * 32 + (lane & 31);
+      if (m >= cm_end) continue;
+      const float sc = sc4[i];
+      {  // EPI_SWIGLU_BWD: N = mlp, aux = saved h [M, 2N] fp32, C = dh [M, 2N]
+        const float* hrow = p.aux_in + (int64_t)m * 2 * p.N;
+        uint16_t* drow = p.C + (int64_t)m * 2 * p.N;
 #pragma unroll
         for (int f = 0; f < 2; ++f)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int col = n0 + wn * 64 + f * 32 + 8 * q + 4 * hh;
-            if (col >= mlp) continue;
-            float a[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) a[u] = silu_f(acc[i][f][4 * q + u]) * acc[i][f + 2][4 * q + u];
-            st8(arow + col, pack4(a[0], a[1], a[2], a[3]));
-            if (hrow) {  // h kept in fp32 for the backward: the gate/up values the SwiGLU used, unrounded
-              f32x4_t gv, uv;
-#pragma unroll
-              for (int u = 0; u < 4; ++u) {
-                gv[u] = acc[i][f][4 * q + u];
-                uv[u] = acc[i][f + 2][4 * q + u];
-              }
-              *reinterpret_cast<f32x4_t*>(hrow + col) = gv;
-              *reinterpret_cast<f32x4_t*>(hrow + mlp + col) = uv;
-            }
-          }
-      } else {  // EPI_SWIGLU_BWD: N = mlp, aux = saved h [M, 2N], C = dh [M, 2N]
-        const float* hrow = p.aux_in + (int64_t)m * 2 * p.N;
-        uint16_t* drow = p.C + (int64_t)m * 2 * p.N;
-#pragma unroll
-        for (int f = 0; f < 4; ++f)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int n = n0 + wn * 128 + f * 32 + 8 * q + 4 * hh;
+            const int n = cn0 + wn * 64 + f * 32 + 8 * q + 4 * hh;
             if (n >= p.N) continue;
             const f32x4_t g = *reinterpret_cast<const f32x4_t*>(hrow + n);
             const f32x4_t u = *reinterpret_cast<const f32x4_t*>(hrow + p.N + n);
             float dg[4], du[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float da = acc[i][f][4 * q + r];
+              const float da = sc * acc[i][f][4 * q + r];
               const float s = sigmoid_f(g[r]);
               dg[r] = da * u[r] * s * (1.0f + g[r] * (1.0f - s));
               du[r] = da * g[r] * s;
@@ -345,6 +480,8 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmP p) {
           }
       }
     }
+    }
+    if (!more) break;
   }
 }
 
@@ -464,12 +601,17 @@ hipError_t launch_grouped_gemm(int op, int epi, const uint16_t* A, const uint16_
   if (M == 0) return hipSuccess;
   GemmP p{A, B, aux_in, aux_out, C, group_offsets, row_slot, slot_scale, E, (int)M, K, N,
           row_slot ? n_slots : (int)M, slot_div > 0 ? slot_div : 1};
-  const dim3 grid(persistent_grid()), block(NTHR);
-  if (op == OP_NN && epi == EPI_NONE) gemm_kernel<OP_NN, EPI_NONE><<<grid, block, 0, stream>>>(p);
-  else if (op == OP_NN && epi == EPI_SWIGLU) gemm_kernel<OP_NN, EPI_SWIGLU><<<grid, block, 0, stream>>>(p);
-  else if (op == OP_NT && epi == EPI_NONE) gemm_kernel<OP_NT, EPI_NONE><<<grid, block, 0, stream>>>(p);
-  else if (op == OP_NT && epi == EPI_SWIGLU_BWD) gemm_kernel<OP_NT, EPI_SWIGLU_BWD><<<grid, block, 0, stream>>>(p);
+  const dim3 grid(persistent_grid()), block(GTHR);
+  const bool g = row_slot != nullptr || slot_scale != nullptr;
+#define MOE_GEMM_LAUNCH(O, P)                                                           \
+  if (g) gemm_kernel<O, P, true><<<grid, block, 0, stream>>>(p);                        \
+  else gemm_kernel<O, P, false><<<grid, block, 0, stream>>>(p);
+  if (op == OP_NN && epi == EPI_NONE) { MOE_GEMM_LAUNCH(OP_NN, EPI_NONE) }
+  else if (op == OP_NN && epi == EPI_SWIGLU) { MOE_GEMM_LAUNCH(OP_NN, EPI_SWIGLU) }
+  else if (op == OP_NT && epi == EPI_NONE) { MOE_GEMM_LAUNCH(OP_NT, EPI_NONE) }
+  else if (op == OP_NT && epi == EPI_SWIGLU_BWD) { MOE_GEMM_LAUNCH(OP_NT, EPI_SWIGLU_BWD) }
   else return hipErrorInvalidValue;
+#undef MOE_GEMM_LAUNCH
   return hipGetLastError();
 }
 
