@@ -21,6 +21,7 @@ constexpr int kTPW = 16;            // tokens per wave
 constexpr int kWaves = 4;
 constexpr int kTB = kTPW * kWaves;  // tokens per workgroup
 constexpr int kBK = 32;             // emb slice staged in LDS per step
+static_assert(2 * kBK == kTB, "the two w buffers must hold the logits of a workgroup's tokens");
 
 // Order-preserving key of a logit: larger logit -> larger key. -0 maps like +0;
 // NaN maps to 0, below every number.
@@ -57,8 +58,8 @@ __global__ __launch_bounds__(256) void route_kernel(int64_t T, int emb, int E, i
                                                     const float* __restrict__ wr, const float* __restrict__ bias,
                                                     const float* __restrict__ logits_in, int32_t* __restrict__ topk_idx,
                                                     float* __restrict__ topk_w) {
-  __shared__ __attribute__((aligned(16))) float s_x[kBK][kTB];
-  __shared__ float s_w[kBK][64 * EQ];
+  __shared__ __attribute__((aligned(16))) float s_x[2][kBK][kTB];
+  __shared__ __attribute__((aligned(16))) float s_w[2][kBK][64 * EQ];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t t0 = (int64_t)blockIdx.x * kTB;
   const int64_t tw = t0 + wave * kTPW;
@@ -78,27 +79,52 @@ __global__ __launch_bounds__(256) void route_kernel(int64_t T, int emb, int E, i
     for (int tt = 0; tt < kTPW; ++tt)
 #pragma unroll
       for (int q = 0; q < EQ; ++q) acc[tt][q] = 0.0f;
-    for (int i0 = 0; i0 < emb; i0 += kBK) {
-      {  // x slice: 64 tokens x 32 values, 16 bytes per thread, widened to fp32 [i][token]
-        const int tk = tid >> 2, seg = tid & 3;
-        const int64_t t = t0 + tk;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (t < T) v = ld16(x + t * emb + i0 + seg * 8);
+    // Slices of kBK emb values are double-buffered: the next slice is loaded
+    // into registers while the current one feeds the FMA chains, then written
+    // to the other LDS buffer; one barrier per slice.
+    const int tk = tid >> 2, seg = tid & 3;  // x: token tk of the block, 8 values at seg*8
+    const int64_t tx = t0 + tk;
+    const bool vec_w = (E & 3) == 0;
+    constexpr int kW4 = kBK * 64 * EQ / 4 / 256;  // float4 of the w slice per thread
+    u32x4_t xr;
+    f32x4_t wr4[kW4];
+    auto load = [&](int i0) {
+      xr = tx < T ? ld16(x + tx * emb + i0 + seg * 8) : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          s_x[seg * 8 + 2 * u][tk] = bf16_lo(v[u]);
-          s_x[seg * 8 + 2 * u + 1][tk] = bf16_hi(v[u]);
+      for (int j = 0; j < kW4; ++j) {
+        const int idx = (tid + 256 * j) * 4, ii = idx / (64 * EQ), e = idx % (64 * EQ);
+        const float* src = wr + (int64_t)(i0 + ii) * E + e;
+        if (vec_w && e + 3 < E) {
+          wr4[j] = *reinterpret_cast<const f32x4_t*>(src);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) wr4[j][u] = e + u < E ? src[u] : 0.0f;
         }
       }
-      for (int idx = tid; idx < kBK * 64 * EQ; idx += 256) {  // wr slice [32][64*EQ], zero past E
-        const int ii = idx / (64 * EQ), e = idx % (64 * EQ);
-        s_w[ii][e] = e < E ? wr[(int64_t)(i0 + ii) * E + e] : 0.0f;
+    };
+    auto store = [&](int b) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        s_x[b][seg * 8 + 2 * u][tk] = bf16_lo(xr[u]);
+        s_x[b][seg * 8 + 2 * u + 1][tk] = bf16_hi(xr[u]);
       }
-      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kW4; ++j) {
+        const int idx = (tid + 256 * j) * 4, ii = idx / (64 * EQ), e = idx % (64 * EQ);
+        *reinterpret_cast<f32x4_t*>(&s_w[b][ii][e]) = wr4[j];
+      }
+    };
+    load(0);
+    store(0);
+    __syncthreads();
+    int b = 0;
+    for (int i0 = 0; i0 < emb; i0 += kBK) {
+      const bool more = i0 + kBK < emb;
+      if (more) load(i0 + kBK);
 #pragma unroll 2
       for (int ii = 0; ii < kBK; ++ii) {
         float xv[kTPW];
-        const f32x4_t* px = reinterpret_cast<const f32x4_t*>(&s_x[ii][wave * kTPW]);
+        const f32x4_t* px = reinterpret_cast<const f32x4_t*>(&s_x[b][ii][wave * kTPW]);
 #pragma unroll
         for (int c = 0; c < kTPW / 4; ++c) {
           const f32x4_t v = px[c];
@@ -109,13 +135,15 @@ __global__ __launch_bounds__(256) void route_kernel(int64_t T, int emb, int E, i
         }
         float wv[EQ];
 #pragma unroll
-        for (int q = 0; q < EQ; ++q) wv[q] = s_w[ii][lane + 64 * q];
+        for (int q = 0; q < EQ; ++q) wv[q] = s_w[b][ii][lane + 64 * q];
 #pragma unroll
         for (int tt = 0; tt < kTPW; ++tt)
 #pragma unroll
           for (int q = 0; q < EQ; ++q) acc[tt][q] = __builtin_fmaf(xv[tt], wv[q], acc[tt][q]);
       }
+      if (more) store(b ^ 1);  // the other buffer was last read before the previous barrier
       __syncthreads();
+      b ^= 1;
     }
     if (bias) {
 #pragma unroll
@@ -128,6 +156,15 @@ __global__ __launch_bounds__(256) void route_kernel(int64_t T, int emb, int E, i
     }
   }
 
+  // The logits go to LDS (into the w buffers: kTB x 64*EQ floats, free after
+  // the last barrier), so the per-token loop below reads them by a runtime
+  // token index. Each wave reads back only its own tokens.
+  float* const s_l = &s_w[0][0][0];
+#pragma unroll
+  for (int tt = 0; tt < kTPW; ++tt)
+#pragma unroll
+    for (int q = 0; q < EQ; ++q) s_l[(wave * kTPW + tt) * 64 * EQ + lane + 64 * q] = acc[tt][q];
+
   // Top-k per token: k rounds of a wave-wide max over (key(logit), -expert).
   // Picked and padding experts hold candidate 0, which no real expert reaches.
 #pragma unroll 1
@@ -138,7 +175,8 @@ __global__ __launch_bounds__(256) void route_kernel(int64_t T, int emb, int E, i
 #pragma unroll
     for (int q = 0; q < EQ; ++q) {
       const int e = lane + 64 * q;
-      cand[q] = e < E ? (((uint64_t)order_key(acc[tt][q]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e)) : 0ull;
+      const float l = s_l[(wave * kTPW + tt) * 64 * EQ + e];
+      cand[q] = e < E ? (((uint64_t)order_key(l) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e)) : 0ull;
     }
     int my_e = 0;
     float my_l = 0.0f;
