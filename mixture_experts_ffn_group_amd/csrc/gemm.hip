@@ -47,10 +47,6 @@ namespace moe {
 namespace {
 
 constexpr int BM = 256, BN = 256;
-// weight-gradient kernel: k-slice of 64 rows, 4 waves, two register-staged LDS stages
-constexpr int BK = 64, NTHR = 256;
-constexpr int kStageBytes = BM * BK * 2;  // one operand, one stage: 32 KB
-constexpr int kLdsBytes = 4 * kStageBytes;
 
 enum { OP_NN = 0, OP_NT = 1 };
 enum { EPI_NONE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_BWD = 2 };
@@ -485,104 +481,174 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
   }
 }
 
-// dW[e] [P, Q] = sum over rows r of group e of A[r]^T D[r]. The contraction runs
-// over the group's rows, so both operands are [row][col] tiles read transposed.
-// Rows past the group end load as zeros; an empty group writes exact zeros.
-__global__ __launch_bounds__(NTHR, 1) void wgrad_kernel(WgradP p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+// dW[e] [P, Q] = sum over the rows r of group e of A[r]^T D[r]. The contraction
+// runs over the group's rows, so both operands are [row][col] tiles that the
+// MFMA reads transposed (ds_read_b64_tr_b16), like the NN weight of the
+// forward GEMM. Same workgroup shape, LDS ring and staged epilogue as
+// gemm_kernel; tiles are (expert, 256-row block of P, 256-column block of Q),
+// numbered expert-major, and the k-loop runs over the expert's own rows.
+// Rows past the group end must add nothing: each k-slice is copied with
+// buffer loads whose range is exactly the slice's valid rows, and the
+// hardware writes zeros for out-of-range lanes. An empty group writes exact
+// zeros.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);                           // range in bytes
+  r[3] = 0x00020000;                                                            // 32-bit data format
+  return r;
+}
+// Buffer -> LDS copy, 16 bytes per lane (lane L at lds + 16 L): lanes whose
+// offset is at or past the resource's range read zeros.
+__device__ __forceinline__ void b2lds16(i32x4_t rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "s"(lds) : "memory");
+}
+
+__global__ __launch_bounds__(GTHR, 1) void wgrad_kernel(WgradP p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kGemmLds];
+  __shared__ __attribute__((aligned(16))) uint8_t s_stage[GTHR / 64][2048];
   const int tp = (p.P + 255) / 256, tq = (p.Q + 255) / 256;
   const int64_t total = (int64_t)p.E * tp * tq;
   uint8_t* const As0 = smem;
-  uint8_t* const Ds0 = smem + 2 * kStageBytes;
-  const int cb = tid & 31, kb = tid >> 5;
+  uint8_t* const Ds0 = smem + NST * kOpStage;
+  const int tid = opaque((int)threadIdx.x), lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t lds_a = lds_addr(As0) + wave_u * 2 * 1024, lds_d = lds_addr(Ds0) + wave_u * 2 * 1024;
 
-  for (int64_t it = 0;; ++it) {
+  // Per tile: expert e, output block (p0, q0), the group's rows [lo, lo + n), nk k-slices.
+  // Loader (both operands [k][n] tiles of 32 rows x 512 bytes): block b = 2*wave + j
+  // holds k-rows 2b, 2b+1; lane L -> k-row 2b + L/32, physical chunk L%32,
+  // logical chunk (L%32) ^ ((k-row & 3) << 2). Columns past P or Q read other
+  // bytes of the slice (or zeros) and only feed outputs that are never stored.
+  int e = 0, p0 = 0, q0 = 0, lo = 0, n = 0, nk = 0;
+  uint32_t a_off[2], d_off[2];
+  auto decode = [&](int64_t it) -> bool {
     const int64_t tl = xcd_tile(it, blockIdx.x, gridDim.x);
-    if (tl >= total) break;
-    const int e = (int)(tl / (tp * tq));
+    if (tl >= total) return false;
+    e = (int)__builtin_amdgcn_readfirstlane((int)(tl / (tp * tq)));
     const int loc = (int)(tl % (tp * tq));
-    const int p0 = (loc / tq) * 256, q0 = (loc % tq) * 256;
-    int lo = p.off[e], hi = p.off[e + 1];
-    lo = min(max(lo, 0), p.M);
-    hi = min(max(hi, 0), p.M);
-    const int n = hi > lo ? hi - lo : 0;
-    const int pc = p0 + cb * 8, qc = q0 + cb * 8;
-
-    u32x4_t ar[8], dr[8];
-    auto load = [&](int k0) {
+    p0 = __builtin_amdgcn_readfirstlane((loc / tq) * 256);
+    q0 = __builtin_amdgcn_readfirstlane((loc % tq) * 256);
+    const int l0 = min(max(p.off[e], 0), p.M), h0 = min(max(p.off[e + 1], 0), p.M);
+    lo = __builtin_amdgcn_readfirstlane(l0);
+    n = __builtin_amdgcn_readfirstlane(h0 > l0 ? h0 - l0 : 0);
+    nk = (n + GBK - 1) / GBK;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = k0 + kb + 8 * i;
-        ar[i] = u32x4_t{0u, 0u, 0u, 0u};
-        dr[i] = u32x4_t{0u, 0u, 0u, 0u};
-        if (row < n) {
-          if (pc < p.P) ar[i] = ld16(p.A + (int64_t)(lo + row) * p.P + pc);
-          if (qc < p.Q) dr[i] = ld16(p.D + (int64_t)(lo + row) * p.Q + qc);
-        }
-      }
-    };
-    auto store = [&](int stage) {
-      uint8_t* As = As0 + stage * kStageBytes;
-      uint8_t* Ds = Ds0 + stage * kStageBytes;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        *reinterpret_cast<u32x4_t*>(As + off_n32(kb + 8 * i, cb)) = ar[i];
-        *reinterpret_cast<u32x4_t*>(Ds + off_n32(kb + 8 * i, cb)) = dr[i];
-      }
-    };
+    for (int j = 0; j < 2; ++j) {
+      const int krow = (wave_u * 2 + j) * 2 + (lane >> 5);
+      const int c = (lane & 31) ^ ((krow & 3) << 2);
+      a_off[j] = (uint32_t)(krow * p.P + p0 + c * 8) * 2u;
+      d_off[j] = (uint32_t)(krow * p.Q + q0 + c * 8) * 2u;
+    }
+    return true;
+  };
+  auto issue_loads = [&](int kt) {
+    const int r0 = lo + kt * GBK, rows = min(GBK, n - kt * GBK);
+    const i32x4_t ra = buffer_rsrc(p.A + (int64_t)r0 * p.P, (uint32_t)(rows * p.P * 2));
+    const i32x4_t rd = buffer_rsrc(p.D + (int64_t)r0 * p.Q, (uint32_t)(rows * p.Q * 2));
+    const uint32_t st = (uint32_t)(kt & (NST - 1)) * kOpStage;
+    b2lds16(ra, a_off[0], lds_a + st);
+    b2lds16(ra, a_off[1], lds_a + st + 1024);
+    b2lds16(rd, d_off[0], lds_d + st);
+    b2lds16(rd, d_off[1], lds_d + st + 1024);
+  };
 
-    f32x16_t acc[4][4];
+  if (!decode(0)) return;
+  for (int s = 0; s < NST; ++s)
+    if (s < nk) issue_loads(s);
+  for (int64_t it = 0;; ++it) {
+    f32x16_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int f = 0; f < 4; ++f)
+      for (int f = 0; f < 2; ++f)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
 
-    const int nk = (n + BK - 1) / BK;
-    if (nk > 0) {
-      load(0);
-      store(0);
-    }
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) load((kt + 1) * BK);
-      const uint8_t* As = As0 + cur * kStageBytes;
-      const uint8_t* Ds = Ds0 + cur * kStageBytes;
+    bf16x8_t af[2][4], df[2][2];
+    auto read_frags = [&](int stage, int ks, int set) {
+      const uint8_t* As = As0 + stage * kOpStage;
+      const uint8_t* Ds = Ds0 + stage * kOpStage;
 #pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        bf16x8_t af[4], df[4];
+      for (int i = 0; i < 4; ++i) af[set][i] = frag_tr(As, lane, ks * 16, wm * 128 + i * 32);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = frag_tr(As, lane, ks * 16, wm * 128 + i * 32);
+      for (int f = 0; f < 2; ++f) df[set][f] = frag_tr(Ds, lane, ks * 16, wn * 64 + f * 32);
+    };
+    auto mfmas = [&](int set) {
 #pragma unroll
-        for (int f = 0; f < 4; ++f) df[f] = frag_tr(Ds, lane, ks * 16, wn * 128 + f * 32);
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int f = 0; f < 2; ++f) acc[i][f] = mfma(df[set][f], af[set][i], acc[i][f]);
+    };
+    // 12 transposed reads per 8 MFMAs: two reads after each of the first four MFMAs, one after the rest
+    auto interleave = [&]() {
 #pragma unroll
-          for (int f = 0; f < 4; ++f) acc[i][f] = mfma(df[f], af[i], acc[i][f]);
+      for (int j = 0; j < 4; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
-      if (kt + 1 < nk) store(cur ^ 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    };
+
+    wait_vm_all();    // this wave's loads of the first k-slices (and the last tile's stores) are done
+    __syncthreads();
+    read_frags(0, 0, 0);
+    // same k-slice schedule as gemm_kernel
+    for (int kt = 0; kt < nk; ++kt) {
+      const int st = kt & (NST - 1);
+      read_frags(st, 1, 1);
+      mfmas(0);
+      interleave();
+      if (kt + 3 < nk) wait_vm_8();
+      else if (kt + 2 < nk) wait_vm_4();
+      else wait_vm_all();
       __syncthreads();
+      if (kt + NST < nk) issue_loads(kt + NST);
+      read_frags((kt + 1) & (NST - 1), 0, 0);
+      mfmas(1);
+      interleave();
     }
 
-    const int hh = lane >> 5;
+    const int ce = e, cp0 = p0, cq0 = q0;
+    const bool more = decode(it + 1);
+    if (more)
+      for (int s = 0; s < NST; ++s)
+        if (s < nk) issue_loads(s);
+    // Epilogue through this wave's staging area, 32 rows x 64 bytes at a time (as in gemm_kernel).
+    const int hh = lane >> 5, r = lane & 31;
+    uint8_t* const stg = s_stage[wave];
+    auto stg64 = [&](int rr, int c) { return rr * 64 + ((c ^ ((rr >> 2) & 3)) << 4); };
+    uint16_t* const Ce = p.C + (int64_t)ce * p.P * p.Q;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int pr = p0 + wm * 128 + i * 32 + (lane & 31);
-      if (pr >= p.P) continue;
-      uint16_t* crow = p.C + ((int64_t)e * p.P + pr) * p.Q;
+      const int pr0 = cp0 + wm * 128 + i * 32;
 #pragma unroll
-      for (int f = 0; f < 4; ++f)
+      for (int f = 0; f < 2; ++f) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int qq = q0 + wn * 128 + f * 32 + 8 * q + 4 * hh;
-          if (qq < p.Q)
-            st8(crow + qq, pack4(acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]));
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<u32x2_t*>(stg + stg64(r, q) + hh * 8) =
+              pack4(acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]);
+        const int qf = cq0 + wn * 64 + f * 32;
+        const int valid = min(4, (p.Q - qf) >> 3);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int rr = 16 * k + (lane >> 2), c = lane & 3;
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + stg64(rr, c));
+          const int pr = pr0 + rr;
+          if (pr < p.P && c < valid) st16(Ce + (int64_t)pr * p.Q + qf + c * 8, v);
         }
+      }
     }
+    if (!more) break;
   }
 }
 
@@ -619,7 +685,7 @@ hipError_t launch_wgrad(const uint16_t* A, const uint16_t* D, const int32_t* gro
                         int Q, uint16_t* C, hipStream_t stream) {
   if (E == 0) return hipSuccess;
   WgradP p{A, D, group_offsets, C, E, (int)M, P, Q};
-  wgrad_kernel<<<dim3(persistent_grid()), dim3(NTHR), 0, stream>>>(p);
+  wgrad_kernel<<<dim3(persistent_grid()), dim3(GTHR), 0, stream>>>(p);
   return hipGetLastError();
 }
 
