@@ -17,11 +17,8 @@
 namespace moe {
 namespace {
 
-constexpr int kTPW = 16;            // tokens per wave
 constexpr int kWaves = 4;
-constexpr int kTB = kTPW * kWaves;  // tokens per workgroup
-constexpr int kBK = 32;             // emb slice staged in LDS per step
-static_assert(2 * kBK == kTB, "the two w buffers must hold the logits of a workgroup's tokens");
+constexpr int kBK = 32;  // emb slice staged in LDS per step
 
 // Order-preserving key of a logit: larger logit -> larger key. -0 maps like +0;
 // NaN maps to 0, below every number.
@@ -53,11 +50,15 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // EQ = experts per lane: lane L holds experts L, L + 64, ..., L + 64 (EQ - 1).
-template <int EQ>
+// kTPW = tokens per wave: 16 up to 128 experts; 8 beyond, which halves the
+// registers of the chains and doubles the number of workgroups.
+template <int EQ, int kTPW>
 __global__ __launch_bounds__(256) void route_kernel(int64_t T, int emb, int E, int k, const uint16_t* __restrict__ x,
                                                     const float* __restrict__ wr, const float* __restrict__ bias,
                                                     const float* __restrict__ logits_in, int32_t* __restrict__ topk_idx,
                                                     float* __restrict__ topk_w) {
+  constexpr int kTB = kTPW * kWaves;  // tokens per workgroup
+  static_assert(kTB <= 2 * kBK, "the two w buffers must hold the logits of a workgroup's tokens");
   __shared__ __attribute__((aligned(16))) float s_x[2][kBK][kTB];
   __shared__ __attribute__((aligned(16))) float s_w[2][kBK][64 * EQ];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -82,14 +83,20 @@ __global__ __launch_bounds__(256) void route_kernel(int64_t T, int emb, int E, i
     // Slices of kBK emb values are double-buffered: the next slice is loaded
     // into registers while the current one feeds the FMA chains, then written
     // to the other LDS buffer; one barrier per slice.
-    const int tk = tid >> 2, seg = tid & 3;  // x: token tk of the block, 8 values at seg*8
+    constexpr int kXV = kTB * kBK / 256;  // x values per thread per slice: 8 or 4
+    const int tk = tid / (kBK / kXV), seg = tid % (kBK / kXV);  // x: token tk of the block, kXV values at seg*kXV
     const int64_t tx = t0 + tk;
     const bool vec_w = (E & 3) == 0;
     constexpr int kW4 = kBK * 64 * EQ / 4 / 256;  // float4 of the w slice per thread
     u32x4_t xr;
     f32x4_t wr4[kW4];
     auto load = [&](int i0) {
-      xr = tx < T ? ld16(x + tx * emb + i0 + seg * 8) : u32x4_t{0u, 0u, 0u, 0u};
+      if (kXV == 8) {
+        xr = tx < T ? ld16(x + tx * emb + i0 + seg * 8) : u32x4_t{0u, 0u, 0u, 0u};
+      } else {
+        const u32x2_t v = tx < T ? *reinterpret_cast<const u32x2_t*>(x + tx * emb + i0 + seg * 4) : u32x2_t{0u, 0u};
+        xr = u32x4_t{v[0], v[1], 0u, 0u};
+      }
 #pragma unroll
       for (int j = 0; j < kW4; ++j) {
         const int idx = (tid + 256 * j) * 4, ii = idx / (64 * EQ), e = idx % (64 * EQ);
@@ -104,9 +111,9 @@ __global__ __launch_bounds__(256) void route_kernel(int64_t T, int emb, int E, i
     };
     auto store = [&](int b) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        s_x[b][seg * 8 + 2 * u][tk] = bf16_lo(xr[u]);
-        s_x[b][seg * 8 + 2 * u + 1][tk] = bf16_hi(xr[u]);
+      for (int u = 0; u < kXV / 2; ++u) {
+        s_x[b][seg * kXV + 2 * u][tk] = bf16_lo(xr[u]);
+        s_x[b][seg * kXV + 2 * u + 1][tk] = bf16_hi(xr[u]);
       }
 #pragma unroll
       for (int j = 0; j < kW4; ++j) {
@@ -210,13 +217,14 @@ __global__ __launch_bounds__(256) void route_kernel(int64_t T, int emb, int E, i
 hipError_t launch_route(int64_t T, int emb, int E, int k, const uint16_t* x, const float* wr, const float* bias,
                         const float* logits_in, int32_t* topk_idx, float* topk_w, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  const dim3 grid((unsigned)((T + kTB - 1) / kTB)), block(256);
   const int eq = (E + 63) / 64;
+  const int tb = (eq <= 2 ? 16 : 8) * kWaves;
+  const dim3 grid((unsigned)((T + tb - 1) / tb)), block(256);
   switch (eq) {
-    case 1: route_kernel<1><<<grid, block, 0, stream>>>(T, emb, E, k, x, wr, bias, logits_in, topk_idx, topk_w); break;
-    case 2: route_kernel<2><<<grid, block, 0, stream>>>(T, emb, E, k, x, wr, bias, logits_in, topk_idx, topk_w); break;
-    case 3: route_kernel<3><<<grid, block, 0, stream>>>(T, emb, E, k, x, wr, bias, logits_in, topk_idx, topk_w); break;
-    default: route_kernel<4><<<grid, block, 0, stream>>>(T, emb, E, k, x, wr, bias, logits_in, topk_idx, topk_w); break;
+    case 1: route_kernel<1, 16><<<grid, block, 0, stream>>>(T, emb, E, k, x, wr, bias, logits_in, topk_idx, topk_w); break;
+    case 2: route_kernel<2, 16><<<grid, block, 0, stream>>>(T, emb, E, k, x, wr, bias, logits_in, topk_idx, topk_w); break;
+    case 3: route_kernel<3, 8><<<grid, block, 0, stream>>>(T, emb, E, k, x, wr, bias, logits_in, topk_idx, topk_w); break;
+    default: route_kernel<4, 8><<<grid, block, 0, stream>>>(T, emb, E, k, x, wr, bias, logits_in, topk_idx, topk_w); break;
   }
   return hipGetLastError();
 }
