@@ -71,7 +71,7 @@ const char* moe_version(void);
 /*
  * moe_query_support: MOE_OK if the layer kernels accept this shape, else the
  * reason (MOE_ERR_SHAPE / MOE_ERR_UNSUPPORTED, detail text set). Supported:
- * 0 <= T, T*k < 2^31; emb % 64 == 0; mlp % 64 == 0; 1 <= k <= 64; k <= E <= 256.
+ * 0 <= T, T*k < 2^31, T*emb < 2^31; emb % 64 == 0; mlp % 64 == 0; 1 <= k <= 64; k <= E <= 256.
  * The pages' own Pallas kernels guard a similar envelope (a capability check
  * on dtype, width multiple of 128 lanes, row count = tokens * k and k <= 128;
  * "MoE: fused TensorCore Pallas permute/combine kernels ...", Code Review).

@@ -68,6 +68,8 @@ int check_shape(const moe_shape_t* s) {
   if (s->emb % 64) return fail(MOE_ERR_UNSUPPORTED, "emb (%d) is not a multiple of 64", s->emb);
   if (s->mlp % 64) return fail(MOE_ERR_UNSUPPORTED, "mlp (%d) is not a multiple of 64", s->mlp);
   if (s->T * (int64_t)s->k >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "T*k >= 2^31");
+  // token rows are read through 32-bit offsets when gathered (dy in the backward)
+  if (s->T * (int64_t)s->emb >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "T*emb >= 2^31");
   if ((int64_t)s->emb * 2 * s->mlp >= (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED, "emb*2*mlp >= 2^31 (per-expert weight too large)");
   if (s->T * (int64_t)s->k * 2 * s->mlp >= (int64_t(1) << 40))

@@ -61,6 +61,7 @@ def _shape(T=64, emb=128, mlp=256, E=8, k=2):
     (dict(emb=96), _lib.MOE_ERR_UNSUPPORTED),
     (dict(mlp=100), _lib.MOE_ERR_UNSUPPORTED),
     (dict(T=1 << 30, k=4, E=8), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(T=1 << 20, emb=2048, k=1, E=8), _lib.MOE_ERR_UNSUPPORTED),  # T*emb = 2^31
     (dict(T=32768, emb=2048, mlp=768, E=128, k=8), _lib.MOE_OK),
     (dict(T=8192, emb=7168, mlp=2048, E=256, k=8), _lib.MOE_OK),
 ])
