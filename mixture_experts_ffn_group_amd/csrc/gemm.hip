@@ -377,14 +377,16 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
         if (s < nk) issue_loads(s);
     // Epilogue. Lane holds rows m = tile row + lane%32 and, per register group q,
     // four consecutive columns 8q + 4*(lane/32) + 0..3 of each 32-wide fragment.
-    // NONE and SWIGLU pass their output through this wave's LDS staging area,
-    // 32 rows x 64 bytes at a time, and store whole 64-byte row segments:
-    // stores straight from the MFMA layout would write 8 bytes into each of 32
-    // rows per instruction.
+    // NONE and SWIGLU pass their output through this wave's 2 KB LDS staging
+    // area and store whole row segments (128 B for NONE, 64 B for the SwiGLU
+    // output): stores straight from the MFMA layout would write 8 bytes into
+    // each of 32 rows per instruction.
     const int hh = lane >> 5;
     uint8_t* const stg = s_stage[wave];
     // [32 rows][64 B] block, 16-byte chunk c of row r at r*64 + ((c ^ ((r >> 2) & 3)) << 4)
     auto stg64 = [&](int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); };
+    // [16 rows][128 B] block: r*128 + ((c ^ ((r >> 1) & 7)) << 4)
+    auto stg128 = [&](int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); };
     const int r = lane & 31;
     // Read the staged block back, four lanes per row, and store rows m0r + 0..31,
     // 16 bytes at column byte offset 16 * (lane % 4) from row_ptr(m).
@@ -398,19 +400,32 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
       }
     };
     if (EPI == EPI_NONE) {
+      // Both 32-column fragments of the wave form 128-byte row segments: stage
+      // 16 rows x 128 B per round and store whole 128-byte lines, 8 lanes per row.
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float sc = sc4[i];
         const int m0r = cm0 + wm * 128 + i * 32;
+        const int n0w = cn0 + wn * 64;
+        const int valid = min(8, (p.N - n0w) >> 3);
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
+        for (int h = 0; h < 2; ++h) {
+          if ((r >> 4) == h) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<u32x2_t*>(stg + stg64(r, q) + hh * 8) =
-                pack4(sc * acc[i][f][4 * q], sc * acc[i][f][4 * q + 1], sc * acc[i][f][4 * q + 2],
-                      sc * acc[i][f][4 * q + 3]);
-          const int n0f = cn0 + wn * 64 + f * 32;
-          drain(m0r, [&](int m) { return (void*)(p.C + (int64_t)m * p.N + n0f); }, min(4, (p.N - n0f) >> 3));
+            for (int f = 0; f < 2; ++f)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<u32x2_t*>(stg + stg128(r - 16 * h, f * 4 + q) + hh * 8) =
+                    pack4(sc * acc[i][f][4 * q], sc * acc[i][f][4 * q + 1], sc * acc[i][f][4 * q + 2],
+                          sc * acc[i][f][4 * q + 3]);
+          }
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            const int rr = 8 * kk + (lane >> 3), c = lane & 7;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + stg128(rr, c));
+            const int m = m0r + 16 * h + rr;
+            if (m < cm_end && c < valid) st16(p.C + (int64_t)m * p.N + n0w + c * 8, v);
+          }
         }
       }
     } else if (EPI == EPI_SWIGLU) {
@@ -623,28 +638,32 @@ __global__ __launch_bounds__(GTHR, 1) void wgrad_kernel(WgradP p) {
     if (more)
       for (int s = 0; s < NST; ++s)
         if (s < nk) issue_loads(s);
-    // Epilogue through this wave's staging area, 32 rows x 64 bytes at a time (as in gemm_kernel).
+    // Epilogue through this wave's staging area, 16 rows x 128 bytes at a time (as in gemm_kernel).
     const int hh = lane >> 5, r = lane & 31;
     uint8_t* const stg = s_stage[wave];
-    auto stg64 = [&](int rr, int c) { return rr * 64 + ((c ^ ((rr >> 2) & 3)) << 4); };
+    auto stg128 = [&](int rr, int c) { return rr * 128 + ((c ^ ((rr >> 1) & 7)) << 4); };
     uint16_t* const Ce = p.C + (int64_t)ce * p.P * p.Q;
+    const int qw = cq0 + wn * 64;
+    const int valid = min(8, (p.Q - qw) >> 3);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int pr0 = cp0 + wm * 128 + i * 32;
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
+      for (int h = 0; h < 2; ++h) {
+        if ((r >> 4) == h) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<u32x2_t*>(stg + stg64(r, q) + hh * 8) =
-              pack4(acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]);
-        const int qf = cq0 + wn * 64 + f * 32;
-        const int valid = min(4, (p.Q - qf) >> 3);
+          for (int f = 0; f < 2; ++f)
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const int rr = 16 * k + (lane >> 2), c = lane & 3;
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + stg64(rr, c));
-          const int pr = pr0 + rr;
-          if (pr < p.P && c < valid) st16(Ce + (int64_t)pr * p.Q + qf + c * 8, v);
+            for (int q = 0; q < 4; ++q)
+              *reinterpret_cast<u32x2_t*>(stg + stg128(r - 16 * h, f * 4 + q) + hh * 8) =
+                  pack4(acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int rr = 8 * kk + (lane >> 3), c = lane & 7;
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + stg128(rr, c));
+          const int pr = pr0 + 16 * h + rr;
+          if (pr < p.P && c < valid) st16(Ce + (int64_t)pr * p.Q + qw + c * 8, v);
         }
       }
     }
