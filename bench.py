@@ -6,12 +6,17 @@
 One step = one pass of the whole forward hot path over one batch: route,
 permute, grouped GEMM 1 (prefused wi, SwiGLU epilogue), grouped GEMM 2 (wo),
 combine. The timed loop calls the library's stage entry points in exactly
-the order moe_ffn_fwd does, with HIP events between launches on the stream
-the kernels run on, so every kernel's duration is measured inside the timed
-region. Inputs are resident in HBM before timing starts. Prints ONE JSON line.
+the order and form moe_ffn_fwd uses, with HIP events between launches on the
+stream the kernels run on, so every kernel's duration is measured inside the
+timed region. Inputs are resident in HBM before timing starts. Prints ONE
+JSON line.
 
-With --backward (DeepSeek-V3-shaped workload) the step also runs the layer
-backward (combine-bwd, NT GEMM + SwiGLU-bwd, NT GEMM, permute-bwd, wgrad x2).
+Forward only is the inference path: the permute builds the expert-sorted
+index and GEMM 1 reads the token rows of x in place through it. With
+--backward (DeepSeek-V3-shaped workload) the forward materialises the sorted
+rows and the fp32 gate/up values for the backward, and the step also runs
+the layer backward (combine-bwd, NT GEMM + SwiGLU-bwd, NT GEMM, permute-bwd,
+wgrad x2).
 """
 from __future__ import annotations
 
@@ -93,6 +98,12 @@ def main():
     st = C.c_void_p(stream.cuda_stream)
     sv = saved
 
+    # Inference (forward only) runs the path moe_ffn_fwd takes without a saved set: the permute builds
+    # the index only and GEMM1 gathers the x rows through sorted_slot. With --backward the forward
+    # materialises xs and h, which the backward reads.
+    gather = not bwd
+    rows = _lib.MoeGemmRows(P(sv["sorted_slot"]), S, k, None) if gather else None
+
     def stage_calls():
         """The forward (and optional backward) as separate library calls, in moe_ffn_fwd order."""
         calls = [
@@ -100,10 +111,11 @@ def main():
                                           P(logits), P(sv["topk_idx"]), P(sv["topk_w"]), st)),
             ("permute", lambda: L.moe_permute(C.byref(shp), P(x), P(sv["topk_idx"]), P(sv["group_sizes"]),
                                               P(sv["group_offsets"]), P(sv["sorted_slot"]), P(sv["slot_row"]),
-                                              P(sv["xs"]), P(pws), pws.numel(), st)),
-            ("gemm1_swiglu", lambda: L.moe_grouped_gemm(0, 1, P(sv["xs"]), P(wi), None, P(sv["h"]) if bwd else None,
-                                                        P(sv["group_offsets"]), E, S, emb, 2 * mlp, None, P(sv["a"]),
-                                                        st)),
+                                              None if gather else P(sv["xs"]), P(pws), pws.numel(), st)),
+            ("gemm1_swiglu", lambda: L.moe_grouped_gemm(0, 1, P(x) if gather else P(sv["xs"]), P(wi), None,
+                                                        P(sv["h"]) if bwd else None, P(sv["group_offsets"]), E, S,
+                                                        emb, 2 * mlp, C.byref(rows) if gather else None,
+                                                        P(sv["a"]), st)),
             ("gemm2", lambda: L.moe_grouped_gemm(0, 0, P(sv["a"]), P(wo), None, None, P(sv["group_offsets"]), E, S,
                                                  mlp, emb, None, P(sv["o"]), st)),
             ("combine", lambda: L.moe_combine(C.byref(shp), P(sv["o"]), P(sv["slot_row"]), P(sv["topk_w"]), P(y),
@@ -161,9 +173,10 @@ def main():
     tokens_per_s = T / (ms_step * 1e-3)
     fwd_flop = 6.0 * S * emb * mlp              # active-expert FLOPs of the two GEMMs
     g1_flop, g2_flop = 4.0 * S * emb * mlp, 2.0 * S * mlp * emb
-    g1_bytes = S * emb * 2 + e_nz * emb * 2 * mlp * 2 + S * mlp * 2 + (S * 2 * mlp * 4 if bwd else 0)
+    a_rows_bytes = T * emb * 2 if gather else S * emb * 2  # GEMM1's A: x read in place, or the sorted copy
+    g1_bytes = a_rows_bytes + e_nz * emb * 2 * mlp * 2 + S * mlp * 2 + (S * 2 * mlp * 4 if bwd else 0)
     g2_bytes = S * mlp * 2 + e_nz * mlp * emb * 2 + S * emb * 2
-    perm_bytes = T * emb * 2 + S * emb * 2 + 12 * S
+    perm_bytes = 12 * S if gather else T * emb * 2 + S * emb * 2 + 12 * S
     comb_bytes = S * emb * 2 + 8 * S + T * emb * 2
     route_flop = 0.0 if logits is not None else 2.0 * T * emb * E
     route_bytes = (T * E * 4 if logits is not None else T * emb * 2 + emb * E * 4) + 8 * S
@@ -180,7 +193,8 @@ def main():
                       peak=PEAK_FP32_FMA_TFLOPS if route_flop else PEAK_HBM_GBS,
                       unit="TFLOP/s" if route_flop else "GB/s"),
         "permute": dict(ms=stage_ms["permute"], bound="hbm", achieved=gb(perm_bytes, stage_ms["permute"]),
-                        peak=PEAK_HBM_GBS, unit="GB/s", bytes=perm_bytes),
+                        peak=PEAK_HBM_GBS, unit="GB/s", bytes=perm_bytes,
+                        rows="index only; GEMM1 gathers the x rows" if gather else "rows copied to xs"),
         "gemm1_swiglu": dict(ms=stage_ms["gemm1_swiglu"], bound="mfma",
                              achieved=tf(g1_flop, stage_ms["gemm1_swiglu"]), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                              flop=g1_flop, bytes=g1_bytes, hbm_gbs=gb(g1_bytes, stage_ms["gemm1_swiglu"])),
@@ -209,7 +223,8 @@ def main():
         except Exception:
             traffic = None
     g1 = stages["gemm1_swiglu"]
-    roofline = {"bound": "mfma", "kernel": "gemm_kernel<NN,SWIGLU> (grouped GEMM 1 on prefused wi)",
+    roofline = {"bound": "mfma", "kernel": "gemm_kernel<NN,SWIGLU%s> (grouped GEMM 1 on prefused wi)"
+                % (", row gather" if gather else ""),
                 "achieved": round(g1["achieved"], 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(g1["frac"], 4), "traffic": traffic,
                 "per_launch_flop": g1_flop, "avg_launch_ms": round(g1["ms"], 5)}

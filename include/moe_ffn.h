@@ -119,6 +119,10 @@ int moe_route(const moe_shape_t* shape, const moe_bf16_t* x, const float* wr, co
  *  group_offsets[E] = S), sorted_slot [S] (row r holds slot t*k + j),
  *  slot_row [S] (its inverse), xs [S, emb] bf16 (row r = x[sorted_slot[r]/k]).
  *  Row order: by expert, then by token (stable), so it is unique.
+ *  xs may be NULL: then only the index is built (group_sizes, group_offsets,
+ *  sorted_slot, slot_row) and x may be NULL too. A grouped GEMM then reads
+ *  the token rows in place through sorted_slot (moe_gemm_rows_t with
+ *  slot_div = k) instead of from a sorted copy.
  *  ws: at least moe_permute_workspace_bytes(shape) bytes of device memory.
  */
 int moe_permute(const moe_shape_t* shape, const moe_bf16_t* x, const int32_t* topk_idx, int32_t* group_sizes,
@@ -219,6 +223,11 @@ typedef struct {
  *  Router inputs as in moe_route. saved: NULL for inference (intermediates
  *  live in the workspace and h is not produced), else every pointer in it
  *  must be set and receives the intermediates.
+ *  For inference the expert-sorted copy xs is not written: the permute builds
+ *  only the index and GEMM1 gathers x rows through sorted_slot, the
+ *  single-device half of the fused MoE kernel of "Fused MoE Kernel
+ *  integration and optimization - #3388" (Summary). With saved, xs is built
+ *  (the weight gradient reads it).
  *  ws: at least moe_workspace_bytes(shape, 0) bytes.
  */
 int moe_ffn_fwd(const moe_shape_t* shape, const moe_bf16_t* x, const float* wr, const float* bias,

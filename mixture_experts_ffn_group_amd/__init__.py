@@ -86,9 +86,9 @@ def route(k: int, x: torch.Tensor | None = None, wr: torch.Tensor | None = None,
     return idx, w
 
 
-def permute(x: torch.Tensor, topk_idx: torch.Tensor, E: int) -> dict:
+def permute(x: torch.Tensor, topk_idx: torch.Tensor, E: int, rows: bool = True) -> dict:
     """Expert-sorted gather: dict of group_sizes [E], group_offsets [E+1], sorted_slot [S], slot_row [S]
-    (int32) and xs [S, emb] bf16."""
+    (int32) and xs [S, emb] bf16. rows=False builds the index only (no xs)."""
     _need(x, "x", torch.bfloat16)
     dev = x.device
     _need(topk_idx, "topk_idx", torch.int32, dev)
@@ -102,7 +102,7 @@ def permute(x: torch.Tensor, topk_idx: torch.Tensor, E: int) -> dict:
                group_offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
                sorted_slot=torch.empty(S, dtype=torch.int32, device=dev),
                slot_row=torch.empty(S, dtype=torch.int32, device=dev),
-               xs=torch.empty((S, emb), dtype=torch.bfloat16, device=dev))
+               xs=torch.empty((S, emb), dtype=torch.bfloat16, device=dev) if rows else None)
     _lib.check(_lib.lib().moe_permute(C.byref(s), _ptr(x), _ptr(topk_idx), _ptr(out["group_sizes"]),
                                       _ptr(out["group_offsets"]), _ptr(out["sorted_slot"]), _ptr(out["slot_row"]),
                                       _ptr(out["xs"]), _ptr(ws), ws.numel(), _stream(dev)), "moe_permute")

@@ -194,11 +194,11 @@ int moe_permute(const moe_shape_t* s, const moe_bf16_t* x, const int32_t* topk_i
   NEED(group_sizes);
   NEED(group_offsets);
   if (s->T > 0) {
-    NEED(x);
     NEED(topk_idx);
     NEED(sorted_slot);
     NEED(slot_row);
-    NEED(xs);
+    MAYBE(xs);  // NULL: index only, the rows are not copied
+    if (xs) NEED(x);
   }
   NEED(ws);
   if (ws_bytes < permute_ws(s)) return fail(MOE_ERR_WORKSPACE, "need %zu workspace bytes", permute_ws(s));
@@ -351,12 +351,17 @@ int moe_ffn_fwd(const moe_shape_t* s, const moe_bf16_t* x, const float* wr, cons
                                             v.topk_w, st),
                           "route"))
     return rc;
+  // Inference (nothing saved): the permute builds only the index, and GEMM1 reads each
+  // token row of x in place through sorted_slot, so the expert-sorted copy xs is never
+  // written. Training keeps xs, which the weight gradient reads.
+  const bool gather = saved == nullptr;
   if (int rc = hip_status(moe::launch_permute(T, emb, E, k, x, v.topk_idx, v.group_sizes, v.group_offsets,
-                                              v.sorted_slot, v.slot_row, v.xs, masks, base, st),
+                                              v.sorted_slot, v.slot_row, gather ? nullptr : v.xs, masks, base, st),
                           "permute"))
     return rc;
-  if (int rc = hip_status(moe::launch_grouped_gemm(MOE_NN, MOE_EPI_SWIGLU, v.xs, wi, nullptr, v.h, v.group_offsets, E,
-                                                   S, emb, 2 * mlp, nullptr, 0, 1, nullptr, v.a, st),
+  if (int rc = hip_status(moe::launch_grouped_gemm(MOE_NN, MOE_EPI_SWIGLU, gather ? x : v.xs, wi, nullptr, v.h,
+                                                   v.group_offsets, E, S, emb, 2 * mlp, gather ? v.sorted_slot : nullptr,
+                                                   gather ? (int)S : 0, gather ? k : 1, nullptr, v.a, st),
                           "gemm1"))
     return rc;
   if (int rc = hip_status(moe::launch_grouped_gemm(MOE_NN, MOE_EPI_NONE, v.a, wo, nullptr, nullptr, v.group_offsets,

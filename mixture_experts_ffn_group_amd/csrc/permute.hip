@@ -147,6 +147,26 @@ __global__ __launch_bounds__(256) void scatter_kernel(int64_t T, int emb, int E,
   }
 }
 
+// Index only (no row copy), one thread per slot s = t*k + j: the same stable
+// rank as scatter_kernel, for callers that read the rows in place through
+// sorted_slot (the grouped GEMM's row gather).
+__global__ __launch_bounds__(256) void index_kernel(int64_t T, int E, int k, const int32_t* __restrict__ topk_idx,
+                                                    const uint64_t* __restrict__ masks,
+                                                    const int32_t* __restrict__ base,
+                                                    int32_t* __restrict__ sorted_slot,
+                                                    int32_t* __restrict__ slot_row) {
+  const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (s >= T * k) return;
+  const int64_t t = s / k;
+  const int64_t b = t / kPermuteBlock;
+  const int tl = (int)(t % kPermuteBlock);
+  const int e = topk_idx[s];
+  if ((unsigned)e >= (unsigned)E) return;
+  const int32_t r = base[b * E + e] + __popcll(masks[b * E + e] & ((1ull << tl) - 1ull));
+  sorted_slot[r] = (int32_t)s;
+  slot_row[s] = r;
+}
+
 }  // namespace
 
 hipError_t launch_permute(int64_t T, int emb, int E, int k, const uint16_t* x, const int32_t* topk_idx,
@@ -159,8 +179,12 @@ hipError_t launch_permute(int64_t T, int emb, int E, int k, const uint16_t* x, c
   // The scan also runs for T == 0 so that group_sizes / group_offsets are written (all zero).
   scan_kernel<<<dim3(1), dim3(1024), 0, stream>>>(nblk, E, masks, group_sizes, group_offsets, base);
   if (T > 0) {
-    scatter_kernel<<<dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream>>>(T, emb, E, k, x, topk_idx, masks, base,
-                                                                           sorted_slot, slot_row, xs);
+    if (xs)
+      scatter_kernel<<<dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream>>>(T, emb, E, k, x, topk_idx, masks, base,
+                                                                             sorted_slot, slot_row, xs);
+    else
+      index_kernel<<<dim3((unsigned)((T * k + 255) / 256)), dim3(256), 0, stream>>>(T, E, k, topk_idx, masks, base,
+                                                                                  sorted_slot, slot_row);
   }
   return hipGetLastError();
 }

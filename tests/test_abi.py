@@ -97,6 +97,10 @@ def test_validation_precedes_any_launch(lib):
         _lib.MOE_ERR_WORKSPACE
     assert lib.moe_permute(C.byref(s), fake, fake, fake, fake, fake, fake, fake, nul, 1 << 20, nul) == \
         _lib.MOE_ERR_NULL
+    # index-only permute: xs and x may be NULL, the index outputs may not
+    assert lib.moe_permute(C.byref(s), nul, fake, fake, fake, nul, fake, nul, fake, 0, nul) == _lib.MOE_ERR_NULL
+    assert lib.moe_permute(C.byref(s), nul, fake, fake, fake, fake, fake, nul, fake, 0, nul) == \
+        _lib.MOE_ERR_WORKSPACE
     # grouped GEMM: bad op, wrong epilogue/op pairs, K not a multiple of 64, N not a multiple of 8
     assert lib.moe_grouped_gemm(7, 0, fake, fake, nul, nul, fake, 4, 128, 64, 64, None, fake, nul) == _lib.MOE_ERR_SHAPE
     assert lib.moe_grouped_gemm(1, 1, fake, fake, nul, nul, fake, 4, 128, 64, 64, None, fake, nul) == \

@@ -93,6 +93,18 @@ def test_layer_forward_is_deterministic_and_writes_every_output():
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
+@pytest.mark.parametrize("name", ["tiny", "mid_skewed"])
+def test_layer_forward_inference_gather_equals_training_forward_bitwise(name):
+    """Inference reads x rows in place through sorted_slot; training materialises xs first. The GEMM
+    arithmetic is the same, so y must agree bit for bit."""
+    h = workloads.make_inputs(name)
+    d = _dev(h)
+    y_inf, _ = _fwd(d, save=False)
+    y_trn, saved = _fwd(d, save=True)
+    assert saved is not None
+    assert torch.equal(y_inf.view(torch.int16), y_trn.view(torch.int16))
+
+
 def test_layer_forward_wo_times_two_doubles_y_exactly():
     h = workloads.make_inputs("tiny")
     d = _dev(h)

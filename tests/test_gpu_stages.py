@@ -104,6 +104,22 @@ def test_permute_bit_exact(T, emb, E, k, skew):
     assert np.array_equal(bits(out["xs"]), oracle.permute(bits(x), ss, k))
 
 
+@pytest.mark.parametrize("T,emb,E,k,skew", [(1000, 256, 16, 4, True), (129, 64, 256, 8, False), (1, 64, 4, 4, False),
+                                            (5000, 128, 128, 8, True), (0, 64, 8, 2, False)])
+def test_permute_index_only_matches_the_oracle_dispatch(T, emb, E, k, skew):
+    """With no xs the permute builds the same index by its own per-slot kernel, and copies no row."""
+    rng = np.random.default_rng(T + 3 * E)
+    x = torch.from_numpy(rng.standard_normal((T, emb)).astype(np.float32)).to(torch.bfloat16)
+    idx = _random_idx(T, E, k, T + 1, skew)
+    out = moe.permute(x.to(DEV), torch.from_numpy(idx).to(DEV), E, rows=False)
+    assert out["xs"] is None
+    gs, go, ss, sr = oracle.dispatch(idx, E)
+    assert np.array_equal(out["group_sizes"].cpu().numpy(), gs)
+    assert np.array_equal(out["group_offsets"].cpu().numpy(), go)
+    assert np.array_equal(out["sorted_slot"].cpu().numpy(), ss)
+    assert np.array_equal(out["slot_row"].cpu().numpy(), sr)
+
+
 def test_permute_empty_expert_and_single_hot_expert():
     T, emb, E, k = 500, 128, 8, 2
     idx = np.zeros((T, k), np.int32)
