@@ -39,7 +39,8 @@ __global__ __launch_bounds__(256) void hist_kernel(int64_t T, int E, int k, int6
     for (int e = lane; e < E; e += 64) masks[blk * E + e] = s_m[wave][e];
 }
 
-// Single workgroup. Thread (e, p) owns a contiguous chunk of blocks of expert e.
+// Single workgroup. Thread (e, p) owns a contiguous chunk of blocks of expert e
+// (loops unrolled so that several mask loads are in flight per thread).
 __global__ __launch_bounds__(1024) void scan_kernel(int64_t nblk, int E, const uint64_t* __restrict__ masks,
                                                     int32_t* __restrict__ group_sizes,
                                                     int32_t* __restrict__ group_offsets, int32_t* __restrict__ base) {
@@ -54,8 +55,10 @@ __global__ __launch_bounds__(1024) void scan_kernel(int64_t nblk, int E, const u
   const int64_t b0 = (int64_t)p * chunk;
   const int64_t b1 = b0 + chunk < nblk ? b0 + chunk : nblk;
   int32_t s = 0;
-  if (active)
+  if (active) {
+#pragma unroll 8
     for (int64_t b = b0; b < b1; ++b) s += __popcll(masks[b * E + e]);
+  }
   s_part[tid] = s;
   __syncthreads();
   if (tid < E) {  // exclusive scan over the chunks of expert tid
@@ -96,6 +99,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(int64_t nblk, int E, const u
   if (tid <= E) group_offsets[tid] = s_excl[tid];
   if (active) {
     int32_t run = s_excl[e] + s_part[p * E + e];
+#pragma unroll 8
     for (int64_t b = b0; b < b1; ++b) {
       base[b * E + e] = run;
       run += __popcll(masks[b * E + e]);
