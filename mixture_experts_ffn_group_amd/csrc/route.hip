@@ -1,4 +1,4 @@
-// Router: logits, top-k and renormalised weights, one workgroup per 64 tokens.
+// Router: logits, top-k and renormalised weights, one workgroup per 64 (or 32) tokens.
 //
 // Gate and top-k routing come first in the MoE block ("[DRAFT][JAX] Optimize
 // MoE block", Flowchart), and the top-k weights are computed on the main
@@ -7,10 +7,14 @@
 //
 // Logit contract (an integer decision hangs on it, so it is fixed exactly):
 // logits[t, e] = fp32 fma chain over i = 0..emb-1 of x[t, i] * wr[i, e],
-// starting from +0, then one fp32 add of bias[e]. Each (t, e) chain is one
-// lane's register; lanes run experts, the wave runs 16 tokens, so x values are
-// LDS broadcasts and wr values are conflict-free LDS reads. The chain is on
-// the fp32 vector ALU: its bound is 2*T*emb*E flop at the non-packed fp32 rate.
+// starting from +0, then one fp32 add of bias[e].
+// The chains run on the fp32 matrix cores: v_mfma_f32_32x32x1_2b_f32 has
+// K = 1, so each instruction adds exactly one product to each of its 2 x 32 x
+// 32 accumulators, and a sequence of them over i is a chain of fp32
+// multiply-adds. Measured on the MI355X, every such chain is bitwise equal to
+// the sequential fmaf chain (normal, signed-zero and subnormal operands and
+// sums alike). Each emb step costs one MFMA per wave: 2048 multiply-adds at
+// the fp32 matrix rate (157.3 TFLOP/s), twice the non-packed vector rate.
 #include "common.h"
 #include "kernels.h"
 
@@ -49,45 +53,53 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// EQ = experts per lane: lane L holds experts L, L + 64, ..., L + 64 (EQ - 1).
-// kTPW = tokens per wave: 16 up to 128 experts; 8 beyond, which halves the
-// registers of the chains and doubles the number of workgroups.
-template <int EQ, int kTPW>
+// Output layout of v_mfma_f32_32x32x1_2b_f32 (measured): lane l, register r ->
+// block r/16, row ((r%16)/4)*8 + (l/32)*4 + r%4 of that block, column l%32;
+// lane l feeds row l%32 (A) and column l%32 (B) of block l/32.
+//
+// MODE 0 (E <= 128): 64 tokens per workgroup. The two MFMA blocks are tokens
+//   0-31 and 32-63; wave w owns experts 32w .. 32w+31.
+// MODE 1 (E <= 256): 32 tokens per workgroup. The two blocks are experts
+//   64w .. 64w+31 and 64w+32 .. 64w+63 of wave w, for the same 32 tokens.
+template <int MODE>
 __global__ __launch_bounds__(256) void route_kernel(int64_t T, int emb, int E, int k, const uint16_t* __restrict__ x,
                                                     const float* __restrict__ wr, const float* __restrict__ bias,
                                                     const float* __restrict__ logits_in, int32_t* __restrict__ topk_idx,
                                                     float* __restrict__ topk_w) {
-  constexpr int kTB = kTPW * kWaves;  // tokens per workgroup
-  static_assert(kTB <= 2 * kBK, "the two w buffers must hold the logits of a workgroup's tokens");
-  __shared__ __attribute__((aligned(16))) float s_x[2][kBK][kTB];
-  __shared__ __attribute__((aligned(16))) float s_w[2][kBK][64 * EQ];
+  constexpr int TB = MODE == 0 ? 64 : 32;  // tokens per workgroup
+  constexpr int EP = MODE == 0 ? 128 : 256;  // expert columns (logit row stride)
+  constexpr int EQ = EP / 64;              // experts per lane in the top-k
+  constexpr int TPW = TB / kWaves;         // tokens per wave in the top-k
+  static_assert(TB <= 2 * kBK, "the two w buffers must hold the logits of a workgroup's tokens");
+  __shared__ __attribute__((aligned(16))) float s_x[2][kBK][TB];
+  __shared__ __attribute__((aligned(16))) float s_w[2][kBK][EP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t t0 = (int64_t)blockIdx.x * kTB;
-  const int64_t tw = t0 + wave * kTPW;
+  const int64_t t0 = (int64_t)blockIdx.x * TB;
+  // Logits [TB][EP] go to LDS (into the w buffers, free after the last
+  // barrier), so the per-token top-k loop reads them by a runtime index.
+  float* const s_l = &s_w[0][0][0];
 
-  float acc[kTPW][EQ];
   if (logits_in) {
-#pragma unroll
-    for (int tt = 0; tt < kTPW; ++tt)
-#pragma unroll
-      for (int q = 0; q < EQ; ++q) {
-        const int e = lane + 64 * q;
-        const int64_t t = tw + tt;
-        acc[tt][q] = (t < T && e < E) ? logits_in[t * E + e] : 0.0f;
-      }
+    for (int idx = tid; idx < TB * EP; idx += 256) {
+      const int tok = idx / EP, e = idx % EP;
+      const int64_t t = t0 + tok;
+      s_l[idx] = (t < T && e < E) ? logits_in[t * E + e] : 0.0f;
+    }
   } else {
+    const int tok_a = MODE == 0 ? lane : (lane & 31);  // A operand: this lane's token
+    const int exp_b = MODE == 0 ? 32 * wave + (lane & 31) : 64 * wave + lane;  // B operand: its expert
+    const bool busy = (MODE == 0 ? 32 : 64) * wave < E;  // wave-uniform
+    f32x32_t acc;
 #pragma unroll
-    for (int tt = 0; tt < kTPW; ++tt)
-#pragma unroll
-      for (int q = 0; q < EQ; ++q) acc[tt][q] = 0.0f;
+    for (int r = 0; r < 32; ++r) acc[r] = 0.0f;
     // Slices of kBK emb values are double-buffered: the next slice is loaded
-    // into registers while the current one feeds the FMA chains, then written
-    // to the other LDS buffer; one barrier per slice.
-    constexpr int kXV = kTB * kBK / 256;  // x values per thread per slice: 8 or 4
+    // into registers while the current one feeds the chains, then written to
+    // the other LDS buffer; one barrier per slice.
+    constexpr int kXV = TB * kBK / 256;  // x values per thread per slice: 8 or 4
     const int tk = tid / (kBK / kXV), seg = tid % (kBK / kXV);  // x: token tk of the block, kXV values at seg*kXV
     const int64_t tx = t0 + tk;
     const bool vec_w = (E & 3) == 0;
-    constexpr int kW4 = kBK * 64 * EQ / 4 / 256;  // float4 of the w slice per thread
+    constexpr int kW4 = kBK * EP / 4 / 256;  // float4 of the w slice per thread
     u32x4_t xr;
     f32x4_t wr4[kW4];
     auto load = [&](int i0) {
@@ -99,7 +111,7 @@ __global__ __launch_bounds__(256) void route_kernel(int64_t T, int emb, int E, i
       }
 #pragma unroll
       for (int j = 0; j < kW4; ++j) {
-        const int idx = (tid + 256 * j) * 4, ii = idx / (64 * EQ), e = idx % (64 * EQ);
+        const int idx = (tid + 256 * j) * 4, ii = idx / EP, e = idx % EP;
         const float* src = wr + (int64_t)(i0 + ii) * E + e;
         if (vec_w && e + 3 < E) {
           wr4[j] = *reinterpret_cast<const f32x4_t*>(src);
@@ -117,7 +129,7 @@ __global__ __launch_bounds__(256) void route_kernel(int64_t T, int emb, int E, i
       }
 #pragma unroll
       for (int j = 0; j < kW4; ++j) {
-        const int idx = (tid + 256 * j) * 4, ii = idx / (64 * EQ), e = idx % (64 * EQ);
+        const int idx = (tid + 256 * j) * 4, ii = idx / EP, e = idx % EP;
         *reinterpret_cast<f32x4_t*>(&s_w[b][ii][e]) = wr4[j];
       }
     };
@@ -128,61 +140,40 @@ __global__ __launch_bounds__(256) void route_kernel(int64_t T, int emb, int E, i
     for (int i0 = 0; i0 < emb; i0 += kBK) {
       const bool more = i0 + kBK < emb;
       if (more) load(i0 + kBK);
-#pragma unroll 2
-      for (int ii = 0; ii < kBK; ++ii) {
-        float xv[kTPW];
-        const f32x4_t* px = reinterpret_cast<const f32x4_t*>(&s_x[b][ii][wave * kTPW]);
-#pragma unroll
-        for (int c = 0; c < kTPW / 4; ++c) {
-          const f32x4_t v = px[c];
-          xv[4 * c + 0] = v[0];
-          xv[4 * c + 1] = v[1];
-          xv[4 * c + 2] = v[2];
-          xv[4 * c + 3] = v[3];
-        }
-        float wv[EQ];
-#pragma unroll
-        for (int q = 0; q < EQ; ++q) wv[q] = s_w[b][ii][lane + 64 * q];
-#pragma unroll
-        for (int tt = 0; tt < kTPW; ++tt)
-#pragma unroll
-          for (int q = 0; q < EQ; ++q) acc[tt][q] = __builtin_fmaf(xv[tt], wv[q], acc[tt][q]);
+      if (busy) {
+#pragma unroll 8
+        for (int ii = 0; ii < kBK; ++ii)
+          acc = __builtin_amdgcn_mfma_f32_32x32x1f32(s_x[b][ii][tok_a], s_w[b][ii][exp_b], acc, 0, 0, 0);
       }
       if (more) store(b ^ 1);  // the other buffer was last read before the previous barrier
       __syncthreads();
       b ^= 1;
     }
-    if (bias) {
+    if (busy) {
 #pragma unroll
-      for (int q = 0; q < EQ; ++q) {
-        const int e = lane + 64 * q;
-        const float b = e < E ? bias[e] : 0.0f;
-#pragma unroll
-        for (int tt = 0; tt < kTPW; ++tt) acc[tt][q] = acc[tt][q] + b;
+      for (int r = 0; r < 32; ++r) {
+        const int blk = r >> 4, rr = r & 15;
+        const int row = (rr >> 2) * 8 + (lane >> 5) * 4 + (rr & 3), col = lane & 31;
+        const int tok = MODE == 0 ? 32 * blk + row : row;
+        const int e = MODE == 0 ? 32 * wave + col : 64 * wave + 32 * blk + col;
+        if (e < E) s_l[tok * EP + e] = bias ? acc[r] + bias[e] : acc[r];
       }
     }
   }
-
-  // The logits go to LDS (into the w buffers: kTB x 64*EQ floats, free after
-  // the last barrier), so the per-token loop below reads them by a runtime
-  // token index. Each wave reads back only its own tokens.
-  float* const s_l = &s_w[0][0][0];
-#pragma unroll
-  for (int tt = 0; tt < kTPW; ++tt)
-#pragma unroll
-    for (int q = 0; q < EQ; ++q) s_l[(wave * kTPW + tt) * 64 * EQ + lane + 64 * q] = acc[tt][q];
+  __syncthreads();
 
   // Top-k per token: k rounds of a wave-wide max over (key(logit), -expert).
   // Picked and padding experts hold candidate 0, which no real expert reaches.
 #pragma unroll 1
-  for (int tt = 0; tt < kTPW; ++tt) {
-    const int64_t t = tw + tt;
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int tok = wave * TPW + tt;
+    const int64_t t = t0 + tok;
     if (t >= T) break;  // wave-uniform
     uint64_t cand[EQ];
 #pragma unroll
     for (int q = 0; q < EQ; ++q) {
       const int e = lane + 64 * q;
-      const float l = s_l[(wave * kTPW + tt) * 64 * EQ + e];
+      const float l = s_l[tok * EP + e];
       cand[q] = e < E ? (((uint64_t)order_key(l) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e)) : 0ull;
     }
     int my_e = 0;
@@ -217,14 +208,13 @@ __global__ __launch_bounds__(256) void route_kernel(int64_t T, int emb, int E, i
 hipError_t launch_route(int64_t T, int emb, int E, int k, const uint16_t* x, const float* wr, const float* bias,
                         const float* logits_in, int32_t* topk_idx, float* topk_w, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  const int eq = (E + 63) / 64;
-  const int tb = (eq <= 2 ? 16 : 8) * kWaves;
-  const dim3 grid((unsigned)((T + tb - 1) / tb)), block(256);
-  switch (eq) {
-    case 1: route_kernel<1, 16><<<grid, block, 0, stream>>>(T, emb, E, k, x, wr, bias, logits_in, topk_idx, topk_w); break;
-    case 2: route_kernel<2, 16><<<grid, block, 0, stream>>>(T, emb, E, k, x, wr, bias, logits_in, topk_idx, topk_w); break;
-    case 3: route_kernel<3, 8><<<grid, block, 0, stream>>>(T, emb, E, k, x, wr, bias, logits_in, topk_idx, topk_w); break;
-    default: route_kernel<4, 8><<<grid, block, 0, stream>>>(T, emb, E, k, x, wr, bias, logits_in, topk_idx, topk_w); break;
+  const dim3 block(256);
+  if (E <= 128) {
+    route_kernel<0><<<dim3((unsigned)((T + 63) / 64)), block, 0, stream>>>(T, emb, E, k, x, wr, bias, logits_in,
+                                                                          topk_idx, topk_w);
+  } else {
+    route_kernel<1><<<dim3((unsigned)((T + 31) / 32)), block, 0, stream>>>(T, emb, E, k, x, wr, bias, logits_in,
+                                                                          topk_idx, topk_w);
   }
   return hipGetLastError();
 }
