@@ -52,6 +52,22 @@ def test_route_with_bias_empty_and_hot_experts():
     assert not (r_idx == 31).any()
 
 
+@pytest.mark.parametrize("E", [64, 200])
+def test_route_bit_exact_with_subnormal_products_and_logits(E):
+    """Products x*wr and the chains' partial sums in the fp32 subnormal range: the chain must still equal
+    the oracle's fmaf chain bitwise (no flush to zero), so the top-k and its tie order match."""
+    rng = np.random.default_rng(E)
+    T, emb, k = 150, 256, 4
+    x = torch.from_numpy((rng.standard_normal((T, emb)) * 1e-20).astype(np.float32)).to(torch.bfloat16)
+    wr = torch.from_numpy((rng.standard_normal((emb, E)) * 1e-19).astype(np.float32))
+    wr[:, 7] = 0.0                          # a zero column: logits exactly 0 -> ties broken by expert id
+    idx, w = moe.route(k, x=x.to(DEV), wr=wr.to(DEV))
+    r_idx, r_w, logits = oracle.route(bits(x), wr.numpy(), None, k)
+    assert np.abs(logits).max() < 2e-37      # the workload really is in the subnormal range
+    assert np.array_equal(idx.cpu().numpy(), r_idx)
+    assert np.abs(w.cpu().numpy() - r_w).max(initial=0) <= W_ABS
+
+
 def test_route_logits_in_with_ties_zero_signs_and_minus_inf():
     rng = np.random.default_rng(11)
     T, E, k = 300, 40, 6
