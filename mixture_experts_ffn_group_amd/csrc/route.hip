@@ -140,10 +140,15 @@ __global__ __launch_bounds__(256) void route_kernel(int64_t T, int emb, int E, i
     for (int i0 = 0; i0 < emb; i0 += kBK) {
       const bool more = i0 + kBK < emb;
       if (more) load(i0 + kBK);
-      if (busy) {
-#pragma unroll 8
-        for (int ii = 0; ii < kBK; ++ii)
-          acc = __builtin_amdgcn_mfma_f32_32x32x1f32(s_x[b][ii][tok_a], s_w[b][ii][exp_b], acc, 0, 0, 0);
+      if (busy) {  // all operands of the slice first, so the chain runs while the reads land
+        float xv[kBK], wv[kBK];
+#pragma unroll
+        for (int ii = 0; ii < kBK; ++ii) {
+          xv[ii] = s_x[b][ii][tok_a];
+          wv[ii] = s_w[b][ii][exp_b];
+        }
+#pragma unroll
+        for (int ii = 0; ii < kBK; ++ii) acc = __builtin_amdgcn_mfma_f32_32x32x1f32(xv[ii], wv[ii], acc, 0, 0, 0);
       }
       if (more) store(b ^ 1);  // the other buffer was last read before the previous barrier
       __syncthreads();
