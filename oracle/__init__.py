@@ -52,6 +52,8 @@ def _lib(real: str) -> C.CDLL:
             "orc_grouped_wgrad": ([_p, C.c_int, _p, C.c_int, _p, _i32, _i64, _i32, _i32, _i32, _p], C.c_int),
             "orc_combine": ([_i64, _i32, _i32, _p, C.c_int, _p, _p, _p], C.c_int),
             "orc_combine_bwd": ([_i64, _i32, _i32, _p, C.c_int, _p, C.c_int, _p, _p, _p, _p], C.c_int),
+            "orc_router_bwd": ([_i64, _i32, _i32, _i32, _p, C.c_int, _p, _p, _p, _p, C.c_int, _p, _p, _p, _p],
+                               C.c_int),
         }
         for name, (args, res) in sigs.items():
             f = getattr(lib, name)
@@ -351,3 +353,25 @@ def combine_bwd(dy, ys, slot_row, topk_w, k: int, real: str = "f32"):
     _check(_lib(real).orc_combine_bwd(T, emb, k, p, dt, yp, ydt, _ptr(slot_row), _ptr(w), _ptr(dys), _ptr(dw)),
            "combine_bwd")
     return dys, dw
+
+
+def router_bwd(x, wr, topk_idx, topk_w, dtopk_w, real: str = "f64", want_dx: bool = True):
+    """Router backward with the picks held fixed: (dlogits [T, E], dwr [emb, E], dbias [E], dx [T, emb] or None)."""
+    x = np.ascontiguousarray(x)
+    wr = _c(wr, np.float32)
+    idx = _c(topk_idx, np.int32)
+    w = _c(topk_w, np.float32)
+    g = np.ascontiguousarray(dtopk_w)
+    T, emb = x.shape
+    E = wr.shape[1]
+    k = idx.shape[1]
+    rt = _np_real(real)
+    dl = np.empty((T, E), rt)
+    dwr = np.empty((emb, E), rt)
+    db = np.empty(E, rt)
+    dx = np.empty((T, emb), rt) if want_dx else None
+    xp, xdt = _typed(x)
+    gp, gdt = _typed(g)
+    _check(_lib(real).orc_router_bwd(T, emb, E, k, xp, xdt, _ptr(wr), _ptr(idx), _ptr(w), gp, gdt, _ptr(dl),
+                                     _ptr(dwr), _ptr(db), _ptr(dx)), "router_bwd")
+    return dl, dwr, db, dx

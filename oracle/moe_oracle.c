@@ -37,6 +37,8 @@
  *    permutation for dx and a reduction for the weight gradient (same entry),
  *    and the permute backward is the combine forward with unit weights
  *    (commit 2).
+ *  - router backward through the renormalised top-k softmax, picks held
+ *    fixed (R7).
  *
  * Readings taken where the pages are silent (each is a choice, not a quote):
  *  R1 logits[t,e] = (fma chain over i = 0..emb-1 of x[t,i]*Wr[i,e], from 0.0f)
@@ -51,6 +53,8 @@
  *  R5 expert-sorted order = key (expert asc, token asc); a token picks an
  *     expert at most once, so the key is unique.
  *  R6 silu(g) = g / (1 + exp(-g)); SwiGLU a = silu(gate) * up.
+ *  R7 the router backward holds the picks fixed (the selection has no
+ *     gradient) and uses the forward's saved weights.
  */
 #include <math.h>
 #include <stdint.h>
@@ -483,6 +487,59 @@ int orc_combine(int64_t T, int32_t emb, int32_t k, const void* ys, int ys_dt, co
 
 /* Combine backward: dys[slot_row[t*k+j]] = w[t,j] * dy[t] (the permutation part) and
    dw[t,j] = <ys[slot_row[t*k+j]], dy[t]> (the reduction part; skipped when ys or dw is NULL). */
+/* Router backward with the picks held fixed: the top-k selection is
+   piecewise constant in the logits, so gradients flow only through the
+   weights. For token t the weights are the softmax over its k picked logits
+   (R4), w_j = exp(l_j) / sum_i exp(l_i), whose Jacobian is
+   dw_j/dl_m = w_j (delta_jm - w_m). With g = dtopk_w[t]:
+     dl[t, e_j] = w_j (g_j - sum_i w_i g_i), every other logit of t gets 0;
+   and through l = x Wr + bias:
+     dWr[i, e] = sum_t x[t, i] dl[t, e],  dbias[e] = sum_t dl[t, e],
+     dx[t, i]  = sum_e dl[t, e] Wr[i, e].
+   w and g are the forward's saved weights and the incoming gradient. The
+   routing gradients complete training ("MoE: fused TensorCore Pallas
+   permute/combine kernels ...", Commits table, commit 1: the combine
+   backward's weight-gradient reduction is what feeds them). */
+int orc_router_bwd(int64_t T, int32_t emb, int32_t E, int32_t k, const void* x, int x_dt, const float* wr,
+                   const int32_t* topk_idx, const float* topk_w, const void* g, int g_dt, real* dlogits, real* dwr,
+                   real* dbias, real* dx) {
+  if (T < 0 || emb <= 0 || E <= 0 || k <= 0 || k > E || !x || !wr || !topk_idx || !topk_w || !g || !dlogits ||
+      !dwr || !valid_dt(x_dt) || !valid_dt(g_dt))
+    return ORC_EINVAL;
+  for (int64_t t = 0; t < T; ++t)
+    for (int32_t j = 0; j < k; ++j) {
+      int32_t e = topk_idx[t * k + j];
+      if (e < 0 || e >= E) return ORC_ERANGE;
+    }
+  for (int64_t i = 0; i < T * (int64_t)E; ++i) dlogits[i] = 0;
+  for (int64_t t = 0; t < T; ++t) {
+    real s = 0;
+    for (int32_t j = 0; j < k; ++j) s += (real)topk_w[t * k + j] * (real)elem(g, g_dt, t * k + j);
+    for (int32_t j = 0; j < k; ++j) {
+      real wj = (real)topk_w[t * k + j];
+      dlogits[t * E + topk_idx[t * k + j]] = wj * ((real)elem(g, g_dt, t * k + j) - s);
+    }
+  }
+  for (int64_t i = 0; i < (int64_t)emb * E; ++i) dwr[i] = 0;
+  if (dbias)
+    for (int32_t e = 0; e < E; ++e) dbias[e] = 0;
+  for (int64_t t = 0; t < T; ++t)
+    for (int32_t e = 0; e < E; ++e) {
+      real d = dlogits[t * E + e];
+      if (d == 0) continue;
+      if (dbias) dbias[e] += d;
+      for (int32_t i = 0; i < emb; ++i) dwr[(int64_t)i * E + e] += (real)elem(x, x_dt, t * emb + i) * d;
+    }
+  if (dx)
+    for (int64_t t = 0; t < T; ++t)
+      for (int32_t i = 0; i < emb; ++i) {
+        real acc = 0;
+        for (int32_t e = 0; e < E; ++e) acc += dlogits[t * E + e] * (real)wr[(int64_t)i * E + e];
+        dx[t * emb + i] = acc;
+      }
+  return ORC_OK;
+}
+
 int orc_combine_bwd(int64_t T, int32_t emb, int32_t k, const void* dy, int dy_dt, const void* ys, int ys_dt,
                     const int32_t* slot_row, const float* w, real* dys, real* dw) {
   if (T < 0 || emb <= 0 || k <= 0 || !dy || !slot_row || !w || !dys || !valid_dt(dy_dt)) return ORC_EINVAL;

@@ -447,3 +447,108 @@ def test_backward_stage_composition_equals_per_token_backward():
         np.testing.assert_allclose(oracle.grouped_wgrad(a, do, go, e, real="f64"), ref[e][1], rtol=1e-9, atol=1e-12)
         np.testing.assert_allclose(oracle.grouped_wgrad(_val(xs), dh, go, e, real="f64"), ref[e][0], rtol=1e-9,
                                    atol=1e-12)
+
+
+# ---------------------------------------------------------------- router backward
+
+def _router_loss(x, wr, bias, idx, g):
+    """sum_t sum_j g[t,j] w[t,j] with w = softmax over each token's picked logits, picks fixed; numpy fp64,
+    written independently of the oracle."""
+    logits = x @ wr + bias
+    picked = np.take_along_axis(logits, idx, axis=1)
+    w = scipy.special.softmax(picked, axis=1)
+    return float((g * w).sum()), w
+
+
+def _router_case(T, emb, E, k, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, emb))
+    wr = rng.standard_normal((emb, E)) * 0.3
+    bias = rng.standard_normal(E) * 0.1
+    logits = x @ wr + bias
+    idx = np.argsort(-logits, axis=1, kind="stable")[:, :k].astype(np.int32)
+    g = rng.standard_normal((T, k))
+    return x, wr, bias, idx, g
+
+
+@pytest.mark.parametrize("T,emb,E,k,seed", [(6, 16, 8, 3, 1), (4, 8, 16, 5, 2), (3, 12, 4, 4, 3)])
+def test_router_backward_matches_central_finite_differences(T, emb, E, k, seed):
+    x, wr, bias, idx, g = _router_case(T, emb, E, k, seed)
+    _, w = _router_loss(x, wr, bias, idx, g)
+    dl, dwr, db, dx = oracle.router_bwd(x, wr.astype(np.float32), idx, w.astype(np.float32), g)
+    rng = np.random.default_rng(seed + 100)
+    h = 1e-5
+
+    def fd(fn, arr, pos):
+        a1, a2 = arr.copy(), arr.copy()
+        a1[pos] += h
+        a2[pos] -= h
+        return (fn(a1) - fn(a2)) / (2 * h)
+
+    wr32 = wr.astype(np.float32).astype(np.float64)  # the oracle reads Wr as fp32
+    for _ in range(12):
+        i, e = rng.integers(emb), rng.integers(E)
+        num = fd(lambda a: _router_loss(x, a, bias, idx, g)[0], wr32, (i, e))
+        assert abs(num - dwr[i, e]) <= 1e-6 + 1e-5 * abs(num), ("dWr", i, e, num, dwr[i, e])
+        e = rng.integers(E)
+        num = fd(lambda a: _router_loss(x, wr32, a, idx, g)[0], bias, (e,))
+        assert abs(num - db[e]) <= 1e-6 + 1e-5 * abs(num), ("dbias", e, num, db[e])
+        t, i = rng.integers(T), rng.integers(emb)
+        num = fd(lambda a: _router_loss(a, wr32, bias, idx, g)[0], x, (t, i))
+        assert abs(num - dx[t, i]) <= 1e-6 + 1e-5 * abs(num), ("dx", t, i, num, dx[t, i])
+    # unpicked experts get no logit gradient; each token's logit gradient sums to zero
+    mask = np.zeros((T, E), bool)
+    np.put_along_axis(mask, idx, True, axis=1)
+    assert (dl[~mask] == 0).all()
+    assert np.abs(dl.sum(axis=1)).max() <= 1e-6 * np.abs(dl).sum(axis=1).max()
+
+
+def test_router_backward_closed_forms():
+    # k = 1: the single weight is 1 whatever the logit -> no router gradient
+    x, wr, bias, idx, g = _router_case(5, 8, 6, 1, 7)
+    dl, dwr, db, dx = oracle.router_bwd(x, wr.astype(np.float32), idx, np.ones((5, 1), np.float32), g)
+    assert not dl.any() and not dwr.any() and not db.any() and not dx.any()
+    # a gradient equal across a token's picks moves nothing (the weights sum to 1)
+    x, wr, bias, idx, g = _router_case(5, 8, 6, 3, 8)
+    _, w = _router_loss(x, wr, bias, idx, g)
+    g = np.repeat(np.arange(1.0, 6.0)[:, None], 3, axis=1)
+    w32 = w.astype(np.float32)
+    dl, _, _, _ = oracle.router_bwd(x, wr.astype(np.float32), idx, w32, g)
+    assert np.abs(dl).max() <= 1e-6 * g.max()  # only the fp32 rounding of sum(w) = 1 remains
+    # dWr is the exact matrix product x^T dl, and dx is dl Wr^T
+    x, wr, bias, idx, g = _router_case(7, 5, 4, 2, 9)
+    _, w = _router_loss(x, wr, bias, idx, g)
+    dl, dwr, db, dx = oracle.router_bwd(x, wr.astype(np.float32), idx, w.astype(np.float32), g)
+    np.testing.assert_allclose(dwr, x.T @ dl, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(db, dl.sum(axis=0), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dx, dl @ wr.astype(np.float32).astype(np.float64).T, rtol=1e-12, atol=1e-14)
+
+
+def test_layer_router_gradient_matches_finite_differences_of_the_layer_output():
+    """y = sum_j w_j(Wr) o_j with the expert outputs o from the oracle forward; L = <y, dy>. The weight gradient
+    reaching the router is the combine backward's dtopk_w, and the router backward turns it into dWr."""
+    T, emb, mlp, E, k = 5, 16, 32, 6, 3
+    x_b, wr, wi, wo = _case(T, emb, mlp, E, k, 21)[:4]
+    x = _val(x_b)
+    rng = np.random.default_rng(22)
+    bias = np.zeros(E)
+    logits = x @ wr.astype(np.float64)
+    idx = np.argsort(-logits, axis=1, kind="stable")[:, :k].astype(np.int32)
+    _, w = _router_loss(x, wr.astype(np.float64), bias, idx, np.zeros((T, k)))
+    y, _, _, o = oracle.ffn_fwd_tokens(x_b, idx, w.astype(np.float32), wi, wo, real="f64", want_intermediates=True)
+    dy = rng.standard_normal((T, emb))
+    g = np.einsum("tjn,tn->tj", o, dy)  # dL/dw_j = <o_j, dy>
+    _, dwr, _, _ = oracle.router_bwd(x_b, wr, idx, w.astype(np.float32), g)
+
+    def loss(wr_):
+        _, w_ = _router_loss(x, wr_, bias, idx, np.zeros((T, k)))
+        return float(np.einsum("tj,tjn,tn->", w_, o, dy))
+
+    wr64 = wr.astype(np.float64)
+    h = 1e-5
+    for i, e in [(0, 0), (3, 2), (15, 5), (7, 1)]:
+        a1, a2 = wr64.copy(), wr64.copy()
+        a1[i, e] += h
+        a2[i, e] -= h
+        num = (loss(a1) - loss(a2)) / (2 * h)
+        assert abs(num - dwr[i, e]) <= 1e-6 + 1e-5 * abs(num), (i, e, num, dwr[i, e])
