@@ -89,6 +89,9 @@ int moe_query_support(const moe_shape_t* shape);
  */
 size_t moe_permute_workspace_bytes(const moe_shape_t* shape);
 size_t moe_workspace_bytes(const moe_shape_t* shape, int with_backward);
+/* moe_route_bwd_workspace_bytes: scratch of moe_route_bwd (per-slot logit
+ * gradients and the transposed router weight). */
+size_t moe_route_bwd_workspace_bytes(const moe_shape_t* shape);
 
 /*
  * moe_route -- gate and top-k routing ("[DRAFT][JAX] Optimize MoE block",
@@ -215,6 +218,32 @@ typedef struct {
   moe_bf16_t* a;
   moe_bf16_t* o;
 } moe_saved_t;
+
+/*
+ * moe_route_bwd -- gradients of the router, the picks held fixed: the top-k
+ * selection has no gradient, so they flow through the top-k weights only,
+ * which are the softmax over each token's k picked logits. The incoming
+ * gradient dtopk_w is the combine backward's reduction ("MoE: fused
+ * TensorCore Pallas permute/combine kernels ...", Commits table, commit 1).
+ * With g = dtopk_w[t] and the forward's weights w:
+ *   dlogits[t, e_j] = w_j (g_j - sum_i w_i g_i)   (0 for experts not picked)
+ *   dwr[i, e]  = sum_t x[t, i] dlogits[t, e]      (fp32, [emb, E], overwritten)
+ *   dbias[e]   = sum_t dlogits[t, e]              (fp32 [E], or NULL)
+ *   dx[t, :]  += sum_j dlogits[t, e_j] wr[:, e_j] (bf16 [T, emb] in/out, or NULL)
+ *  x [T, emb] bf16 and wr [emb, E] fp32 are the forward's router inputs;
+ *  topk_idx, topk_w [T, k] its routing; sorted_slot [S] and group_offsets
+ *  [E+1] its permute index (moe_permute); dtopk_w [T, k] fp32 (moe_combine_bwd
+ *  or moe_ffn_bwd).
+ *  Order: dwr and dbias sum each expert's rows in expert-sorted (token)
+ *  order with fp32 fused multiply-adds; the sum of s in dlogits runs over the
+ *  picks in order; dx adds the k terms to the incoming value in fp32, in
+ *  pick order, then rounds once. Results do not depend on scheduling.
+ *  ws: at least moe_route_bwd_workspace_bytes(shape) bytes.
+ */
+int moe_route_bwd(const moe_shape_t* shape, const moe_bf16_t* x, const float* wr, const int32_t* topk_idx,
+                  const float* topk_w, const float* dtopk_w, const int32_t* sorted_slot,
+                  const int32_t* group_offsets, float* dwr, float* dbias, moe_bf16_t* dx, void* ws, size_t ws_bytes,
+                  moe_stream_t stream);
 
 /*
  * moe_ffn_fwd -- the whole MoE FFN forward: route, permute, grouped GEMM on

@@ -210,6 +210,33 @@ def _saved_struct(saved: dict) -> MoeSaved:
     return MoeSaved(*[saved[n].data_ptr() for n in _SAVED_NAMES])
 
 
+def route_bwd(x: torch.Tensor, wr: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor,
+              dtopk_w: torch.Tensor, sorted_slot: torch.Tensor, group_offsets: torch.Tensor,
+              dx: torch.Tensor | None = None, want_dbias: bool = True) -> dict:
+    """Router gradients with the picks held fixed (see moe_route_bwd): dict(dwr [emb, E] fp32, dbias [E] fp32
+    or None). dx (bf16 [T, emb], optional) is updated in place: dx += dlogits . wr^T."""
+    _need(x, "x", torch.bfloat16)
+    dev = x.device
+    for t, n, d in ((wr, "wr", torch.float32), (topk_idx, "topk_idx", torch.int32), (topk_w, "topk_w", torch.float32),
+                    (dtopk_w, "dtopk_w", torch.float32), (sorted_slot, "sorted_slot", torch.int32),
+                    (group_offsets, "group_offsets", torch.int32), (dx, "dx", torch.bfloat16)):
+        _need(t, n, d, dev)
+    T, emb = x.shape
+    E = wr.shape[1]
+    k = topk_idx.shape[1]
+    s = _lib.shape(T, emb, 64, E, k)
+    ws_n = int(_lib.lib().moe_route_bwd_workspace_bytes(C.byref(s)))
+    if ws_n == 0:
+        _lib.check(_lib.lib().moe_query_support(C.byref(s)), "route_bwd")
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    dwr = torch.empty((emb, E), dtype=torch.float32, device=dev)
+    dbias = torch.empty(E, dtype=torch.float32, device=dev) if want_dbias else None
+    _lib.check(_lib.lib().moe_route_bwd(C.byref(s), _ptr(x), _ptr(wr), _ptr(topk_idx), _ptr(topk_w), _ptr(dtopk_w),
+                                        _ptr(sorted_slot), _ptr(group_offsets), _ptr(dwr), _ptr(dbias), _ptr(dx),
+                                        _ptr(ws), ws.numel(), _stream(dev)), "moe_route_bwd")
+    return dict(dwr=dwr, dbias=dbias)
+
+
 def ffn_fwd(x: torch.Tensor, wi: torch.Tensor, wo: torch.Tensor, k: int, wr: torch.Tensor | None = None,
             bias: torch.Tensor | None = None, logits: torch.Tensor | None = None, save: bool = False,
             workspace: torch.Tensor | None = None, out: torch.Tensor | None = None):

@@ -46,6 +46,7 @@ SIGNATURES = {
     "moe_query_support": ([_SHP], C.c_int),
     "moe_permute_workspace_bytes": ([_SHP], _sz),
     "moe_workspace_bytes": ([_SHP, C.c_int], _sz),
+    "moe_route_bwd_workspace_bytes": ([_SHP], _sz),
     "moe_route": ([_SHP, _p, _p, _p, _p, _p, _p, _p], C.c_int),
     "moe_permute": ([_SHP, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p], C.c_int),
     "moe_grouped_gemm": ([C.c_int, C.c_int, _p, _p, _p, _p, _p, _i32, _i64, _i32, _i32, C.POINTER(MoeGemmRows), _p,
@@ -55,6 +56,7 @@ SIGNATURES = {
     "moe_combine_bwd": ([_SHP, _p, _p, _p, _p, _p, _p, _p], C.c_int),
     "moe_ffn_fwd": ([_SHP, _p, _p, _p, _p, _p, _p, _p, C.POINTER(MoeSaved), _p, _sz, _p], C.c_int),
     "moe_ffn_bwd": ([_SHP, _p, C.POINTER(MoeSaved), _p, _p, _p, _p, _p, _p, _p, _sz, _p], C.c_int),
+    "moe_route_bwd": ([_SHP, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p], C.c_int),
 }
 
 

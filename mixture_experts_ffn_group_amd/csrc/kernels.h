@@ -38,4 +38,10 @@ hipError_t launch_combine(int64_t T, int emb, int k, const uint16_t* ys, const i
 hipError_t launch_combine_bwd(int64_t T, int emb, int k, const uint16_t* dy, const uint16_t* ys,
                               const int32_t* slot_row, const float* w, uint16_t* dys, float* dw, hipStream_t stream);
 
+// Router backward, picks held fixed. dl: [T*k] fp32 scratch; wrt: [E, emb] fp32 scratch (used when dx != NULL).
+hipError_t launch_route_bwd(int64_t T, int emb, int E, int k, const uint16_t* x, const float* wr,
+                            const int32_t* topk_idx, const float* topk_w, const float* dtopk_w,
+                            const int32_t* sorted_slot, const int32_t* group_offsets, float* dwr, float* dbias,
+                            uint16_t* dx, float* dl, float* wrt, hipStream_t stream);
+
 }  // namespace moe

@@ -166,6 +166,16 @@ size_t moe_workspace_bytes(const moe_shape_t* shape, int with_backward) {
   return with_backward ? bwd_ws(shape) : fwd_ws(shape);
 }
 
+// per-slot logit gradients, then Wr transposed
+size_t route_bwd_ws(const moe_shape_t* s) {
+  return round_up(4 * (size_t)s->T * s->k) + round_up(4 * (size_t)s->E * s->emb);
+}
+
+size_t moe_route_bwd_workspace_bytes(const moe_shape_t* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  return route_bwd_ws(shape);
+}
+
 int moe_route(const moe_shape_t* s, const moe_bf16_t* x, const float* wr, const float* bias, const float* logits_in,
               int32_t* topk_idx, float* topk_w, moe_stream_t stream) {
   g_detail[0] = 0;
@@ -292,6 +302,35 @@ int moe_combine_bwd(const moe_shape_t* s, const moe_bf16_t* dy, const moe_bf16_t
   return hip_status(moe::launch_combine_bwd(s->T, s->emb, s->k, dy, ys, slot_row, topk_w, dys, dtopk_w,
                                             (hipStream_t)stream),
                     "moe_combine_bwd");
+}
+
+int moe_route_bwd(const moe_shape_t* s, const moe_bf16_t* x, const float* wr, const int32_t* topk_idx,
+                  const float* topk_w, const float* dtopk_w, const int32_t* sorted_slot,
+                  const int32_t* group_offsets, float* dwr, float* dbias, moe_bf16_t* dx, void* ws, size_t ws_bytes,
+                  moe_stream_t stream) {
+  g_detail[0] = 0;
+  if (int rc = check_shape(s)) return rc;
+  NEED(wr);
+  NEED(group_offsets);
+  NEED(dwr);
+  MAYBE(dbias);
+  if (s->T > 0) {  // with no tokens, per-token buffers may be empty (NULL)
+    NEED(x);
+    NEED(topk_idx);
+    NEED(topk_w);
+    NEED(dtopk_w);
+    NEED(sorted_slot);
+    MAYBE(dx);
+  }
+  NEED(ws);
+  if (ws_bytes < route_bwd_ws(s)) return fail(MOE_ERR_WORKSPACE, "need %zu workspace bytes", route_bwd_ws(s));
+  Carver c{static_cast<char*>(ws)};
+  float* dl = c.take<float>(s->T * s->k);
+  float* wrt = c.take<float>((int64_t)s->E * s->emb);
+  return hip_status(moe::launch_route_bwd(s->T, s->emb, s->E, s->k, x, wr, topk_idx, topk_w, dtopk_w, sorted_slot,
+                                          group_offsets, dwr, dbias, s->T > 0 ? dx : nullptr, dl, wrt,
+                                          (hipStream_t)stream),
+                    "moe_route_bwd");
 }
 
 int moe_ffn_fwd(const moe_shape_t* s, const moe_bf16_t* x, const float* wr, const float* bias, const float* logits_in,

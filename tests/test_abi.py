@@ -118,6 +118,14 @@ def test_validation_precedes_any_launch(lib):
     assert lib.moe_grouped_gemm_wgrad(fake, fake, nul, 4, 128, 64, 64, fake, nul) == _lib.MOE_ERR_NULL
     assert lib.moe_combine(C.byref(s), fake, fake, odd, fake, nul) == _lib.MOE_ERR_ALIGN
     assert lib.moe_combine_bwd(C.byref(s), fake, nul, fake, nul, fake, nul, nul) == _lib.MOE_ERR_NULL
+    # router backward: dwr required, dtopk_w required with tokens, workspace size checked
+    assert lib.moe_route_bwd(C.byref(s), fake, fake, fake, fake, fake, fake, fake, nul, nul, nul, fake, 1 << 20,
+                             nul) == _lib.MOE_ERR_NULL
+    assert lib.moe_route_bwd(C.byref(s), fake, fake, fake, fake, nul, fake, fake, fake, nul, nul, fake, 1 << 20,
+                             nul) == _lib.MOE_ERR_NULL
+    assert lib.moe_route_bwd(C.byref(s), fake, fake, fake, fake, fake, fake, fake, fake, nul, nul, fake, 16,
+                             nul) == _lib.MOE_ERR_WORKSPACE
+    assert lib.moe_route_bwd_workspace_bytes(C.byref(s)) >= 64 * 2 * 4 + 8 * 128 * 4
     # layer calls: workspace too small, missing saved set
     assert lib.moe_ffn_fwd(C.byref(s), fake, fake, nul, nul, fake, fake, fake, None, fake, 16, nul) == \
         _lib.MOE_ERR_WORKSPACE

@@ -327,3 +327,89 @@ def test_wgrad_matches_oracle_and_zeros_empty_groups(M, P, Q, E, empty):
             assert (Cn[e] == 0).all()
         else:
             assert_close(Cn[e], ref, f"dW[{e}]")
+
+
+# ---------------------------------------------------------------- router backward
+
+def _route_bwd_case(T, emb, E, k, seed, empty=()):
+    rng = np.random.default_rng(seed)
+    x = torch.from_numpy(rng.standard_normal((T, emb)).astype(np.float32)).to(torch.bfloat16)
+    wr = torch.from_numpy((rng.standard_normal((emb, E)) * 0.05).astype(np.float32))
+    bias = torch.zeros(E)
+    bias[list(empty)] = -float("inf")
+    idx, w = moe.route(k, x=x.to(DEV), wr=wr.to(DEV), bias=bias.to(DEV))
+    perm = moe.permute(x.to(DEV), idx, E, rows=False)
+    g = torch.from_numpy(rng.standard_normal((T, k)).astype(np.float32)).to(DEV)
+    dx0 = torch.from_numpy(rng.standard_normal((T, emb)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    return x, wr, idx, w, g, perm, dx0
+
+
+def _check_route_bwd(x, wr, idx, w, g, perm, dx0, out, dx, want_dx=True):
+    T, emb = x.shape
+    E = wr.shape[1]
+    k = idx.shape[1]
+    xb = bits(x)
+    dl, dwr, db, dxr = oracle.router_bwd(xb, wr.numpy(), idx.cpu().numpy(), w.cpu().numpy(),
+                                         g.cpu().numpy().astype(np.float64), want_dx=want_dx)
+    n_max = int(np.diff(perm["group_offsets"].cpu().numpy()).max(initial=0))
+    eps = 2.0 ** -24
+    xa = np.abs(bf16_values(xb))
+    # Error of the fp32 logit gradient dl_j = w_j (g_j - s), s = sum_i w_i g_i: the fp32 chain for s errs by up to
+    # k eps sum|w g|, which the subtraction turns into an absolute error of dl (g_j ~ s cancels), plus three
+    # roundings relative to dl itself.
+    wn = w.cpu().numpy().astype(np.float64)
+    gn = g.cpu().numpy().astype(np.float64)
+    s_mag = (np.abs(wn) * np.abs(gn)).sum(axis=1, keepdims=True)
+    ddl_slot = wn * (k + 2) * eps * s_mag + 3 * eps * np.abs(np.take_along_axis(dl, idx.cpu().numpy(), axis=1))
+    ddl = np.zeros_like(dl)
+    np.put_along_axis(ddl, idx.cpu().numpy(), ddl_slot, axis=1)
+    # dWr, dbias: fp32 chain over a group's rows, plus the propagated error of dl
+    bound = (n_max + 8) * eps * (xa.T @ np.abs(dl)) + xa.T @ ddl + 1e-30
+    got = out["dwr"].cpu().numpy().astype(np.float64)
+    assert (np.abs(got - dwr) <= bound).all(), np.abs(got - dwr).max()
+    got_b = out["dbias"].cpu().numpy().astype(np.float64)
+    assert (np.abs(got_b - db) <= (n_max + 8) * eps * np.abs(dl).sum(axis=0) + ddl.sum(axis=0) + 1e-30).all()
+    if want_dx:
+        d0 = to_np(dx0)
+        exact = d0 + dxr
+        wra = np.abs(wr.numpy().astype(np.float64))
+        mag = np.abs(d0) + np.abs(dl) @ wra.T
+        assert np.all(np.abs(to_np(dx) - exact) <= _combine_bound(exact, mag, k + 1) + ddl @ wra.T + 1e-30)
+
+
+@pytest.mark.parametrize("T,emb,E,k,seed,empty", [(300, 256, 16, 4, 1, ()), (129, 64, 256, 8, 2, (3, 77)),
+                                                  (1000, 1024, 128, 8, 3, (0,)), (77, 7168, 200, 6, 4, ()),
+                                                  (50, 128, 8, 8, 5, ())])
+def test_route_bwd_matches_oracle(T, emb, E, k, seed, empty):
+    x, wr, idx, w, g, perm, dx0 = _route_bwd_case(T, emb, E, k, seed, empty)
+    dx = dx0.clone()
+    out = moe.route_bwd(x.to(DEV), wr.to(DEV), idx, w, g, perm["sorted_slot"], perm["group_offsets"], dx=dx)
+    _check_route_bwd(x, wr, idx, w, g, perm, dx0, out, dx)
+    for e in empty:  # an expert no token picked gets exact zeros
+        assert (out["dwr"][:, e] == 0).all() and out["dbias"][e] == 0
+
+
+def test_route_bwd_single_pick_and_no_tokens():
+    x, wr, idx, w, g, perm, dx0 = _route_bwd_case(200, 128, 16, 1, 6)
+    dx = dx0.clone()
+    out = moe.route_bwd(x.to(DEV), wr.to(DEV), idx, w, g, perm["sorted_slot"], perm["group_offsets"], dx=dx)
+    assert (out["dwr"] == 0).all() and (out["dbias"] == 0).all()  # one pick: its weight is 1 whatever the logit
+    assert torch.equal(dx.view(torch.int16), dx0.view(torch.int16))
+    e0 = torch.empty((0, 128), dtype=torch.bfloat16, device=DEV)
+    i0 = torch.empty((0, 4), dtype=torch.int32, device=DEV)
+    f0 = torch.empty((0, 4), dtype=torch.float32, device=DEV)
+    s0 = torch.empty(0, dtype=torch.int32, device=DEV)
+    go = torch.zeros(17, dtype=torch.int32, device=DEV)
+    out = moe.route_bwd(e0, wr.to(DEV), i0, f0, f0, s0, go)
+    assert (out["dwr"] == 0).all() and (out["dbias"] == 0).all()
+
+
+def test_route_bwd_full_size_gemma4_class():
+    inp = workloads.make_inputs("gemma4_class", with_weights=False)
+    wl = inp["workload"]
+    x, wr = inp["x"], inp["wr"]
+    idx, w = moe.route(wl.k, x=x.to(DEV), wr=wr.to(DEV))
+    perm = moe.permute(x.to(DEV), idx, wl.E, rows=False)
+    g = torch.from_numpy(np.random.default_rng(5).standard_normal((wl.T, wl.k)).astype(np.float32)).to(DEV)
+    out = moe.route_bwd(x.to(DEV), wr.to(DEV), idx, w, g, perm["sorted_slot"], perm["group_offsets"])
+    _check_route_bwd(x, wr, idx, w, g, perm, None, out, None, want_dx=False)
