@@ -16,7 +16,8 @@ index and GEMM 1 reads the token rows of x in place through it. With
 --backward (DeepSeek-V3-shaped workload) the forward materialises the sorted
 rows and the fp32 gate/up values for the backward, and the step also runs
 the layer backward (combine-bwd, NT GEMM + SwiGLU-bwd, NT GEMM, permute-bwd,
-wgrad x2).
+wgrad x2) and, where the router is learned, the router backward (logit
+gradients from dtopk_w, dWr, and dx += dlogits . Wr^T onto the layer's dx).
 """
 from __future__ import annotations
 
@@ -90,6 +91,12 @@ def main():
         grads = dict(dx=torch.empty((T, emb), dtype=torch.bfloat16, device=dev),
                      dwi=torch.empty_like(wi), dwo=torch.empty_like(wo),
                      dtopk_w=torch.empty((T, k), dtype=torch.float32, device=dev))
+    router_bwd = bwd and wr is not None
+    if router_bwd:
+        rbws = torch.empty(max(16, int(_lib.lib().moe_route_bwd_workspace_bytes(
+            __import__("ctypes").byref(_lib.shape(T, emb, mlp, E, k))))), dtype=torch.uint8, device=dev)
+        grads["dwr"] = torch.empty((emb, E), dtype=torch.float32, device=dev)
+        grads["dbias"] = torch.empty(E, dtype=torch.float32, device=dev) if bias is not None else None
 
     import ctypes as C
     L = _lib.lib()
@@ -126,6 +133,12 @@ def main():
                                                             P(wi), P(wo), P(grads["dx"]), P(grads["dwi"]),
                                                             P(grads["dwo"]), P(grads["dtopk_w"]), P(bws), bws.numel(),
                                                             st)))
+        if router_bwd:
+            calls.append(("route_bwd", lambda: L.moe_route_bwd(C.byref(shp), P(x), P(wr), P(sv["topk_idx"]),
+                                                               P(sv["topk_w"]), P(grads["dtopk_w"]),
+                                                               P(sv["sorted_slot"]), P(sv["group_offsets"]),
+                                                               P(grads["dwr"]), P(grads["dbias"]), P(grads["dx"]),
+                                                               P(rbws), rbws.numel(), st)))
         return calls
 
     calls = stage_calls()
@@ -208,6 +221,12 @@ def main():
         stages["backward"] = dict(ms=stage_ms["backward"], bound="mfma",
                                   achieved=tf(12.0 * S * emb * mlp, stage_ms["backward"]), peak=PEAK_BF16_TFLOPS,
                                   unit="TFLOP/s")
+    if router_bwd:
+        # x read once, dx read and written, Wr read (fp32), dWr written, per-slot index/weight/gradient reads
+        rb_bytes = 3 * T * emb * 2 + 2 * emb * E * 4 + (4 + 4 + 4 + 4) * S
+        stages["route_bwd"] = dict(ms=stage_ms["route_bwd"], bound="hbm", achieved=gb(rb_bytes, stage_ms["route_bwd"]),
+                                   peak=PEAK_HBM_GBS, unit="GB/s", bytes=rb_bytes,
+                                   fp32_flop=4.0 * S * emb)
     for v in stages.values():
         v["frac"] = v["achieved"] / v["peak"]
     gemm_ms = stage_ms["gemm1_swiglu"] + stage_ms["gemm2"]
@@ -247,7 +266,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "emb": emb, "mlp": mlp, "E": E, "k": k,
-                   "pass": "forward+backward" if bwd else "forward", "parallelism": "none (1 GPU)"},
+                   "pass": "forward+backward" if bwd else "forward", "router_backward": router_bwd,
+                   "parallelism": "none (1 GPU)"},
         "layer_tflops": round(tf(fwd_flop * (3 if bwd else 1), ms_step), 2),
         "gemm_stage_tflops": round(tf(fwd_flop, gemm_ms), 2),
         "gemm_stage_frac": round(tf(fwd_flop, gemm_ms) / PEAK_BF16_TFLOPS, 4),

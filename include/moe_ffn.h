@@ -90,7 +90,8 @@ int moe_query_support(const moe_shape_t* shape);
 size_t moe_permute_workspace_bytes(const moe_shape_t* shape);
 size_t moe_workspace_bytes(const moe_shape_t* shape, int with_backward);
 /* moe_route_bwd_workspace_bytes: scratch of moe_route_bwd (per-slot logit
- * gradients and the transposed router weight). */
+ * gradients, the sorted rows' tokens and gradients, and [E, emb] copies of
+ * the router weight and its gradient). */
 size_t moe_route_bwd_workspace_bytes(const moe_shape_t* shape);
 
 /*

@@ -42,6 +42,7 @@ hipError_t launch_combine_bwd(int64_t T, int emb, int k, const uint16_t* dy, con
 hipError_t launch_route_bwd(int64_t T, int emb, int E, int k, const uint16_t* x, const float* wr,
                             const int32_t* topk_idx, const float* topk_w, const float* dtopk_w,
                             const int32_t* sorted_slot, const int32_t* group_offsets, float* dwr, float* dbias,
-                            uint16_t* dx, float* dl, float* wrt, hipStream_t stream);
+                            uint16_t* dx, float* dl, float* dls, int32_t* tok, float* wrt, float* dwrt,
+                            hipStream_t stream);
 
 }  // namespace moe

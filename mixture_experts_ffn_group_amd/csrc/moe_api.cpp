@@ -168,7 +168,7 @@ size_t moe_workspace_bytes(const moe_shape_t* shape, int with_backward) {
 
 // per-slot logit gradients, then Wr transposed
 size_t route_bwd_ws(const moe_shape_t* s) {
-  return round_up(4 * (size_t)s->T * s->k) + round_up(4 * (size_t)s->E * s->emb);
+  return 3 * round_up(4 * (size_t)s->T * s->k) + 2 * round_up(4 * (size_t)s->E * s->emb);
 }
 
 size_t moe_route_bwd_workspace_bytes(const moe_shape_t* shape) {
@@ -326,10 +326,13 @@ int moe_route_bwd(const moe_shape_t* s, const moe_bf16_t* x, const float* wr, co
   if (ws_bytes < route_bwd_ws(s)) return fail(MOE_ERR_WORKSPACE, "need %zu workspace bytes", route_bwd_ws(s));
   Carver c{static_cast<char*>(ws)};
   float* dl = c.take<float>(s->T * s->k);
+  float* dls = c.take<float>(s->T * s->k);
+  int32_t* tok = c.take<int32_t>(s->T * s->k);
   float* wrt = c.take<float>((int64_t)s->E * s->emb);
+  float* dwrt = c.take<float>((int64_t)s->E * s->emb);
   return hip_status(moe::launch_route_bwd(s->T, s->emb, s->E, s->k, x, wr, topk_idx, topk_w, dtopk_w, sorted_slot,
-                                          group_offsets, dwr, dbias, s->T > 0 ? dx : nullptr, dl, wrt,
-                                          (hipStream_t)stream),
+                                          group_offsets, dwr, dbias, s->T > 0 ? dx : nullptr, dl, dls, tok, wrt,
+                                          dwrt, (hipStream_t)stream),
                     "moe_route_bwd");
 }
 

@@ -125,7 +125,7 @@ def test_validation_precedes_any_launch(lib):
                              nul) == _lib.MOE_ERR_NULL
     assert lib.moe_route_bwd(C.byref(s), fake, fake, fake, fake, fake, fake, fake, fake, nul, nul, fake, 16,
                              nul) == _lib.MOE_ERR_WORKSPACE
-    assert lib.moe_route_bwd_workspace_bytes(C.byref(s)) >= 64 * 2 * 4 + 8 * 128 * 4
+    assert lib.moe_route_bwd_workspace_bytes(C.byref(s)) >= 3 * 64 * 2 * 4 + 2 * 8 * 128 * 4
     # layer calls: workspace too small, missing saved set
     assert lib.moe_ffn_fwd(C.byref(s), fake, fake, nul, nul, fake, fake, fake, None, fake, 16, nul) == \
         _lib.MOE_ERR_WORKSPACE
