@@ -238,8 +238,17 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
       else hi = mid;
     }
     const int e = lo;
+    // Tile order inside an expert: with 4 or more row blocks the row block
+    // varies fastest, so the workgroups of an XCD share one weight panel while
+    // they sweep the expert's rows (measured: wo GEMM 1.01 -> 0.97 ms at 128
+    // experts of ~2048 rows, K = 768). With 1-3 row blocks the column tile
+    // varies fastest, so all column tiles read the same row block at once (the
+    // other order cost 12 % at 256 experts of ~256 rows, K = 7168).
     const int local = tile - s_pref[e];
-    const int mt = local / ntn, nt = local % ntn;
+    const int nmt = (s_pref[e + 1] - s_pref[e]) / ntn;
+    const bool rows_fast = nmt >= 4;
+    const int mt = rows_fast ? local % nmt : local / ntn;
+    const int nt = rows_fast ? local / nmt : local % ntn;
     m0 = __builtin_amdgcn_readfirstlane(s_lo[e] + mt * BM);
     m_end = __builtin_amdgcn_readfirstlane(max(s_lo[e + 1], s_lo[e]));
     n0 = __builtin_amdgcn_readfirstlane(nt * tile_n);

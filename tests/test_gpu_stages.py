@@ -276,6 +276,29 @@ def test_grouped_gemm_nt_swiglu_bwd(M, K, N, E, empty):
     assert_close(to_np(dh), ref, "dh")
 
 
+# Groups whose last 256-row tile ends at every 32-row block boundary of either half of the tile, and just past
+# it (a tile multiplies only its blocks that hold rows of the group), plus an empty group.
+PARTIAL_SIZES = [1, 32, 33, 64, 65, 128, 129, 160, 224, 255, 256, 257, 300, 543, 0]
+
+
+@pytest.mark.parametrize("op,epi", [("nn", "none"), ("nn", "swiglu"), ("nt", "none"), ("nt", "swiglu_bwd")])
+def test_grouped_gemm_partial_tiles_every_block_count(op, epi):
+    K, N = 192, 320
+    sizes = np.array(PARTIAL_SIZES, np.int64)
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M, E = int(off[-1]), len(sizes)
+    rng = np.random.default_rng(31)
+    A = _bf16_dev(rng.standard_normal((M, K)))
+    Nb = 2 * N if epi == "swiglu" else N
+    B = _bf16_dev(rng.standard_normal((E, K, Nb) if op == "nn" else (E, Nb, K)) * (0.5 / np.sqrt(K)))
+    h = (rng.standard_normal((M, 2 * N)) * 0.5).astype(np.float32)
+    got = moe.grouped_gemm(A, B, torch.from_numpy(off).to(DEV), op=op, epilogue=epi,
+                           aux_in=torch.from_numpy(h).to(DEV) if epi == "swiglu_bwd" else None)
+    ref = oracle.grouped_gemm(0 if op == "nn" else 1, {"none": 0, "swiglu": 1, "swiglu_bwd": 2}[epi], bits(A),
+                              bits(B), off, aux=h if epi == "swiglu_bwd" else None)
+    assert_close(to_np(got), ref, f"{op}/{epi}")
+
+
 @pytest.mark.parametrize("op,epi", [("nn", "none"), ("nn", "swiglu"), ("nt", "none"), ("nt", "swiglu_bwd")])
 def test_grouped_gemm_row_gather_and_row_scale(op, epi):
     """Rows read in place from A [T, K] through slots t*k + j, each output row scaled by w[slot] in fp32:
