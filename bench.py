@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-PEAK_FP32_FMA_TFLOPS = 78.6    # non-packed fp32 FMA: 256 CU x 64 lanes x 2 flop x 2.4 GHz
+PEAK_FP32_MFMA_TFLOPS = 157.3  # dense fp32 matrix cores (the router's fma chains run on them)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 GEMM_SRC = os.path.join(ROOT, "mixture_experts_ffn_group_amd", "csrc", "gemm.hip")
 
@@ -201,9 +201,9 @@ def main():
         return b / (ms * 1e-3) / 1e9
 
     stages = {
-        "route": dict(ms=stage_ms["route"], bound="alu" if route_flop else "hbm",
+        "route": dict(ms=stage_ms["route"], bound="mfma" if route_flop else "hbm",
                       achieved=tf(route_flop, stage_ms["route"]) if route_flop else gb(route_bytes, stage_ms["route"]),
-                      peak=PEAK_FP32_FMA_TFLOPS if route_flop else PEAK_HBM_GBS,
+                      peak=PEAK_FP32_MFMA_TFLOPS if route_flop else PEAK_HBM_GBS,
                       unit="TFLOP/s" if route_flop else "GB/s"),
         "permute": dict(ms=stage_ms["permute"], bound="hbm", achieved=gb(perm_bytes, stage_ms["permute"]),
                         peak=PEAK_HBM_GBS, unit="GB/s", bytes=perm_bytes,

@@ -510,7 +510,7 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
 // MFMA reads transposed (ds_read_b64_tr_b16), like the NN weight of the
 // forward GEMM. Same workgroup shape, LDS ring and staged epilogue as
 // gemm_kernel; tiles are (expert, 256-row block of P, 256-column block of Q),
-// numbered expert-major, and the k-loop runs over the expert's own rows.
+// dealt to the XCDs by expert, and the k-loop runs over the expert's own rows.
 // Rows past the group end must add nothing: each k-slice is copied with
 // buffer loads whose range is exactly the slice's valid rows, and the
 // hardware writes zeros for out-of-range lanes. An empty group writes exact
@@ -535,8 +535,12 @@ __device__ __forceinline__ void b2lds16(i32x4_t rsrc, uint32_t voff, uint32_t ld
 __global__ __launch_bounds__(GTHR, 1) void wgrad_kernel(WgradP p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kGemmLds];
   __shared__ __attribute__((aligned(16))) uint8_t s_stage[GTHR / 64][2048];
+  // group offsets, clamped to [0, M], read once: a tile's rows are then known
+  // without a global load between two tiles
+  __shared__ int s_off[kMaxExperts + 1];
+  for (int i = threadIdx.x; i <= p.E; i += GTHR) s_off[i] = min(max(p.off[i], 0), p.M);
+  __syncthreads();
   const int tp = (p.P + 255) / 256, tq = (p.Q + 255) / 256;
-  const int64_t total = (int64_t)p.E * tp * tq;
   uint8_t* const As0 = smem;
   uint8_t* const Ds0 = smem + NST * kOpStage;
   const int tid = opaque((int)threadIdx.x), lane = tid & 63, wave = tid >> 6;
@@ -551,14 +555,25 @@ __global__ __launch_bounds__(GTHR, 1) void wgrad_kernel(WgradP p) {
   // bytes of the slice (or zeros) and only feed outputs that are never stored.
   int e = 0, p0 = 0, q0 = 0, lo = 0, n = 0, nk = 0;
   uint32_t a_off[2], d_off[2];
+  // Tiles are dealt by expert: XCD x (workgroups w with w % 8 == x) takes
+  // experts x, x + 8, ..., each expert's tiles in turn over its G / 8
+  // workgroups. Every expert has the same number of tiles whatever its row
+  // count, so the XCDs stay balanced when E is a multiple of 8, and an
+  // expert's operand rows are read into one XCD's L2 rather than into all
+  // eight. Inside an expert the dimension with fewer 256-blocks varies
+  // fastest: its panels stay in L2 while the other dimension's stream past
+  // once each.
+  const int per_xcd = gridDim.x / kNumXcd;
+  const int my_xcd = blockIdx.x % kNumXcd, my_slot = blockIdx.x / kNumXcd;
   auto decode = [&](int64_t it) -> bool {
-    const int64_t tl = xcd_tile(it, blockIdx.x, gridDim.x);
-    if (tl >= total) return false;
-    e = (int)__builtin_amdgcn_readfirstlane((int)(tl / (tp * tq)));
-    const int loc = (int)(tl % (tp * tq));
-    p0 = __builtin_amdgcn_readfirstlane((loc / tq) * 256);
-    q0 = __builtin_amdgcn_readfirstlane((loc % tq) * 256);
-    const int l0 = min(max(p.off[e], 0), p.M), h0 = min(max(p.off[e + 1], 0), p.M);
+    const int64_t j = it * per_xcd + my_slot;
+    const int64_t ee = my_xcd + (int64_t)kNumXcd * (j / ((int64_t)tp * tq));
+    if (ee >= p.E) return false;
+    e = __builtin_amdgcn_readfirstlane((int)ee);
+    const int loc = (int)(j % ((int64_t)tp * tq));
+    p0 = __builtin_amdgcn_readfirstlane((tq <= tp ? loc / tq : loc % tp) * 256);
+    q0 = __builtin_amdgcn_readfirstlane((tq <= tp ? loc % tq : loc / tp) * 256);
+    const int l0 = s_off[e], h0 = s_off[e + 1];
     lo = __builtin_amdgcn_readfirstlane(l0);
     n = __builtin_amdgcn_readfirstlane(h0 > l0 ? h0 - l0 : 0);
     nk = (n + GBK - 1) / GBK;
@@ -672,7 +687,10 @@ __global__ __launch_bounds__(GTHR, 1) void wgrad_kernel(WgradP p) {
           const int rr = 8 * kk + (lane >> 3), c = lane & 7;
           const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + stg128(rr, c));
           const int pr = pr0 + 16 * h + rr;
-          if (pr < p.P && c < valid) st16(Ce + (int64_t)pr * p.Q + qw + c * 8, v);
+          // non-temporal: the output is several times the operands and is not read back here, so it
+          // streams past L2 instead of evicting the operand panels the next tiles read
+          if (pr < p.P && c < valid)
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(Ce + (int64_t)pr * p.Q + qw + c * 8));
         }
       }
     }

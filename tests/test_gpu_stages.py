@@ -334,8 +334,11 @@ def test_grouped_gemm_rows_past_last_group_untouched():
     assert_close(got[:450], oracle.grouped_gemm(0, 0, bits(A), bits(B), off)[:450], "C")
 
 
+# The last two cases have 16 experts of 32 tiles each, so every workgroup runs several tiles of the experts
+# its XCD is dealt, with groups of ~150 rows (5 k-slices) and of ~37 rows (2 k-slices).
 @pytest.mark.parametrize("M,P,Q,E,empty", [(700, 128, 512, 4, (2,)), (1000, 256, 200, 5, (0,)),
-                                           (90, 64, 64, 8, (1, 2, 3)), (3000, 768, 256, 3, ())])
+                                           (90, 64, 64, 8, (1, 2, 3)), (3000, 768, 256, 3, ()),
+                                           (2400, 2048, 1024, 16, (3,)), (600, 1024, 2048, 16, (5,))])
 def test_wgrad_matches_oracle_and_zeros_empty_groups(M, P, Q, E, empty):
     rng = np.random.default_rng(P + Q)
     off = _offsets(M, E, P + Q, empty)
