@@ -1,7 +1,7 @@
 """Benchmark of the MoE FFN layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gemma4_class]
-                    [--no-cpu-baseline] [--stage-json PATH]
+                    [--backward [--recompute-h]] [--no-cpu-baseline] [--stage-json PATH]
 
 One step = one pass of the whole forward hot path over one batch: route,
 permute, grouped GEMM 1 (prefused wi, SwiGLU epilogue), grouped GEMM 2 (wo),
@@ -18,6 +18,8 @@ rows and the fp32 gate/up values for the backward, and the step also runs
 the layer backward (combine-bwd, NT GEMM + SwiGLU-bwd, NT GEMM, permute-bwd,
 wgrad x2) and, where the router is learned, the router backward (logit
 gradients from dtopk_w, dWr, and dx += dlogits . Wr^T onto the layer's dx).
+With --recompute-h the forward keeps no fp32 gate/up values and the backward
+recomputes them with one more GEMM1 (the saved bytes are reported).
 """
 from __future__ import annotations
 
@@ -45,6 +47,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gemma4_class")
     ap.add_argument("--backward", action="store_true")
+    ap.add_argument("--recompute-h", action="store_true",
+                    help="with --backward: the forward keeps no h and the backward recomputes it (full remat)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--stage-json", default=None, help="also write per-stage details to this file")
@@ -79,15 +83,17 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     # buffers (allocated once, outside the timed region)
-    saved = moe.alloc_saved(T, emb, mlp, E, k, dev)
+    bwd = args.backward
+    remat = bwd and args.recompute_h
+    saved = moe.alloc_saved(T, emb, mlp, E, k, dev, keep_h=not remat)
     y = torch.empty((T, emb), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(moe.workspace_bytes(T, emb, mlp, E, k), dtype=torch.uint8, device=dev)
     pws = torch.empty(max(16, int(_lib.lib().moe_permute_workspace_bytes(
         __import__("ctypes").byref(_lib.shape(T, emb, mlp, E, k))))), dtype=torch.uint8, device=dev)
-    bwd = args.backward
     if bwd:
         dy = inp["dy"]
-        bws = torch.empty(moe.workspace_bytes(T, emb, mlp, E, k, backward=True), dtype=torch.uint8, device=dev)
+        bws = torch.empty(moe.workspace_bytes(T, emb, mlp, E, k, backward=True, recompute_h=remat),
+                          dtype=torch.uint8, device=dev)
         grads = dict(dx=torch.empty((T, emb), dtype=torch.bfloat16, device=dev),
                      dwi=torch.empty_like(wi), dwo=torch.empty_like(wo),
                      dtopk_w=torch.empty((T, k), dtype=torch.float32, device=dev))
@@ -267,11 +273,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "emb": emb, "mlp": mlp, "E": E, "k": k,
                    "pass": "forward+backward" if bwd else "forward", "router_backward": router_bwd,
+                   "recompute_h": remat,
                    "parallelism": "none (1 GPU)"},
         "layer_tflops": round(tf(fwd_flop * (3 if bwd else 1), ms_step), 2),
         "gemm_stage_tflops": round(tf(fwd_flop, gemm_ms), 2),
         "gemm_stage_frac": round(tf(fwd_flop, gemm_ms) / PEAK_BF16_TFLOPS, 4),
         "fused_entry_ms": None if fused_ms is None else round(fused_ms, 4),
+        # activations kept from the forward for the backward (the saved set)
+        "saved_bytes": sum(v.numel() * v.element_size() for v in saved.values() if v is not None) if bwd else None,
         "stages": {k_: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                    for k_, v in stages.items()},
         "roofline": roofline,

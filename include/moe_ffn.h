@@ -85,7 +85,8 @@ int moe_query_support(const moe_shape_t* shape);
  *    masks and row bases).
  *  moe_workspace_bytes: scratch of moe_ffn_fwd (with_backward = 0: routing,
  *    indices and the xs/a/o activations when no saved set is given) or of
- *    moe_ffn_bwd (with_backward = 1: the do/dh/dxs activations).
+ *    moe_ffn_bwd (with_backward = 1: the do/dh/dxs activations; 2: also h,
+ *    for a saved set whose h is NULL).
  */
 size_t moe_permute_workspace_bytes(const moe_shape_t* shape);
 size_t moe_workspace_bytes(const moe_shape_t* shape, int with_backward);
@@ -205,8 +206,12 @@ int moe_combine_bwd(const moe_shape_t* shape, const moe_bf16_t* dy, const moe_bf
 /* Caller-owned activations of one forward pass, kept for the backward. All
    device pointers: topk_idx [T,k], topk_w [T,k], group_sizes [E],
    group_offsets [E+1], sorted_slot [S], slot_row [S], xs [S,emb] bf16,
-   h [S,2*mlp] fp32 (the gate/up pre-activations, unrounded), a [S,mlp] bf16,
-   o [S,emb] bf16. */
+   h [S,2*mlp] fp32 (the gate/up pre-activations, unrounded) or NULL, a
+   [S,mlp] bf16, o [S,emb] bf16. With h NULL the forward does not keep the
+   gate/up values and the backward recomputes them (the Gemma4 workload of
+   "MoE: fused TensorCore Pallas permute/combine kernels ...", Context, runs
+   with full rematerialisation): 8*S*mlp fewer bytes held between the passes
+   for one more GEMM1 in the backward. */
 typedef struct {
   int32_t* topk_idx;
   float* topk_w;
@@ -252,7 +257,7 @@ int moe_route_bwd(const moe_shape_t* shape, const moe_bf16_t* x, const float* wr
  * wo [E, mlp, emb], combine. y [T, emb] bf16.
  *  Router inputs as in moe_route. saved: NULL for inference (intermediates
  *  live in the workspace and h is not produced), else every pointer in it
- *  must be set and receives the intermediates.
+ *  but h must be set and receives the intermediates (h NULL: not kept).
  *  For inference the expert-sorted copy xs is not written: the permute builds
  *  only the index and GEMM1 gathers x rows through sorted_slot, the
  *  single-device half of the fused MoE kernel of "Fused MoE Kernel
@@ -274,7 +279,11 @@ int moe_ffn_fwd(const moe_shape_t* shape, const moe_bf16_t* x, const float* wr, 
  *  dy [T, emb] bf16; saved from a moe_ffn_fwd call with the same shape and
  *  weights. Outputs (each may be NULL to skip it): dx [T, emb] bf16,
  *  dwi [E, emb, 2*mlp] bf16, dwo [E, mlp, emb] bf16, dtopk_w [T, k] fp32.
- *  ws: at least moe_workspace_bytes(shape, 1) bytes.
+ *  If saved->h is NULL, h is first recomputed from xs and wi by the
+ *  forward's own GEMM, which gives the same bits as a kept h, so the
+ *  gradients are identical either way.
+ *  ws: at least moe_workspace_bytes(shape, 1) bytes, or
+ *  moe_workspace_bytes(shape, 2) if saved->h is NULL.
  */
 int moe_ffn_bwd(const moe_shape_t* shape, const moe_bf16_t* dy, const moe_saved_t* saved, const moe_bf16_t* wi,
                 const moe_bf16_t* wo, moe_bf16_t* dx, moe_bf16_t* dwi, moe_bf16_t* dwo, float* dtopk_w, void* ws,

@@ -57,9 +57,10 @@ def query_support(T: int, emb: int, mlp: int, E: int, k: int) -> None:
     _lib.check(_lib.lib().moe_query_support(C.byref(s)), "moe_query_support")
 
 
-def workspace_bytes(T: int, emb: int, mlp: int, E: int, k: int, backward: bool = False) -> int:
+def workspace_bytes(T: int, emb: int, mlp: int, E: int, k: int, backward: bool = False,
+                    recompute_h: bool = False) -> int:
     s = _lib.shape(T, emb, mlp, E, k)
-    return int(_lib.lib().moe_workspace_bytes(C.byref(s), int(backward)))
+    return int(_lib.lib().moe_workspace_bytes(C.byref(s), (2 if recompute_h else 1) if backward else 0))
 
 
 def route(k: int, x: torch.Tensor | None = None, wr: torch.Tensor | None = None, bias: torch.Tensor | None = None,
@@ -191,7 +192,8 @@ def combine_bwd(dy: torch.Tensor, ys: torch.Tensor | None, slot_row: torch.Tenso
 _SAVED_NAMES = ("topk_idx", "topk_w", "group_sizes", "group_offsets", "sorted_slot", "slot_row", "xs", "h", "a", "o")
 
 
-def alloc_saved(T: int, emb: int, mlp: int, E: int, k: int, device) -> dict:
+def alloc_saved(T: int, emb: int, mlp: int, E: int, k: int, device, keep_h: bool = True) -> dict:
+    """Buffers of one forward pass for the backward; keep_h=False leaves h out (the backward recomputes it)."""
     S = T * k
     i32, f32, bf = torch.int32, torch.float32, torch.bfloat16
     return dict(topk_idx=torch.empty((T, k), dtype=i32, device=device),
@@ -201,13 +203,13 @@ def alloc_saved(T: int, emb: int, mlp: int, E: int, k: int, device) -> dict:
                 sorted_slot=torch.empty(S, dtype=i32, device=device),
                 slot_row=torch.empty(S, dtype=i32, device=device),
                 xs=torch.empty((S, emb), dtype=bf, device=device),
-                h=torch.empty((S, 2 * mlp), dtype=f32, device=device),
+                h=torch.empty((S, 2 * mlp), dtype=f32, device=device) if keep_h else None,
                 a=torch.empty((S, mlp), dtype=bf, device=device),
                 o=torch.empty((S, emb), dtype=bf, device=device))
 
 
 def _saved_struct(saved: dict) -> MoeSaved:
-    return MoeSaved(*[saved[n].data_ptr() for n in _SAVED_NAMES])
+    return MoeSaved(*[0 if saved[n] is None else saved[n].data_ptr() for n in _SAVED_NAMES])
 
 
 def route_bwd(x: torch.Tensor, wr: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor,
@@ -239,8 +241,9 @@ def route_bwd(x: torch.Tensor, wr: torch.Tensor, topk_idx: torch.Tensor, topk_w:
 
 def ffn_fwd(x: torch.Tensor, wi: torch.Tensor, wo: torch.Tensor, k: int, wr: torch.Tensor | None = None,
             bias: torch.Tensor | None = None, logits: torch.Tensor | None = None, save: bool = False,
-            workspace: torch.Tensor | None = None, out: torch.Tensor | None = None):
-    """MoE FFN forward. Returns (y [T, emb] bf16, saved dict or None)."""
+            workspace: torch.Tensor | None = None, out: torch.Tensor | None = None, keep_h: bool = True):
+    """MoE FFN forward. Returns (y [T, emb] bf16, saved dict or None). With save and keep_h=False the
+    saved set has no h, and ffn_bwd recomputes it."""
     _need(x, "x", torch.bfloat16)
     dev = x.device
     for t, n, d in ((wi, "wi", torch.bfloat16), (wo, "wo", torch.bfloat16), (wr, "wr", torch.float32),
@@ -256,7 +259,7 @@ def ffn_fwd(x: torch.Tensor, wi: torch.Tensor, wo: torch.Tensor, k: int, wr: tor
     ws = workspace if workspace is not None and workspace.numel() >= ws_n else \
         torch.empty(ws_n, dtype=torch.uint8, device=dev)
     y = out if out is not None else torch.empty((T, emb), dtype=torch.bfloat16, device=dev)
-    saved = alloc_saved(T, emb, mlp, E, k, dev) if save else None
+    saved = alloc_saved(T, emb, mlp, E, k, dev, keep_h=keep_h) if save else None
     sv = C.byref(_saved_struct(saved)) if save else None
     _lib.check(_lib.lib().moe_ffn_fwd(C.byref(s), _ptr(x), _ptr(wr), _ptr(bias), _ptr(logits), _ptr(wi), _ptr(wo),
                                       _ptr(y), sv, _ptr(ws), ws.numel(), _stream(dev)), "moe_ffn_fwd")
@@ -274,7 +277,7 @@ def ffn_bwd(dy: torch.Tensor, saved: dict, wi: torch.Tensor, wo: torch.Tensor, k
     E, _, n2 = wi.shape
     mlp = n2 // 2
     s = _lib.shape(T, emb, mlp, E, k)
-    ws_n = int(_lib.lib().moe_workspace_bytes(C.byref(s), 1))
+    ws_n = int(_lib.lib().moe_workspace_bytes(C.byref(s), 2 if saved.get("h") is None else 1))
     if ws_n == 0:
         _lib.check(_lib.lib().moe_query_support(C.byref(s)), "ffn_bwd")
     ws = workspace if workspace is not None and workspace.numel() >= ws_n else \

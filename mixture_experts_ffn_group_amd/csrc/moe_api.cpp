@@ -110,6 +110,12 @@ size_t bwd_ws(const moe_shape_t* s) {
   const size_t S = (size_t)s->T * s->k;
   return round_up(S * s->emb * 2) /*do*/ + round_up(S * 2 * s->mlp * 2) /*dh*/ + round_up(S * s->emb * 2) /*dxs*/;
 }
+// Backward that recomputes h (the saved set has none): h [S, 2*mlp] fp32, and the SwiGLU output the
+// recomputing GEMM also writes, which shares the dxs buffer unless mlp > emb.
+size_t bwd_remat_ws(const moe_shape_t* s) {
+  const size_t S = (size_t)s->T * s->k;
+  return bwd_ws(s) + round_up(S * 2 * s->mlp * 4) + (s->mlp > s->emb ? round_up(S * s->mlp * 2) : 0);
+}
 
 int check_gemm(int op, int epi, int64_t M, int K, int N, int E) {
   if (op != MOE_NN && op != MOE_NT) return fail(MOE_ERR_SHAPE, "op must be MOE_NN or MOE_NT");
@@ -163,7 +169,7 @@ size_t moe_permute_workspace_bytes(const moe_shape_t* shape) {
 
 size_t moe_workspace_bytes(const moe_shape_t* shape, int with_backward) {
   if (check_shape(shape) != MOE_OK) return 0;
-  return with_backward ? bwd_ws(shape) : fwd_ws(shape);
+  return with_backward == 2 ? bwd_remat_ws(shape) : with_backward ? bwd_ws(shape) : fwd_ws(shape);
 }
 
 // per-slot logit gradients, then Wr transposed
@@ -366,7 +372,7 @@ int moe_ffn_fwd(const moe_shape_t* s, const moe_bf16_t* x, const float* wr, cons
       NEED(saved->sorted_slot);
       NEED(saved->slot_row);
       NEED(saved->xs);
-      NEED(saved->h);
+      MAYBE(saved->h);  // NULL: h is not kept, and moe_ffn_bwd recomputes it
       NEED(saved->a);
       NEED(saved->o);
     }
@@ -426,7 +432,7 @@ int moe_ffn_bwd(const moe_shape_t* s, const moe_bf16_t* dy, const moe_saved_t* s
     NEED(saved->sorted_slot);
     NEED(saved->slot_row);
     NEED(saved->xs);
-    NEED(saved->h);
+    MAYBE(saved->h);  // NULL: recomputed here from xs and wi
     NEED(saved->a);
     NEED(saved->o);
   }
@@ -437,7 +443,9 @@ int moe_ffn_bwd(const moe_shape_t* s, const moe_bf16_t* dy, const moe_saved_t* s
   MAYBE(dwo);
   MAYBE(dtopk_w);
   NEED(ws);
-  if (ws_bytes < bwd_ws(s)) return fail(MOE_ERR_WORKSPACE, "need %zu workspace bytes", bwd_ws(s));
+  const bool remat = saved->h == nullptr;
+  const size_t need_ws = remat ? bwd_remat_ws(s) : bwd_ws(s);
+  if (ws_bytes < need_ws) return fail(MOE_ERR_WORKSPACE, "need %zu workspace bytes", need_ws);
   const int64_t T = s->T, S = T * s->k;
   const int emb = s->emb, mlp = s->mlp, E = s->E, k = s->k;
   const hipStream_t st = (hipStream_t)stream;
@@ -445,6 +453,7 @@ int moe_ffn_bwd(const moe_shape_t* s, const moe_bf16_t* dy, const moe_saved_t* s
   moe_bf16_t* d_o = c.take<moe_bf16_t>(S * emb);
   moe_bf16_t* dh = c.take<moe_bf16_t>(S * 2 * mlp);
   moe_bf16_t* dxs = c.take<moe_bf16_t>(S * emb);
+  const float* h = saved->h;
   // combine backward: do (the permutation part) and dtopk_w (the reduction part)
   if (int rc = hip_status(moe::launch_combine_bwd(T, emb, k, dy, dtopk_w ? saved->o : nullptr, saved->slot_row,
                                                   saved->topk_w, d_o, dtopk_w, st),
@@ -455,8 +464,20 @@ int moe_ffn_bwd(const moe_shape_t* s, const moe_bf16_t* dy, const moe_saved_t* s
       return rc;
   }
   if (!dx && !dwi) return MOE_OK;
+  if (remat && S > 0) {
+    // Recompute h = xs . wi[e] with the forward's own GEMM (same kernel, same inputs: the same bits as a
+    // saved h). Its SwiGLU output is not needed and goes to the dxs buffer, which is written only later.
+    float* hr = c.take<float>(S * 2 * mlp);
+    moe_bf16_t* a_tmp = mlp > emb ? c.take<moe_bf16_t>(S * mlp) : dxs;
+    if (int rc = hip_status(moe::launch_grouped_gemm(MOE_NN, MOE_EPI_SWIGLU, saved->xs, wi, nullptr, hr,
+                                                     saved->group_offsets, E, S, emb, 2 * mlp, nullptr, 0, 1,
+                                                     nullptr, a_tmp, st),
+                            "recompute h"))
+      return rc;
+    h = hr;
+  }
   // da = w * (dy . wo[e]^T): dy rows read in place through sorted_slot, the top-k weight applied in fp32
-  if (int rc = hip_status(moe::launch_grouped_gemm(MOE_NT, MOE_EPI_SWIGLU_BWD, dy, wo, saved->h, nullptr,
+  if (int rc = hip_status(moe::launch_grouped_gemm(MOE_NT, MOE_EPI_SWIGLU_BWD, dy, wo, h, nullptr,
                                                    saved->group_offsets, E, S, emb, mlp, saved->sorted_slot, (int)S, k,
                                                    saved->topk_w, dh, st),
                           "dh"))

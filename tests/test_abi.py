@@ -134,6 +134,12 @@ def test_validation_precedes_any_launch(lib):
     partial = _lib.MoeSaved(*([0x1000] * 9 + [0]))
     assert lib.moe_ffn_fwd(C.byref(s), fake, fake, nul, nul, fake, fake, fake, C.byref(partial), fake, 1 << 40,
                            nul) == _lib.MOE_ERR_NULL
+    # a saved set without h: the backward recomputes it and needs the larger workspace
+    ws1, ws2 = lib.moe_workspace_bytes(C.byref(s), 1), lib.moe_workspace_bytes(C.byref(s), 2)
+    assert ws2 >= ws1 + s.T * s.k * 2 * s.mlp * 4
+    no_h = _lib.MoeSaved(*([0x1000] * 7 + [0] + [0x1000] * 2))
+    assert lib.moe_ffn_bwd(C.byref(s), fake, C.byref(no_h), fake, fake, fake, fake, fake, fake, fake, ws1,
+                           nul) == _lib.MOE_ERR_WORKSPACE
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

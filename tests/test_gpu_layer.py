@@ -149,6 +149,26 @@ def test_layer_backward_every_token_and_expert():
     assert torch.equal(g2["dx"].view(torch.int16), g["dx"].view(torch.int16))
 
 
+@pytest.mark.parametrize("T,emb,mlp,E,k", [(384, 256, 128, 8, 2), (300, 128, 256, 6, 3)])
+def test_layer_backward_recomputing_h_equals_kept_h_bitwise(T, emb, mlp, E, k):
+    """Full rematerialisation of h: the forward keeps no h and the backward recomputes it with the forward's
+    own GEMM, so every gradient and every other kept activation is bit-identical to the run that keeps h
+    (mlp > emb in the second case puts the recomputed SwiGLU output in a buffer of its own)."""
+    wl = workloads.custom(T, emb, mlp, E, k, seed=91, sigma_w=0.02, backward=True)
+    d = _dev(workloads.make_inputs(wl))
+    y1, s1 = moe.ffn_fwd(d["x"], d["wi"], d["wo"], k, wr=d["wr"], bias=d["bias"], save=True)
+    y2, s2 = moe.ffn_fwd(d["x"], d["wi"], d["wo"], k, wr=d["wr"], bias=d["bias"], save=True, keep_h=False)
+    assert s2["h"] is None
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    for n, v in s1.items():
+        if n != "h":
+            assert torch.equal(v.view(torch.uint8), s2[n].view(torch.uint8)), n
+    g1 = moe.ffn_bwd(d["dy"], s1, d["wi"], d["wo"], k)
+    g2 = moe.ffn_bwd(d["dy"], s2, d["wi"], d["wo"], k)
+    for n in ("dx", "dwi", "dwo", "dtopk_w"):
+        assert torch.equal(g1[n].view(torch.uint8), g2[n].view(torch.uint8)), n
+
+
 # ---------------------------------------------------------------- full-size workloads
 
 def _sample_tokens(T, n, seed):
