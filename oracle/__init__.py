@@ -21,7 +21,7 @@ import numpy as np
 from . import build as _build
 
 BF16, F32, F64 = 0, 1, 2
-_ERR = {1: "invalid argument", 2: "NaN logit", 3: "index out of range", 4: "expert picked twice by a token",
+_ERR = {1: "invalid argument", 2: "NaN input", 3: "index out of range", 4: "expert picked twice by a token",
         5: "out of memory"}
 _libs: dict[str, C.CDLL] = {}
 
@@ -52,6 +52,8 @@ def _lib(real: str) -> C.CDLL:
             "orc_grouped_wgrad": ([_p, C.c_int, _p, C.c_int, _p, _i32, _i64, _i32, _i32, _i32, _p], C.c_int),
             "orc_combine": ([_i64, _i32, _i32, _p, C.c_int, _p, _p, _p], C.c_int),
             "orc_combine_bwd": ([_i64, _i32, _i32, _p, C.c_int, _p, C.c_int, _p, _p, _p, _p], C.c_int),
+            "orc_e4m3_value": ([C.c_uint8], C.c_double),
+            "orc_mx_quantize": ([_i64, _i32, _p, _p, _p], C.c_int),
             "orc_router_bwd": ([_i64, _i32, _i32, _i32, _p, C.c_int, _p, _p, _p, _p, C.c_int, _p, _p, _p, _p],
                                C.c_int),
         }
@@ -375,3 +377,57 @@ def router_bwd(x, wr, topk_idx, topk_w, dtopk_w, real: str = "f64", want_dx: boo
     _check(_lib(real).orc_router_bwd(T, emb, E, k, xp, xdt, _ptr(wr), _ptr(idx), _ptr(w), gp, gdt, _ptr(dl),
                                      _ptr(dwr), _ptr(db), _ptr(dx)), "router_bwd")
     return dl, dwr, db, dx
+
+
+# ---------------------------------------------------------------- MXFP8
+
+def e4m3_value(code: int) -> float:
+    """Value of one FP8 E4M3 ("FN") code (NaN for 0x7f / 0xff)."""
+    return float(_lib("f32").orc_e4m3_value(int(code) & 0xFF))
+
+
+def mx_quantize(x_bits):
+    """MXFP8 of x [M, K] (bf16 bits) in blocks of 32 along K: (codes [M, K] uint8 E4M3, scales [M, K/32] uint8
+    E8M0). See moe_oracle.c, reading R8."""
+    x_bits = _c(x_bits, np.uint16)
+    M, K = x_bits.shape
+    codes = np.empty((M, K), np.uint8)
+    scales = np.empty((M, K // 32), np.uint8)
+    _check(_lib("f32").orc_mx_quantize(M, K, _ptr(x_bits), _ptr(codes), _ptr(scales)), "mx_quantize")
+    return codes, scales
+
+
+_E4M3_TABLE = None
+
+
+def mx_dequantize(codes, scales) -> np.ndarray:
+    """float64 values code * 2^(scale - 127) of an MXFP8 tensor [..., K] with scales [..., K/32]."""
+    global _E4M3_TABLE
+    if _E4M3_TABLE is None:
+        _E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], np.float64)
+    codes = np.asarray(codes, np.uint8)
+    scales = np.asarray(scales, np.uint8)
+    v = _E4M3_TABLE[codes]
+    f = np.ldexp(1.0, scales.astype(np.int64) - 127)
+    return v * np.repeat(f, 32, axis=-1)
+
+
+def mx_grouped_gemm_nt(a_codes, a_scales, b_codes, b_scales, group_offsets, epi: int = 0) -> np.ndarray:
+    """Grouped GEMM on MXFP8 operands, in float64 on the dequantized values: rows of group e of
+    A [M, K] times B[e] [N, K] transposed; epi 0 none, 1 SwiGLU (gate = columns [0, N/2), up = [N/2, N)).
+    The contraction runs over the exact products, so the only error of a device result against this is
+    its own summation."""
+    A = mx_dequantize(a_codes, a_scales)
+    B = mx_dequantize(b_codes, b_scales)
+    off = np.asarray(group_offsets, np.int64)
+    M = A.shape[0]
+    N = B.shape[1]
+    C_ = np.zeros((M, N), np.float64)
+    for e in range(B.shape[0]):
+        lo, hi = off[e], off[e + 1]
+        if hi > lo:
+            C_[lo:hi] = A[lo:hi] @ B[e].T
+    if epi == 1:
+        g, u = C_[:, : N // 2], C_[:, N // 2:]
+        return g / (1.0 + np.exp(-g)) * u
+    return C_

@@ -55,6 +55,17 @@
  *  R6 silu(g) = g / (1 + exp(-g)); SwiGLU a = silu(gate) * up.
  *  R7 the router backward holds the picks fixed (the selection has no
  *     gradient) and uses the forward's saved weights.
+ *  R8 MXFP8 ("[DRAFT][JAX] Optimize MoE block", Changes: MXFP8 quantization
+ *     of the MoE block) follows the OCP microscaling format: blocks of 32
+ *     consecutive elements along the contraction dimension share one
+ *     power-of-two scale stored as E8M0 (code c means 2^(c-127)), and the
+ *     elements are FP8 E4M3 (OCP "FN": bias 7, largest finite 448, no
+ *     infinities). The scale is 2^(floor(log2(amax)) - 8), 8 being the
+ *     exponent of E4M3's largest normal, its code clamped to [0, 254]; an
+ *     all-zero block takes code 0. Each element is v / scale (exact: a
+ *     power-of-two rescaling) rounded to the nearest E4M3 value, ties to an
+ *     even mantissa, magnitudes above 448 saturating to 448, the sign kept
+ *     (also on zero).
  */
 #include <math.h>
 #include <stdint.h>
@@ -556,6 +567,74 @@ int orc_combine_bwd(int64_t T, int32_t emb, int32_t k, const void* dy, int dy_dt
         if (ys && dw) acc += (real)elem(ys, ys_dt, r * emb + n) * d;
       }
       if (ys && dw) dw[t * k + j] = acc;
+    }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ MXFP8 */
+
+/* Value of an E4M3 ("FN") code: sign, 4-bit exponent (bias 7), 3-bit
+ * mantissa; exponent 0 is subnormal (m/8 * 2^-6). Codes 0x7f / 0xff are NaN
+ * and never produced by the quantizer. */
+double orc_e4m3_value(uint8_t c) {
+  const double sgn = (c & 0x80) ? -1.0 : 1.0;
+  const int e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  return e == 0 ? sgn * ldexp((double)m, -9) : sgn * ldexp(8.0 + m, e - 10);
+}
+
+/* Nearest E4M3 code to v (ties to even mantissa, |v| > 448 saturates). v is
+ * finite. Works on the exact value: the grid spacing below 2^-6 is 2^-9,
+ * and in [2^e, 2^(e+1)) it is 2^(e-3). */
+static uint8_t e4m3_encode(double v) {
+  const uint8_t sgn = signbit(v) ? 0x80 : 0x00;
+  double a = fabs(v);
+  if (a >= 448.0) return (uint8_t)(sgn | 0x7e);
+  int e;
+  frexp(a, &e); /* a = f * 2^e, f in [0.5, 1): a in [2^(e-1), 2^e) */
+  int ex = e - 1;
+  if (ex < -6) ex = -6; /* subnormal range shares the spacing of [2^-6, 2^-5) */
+  const double q = ldexp(1.0, ex - 3);
+  const double n = a / q; /* exact: q is a power of two */
+  double r = floor(n);
+  const double frac = n - r;
+  if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+  const double val = r * q;
+  if (val > 448.0) return (uint8_t)(sgn | 0x7e);
+  if (val == 0.0) return sgn;
+  if (val < ldexp(1.0, -6)) return (uint8_t)(sgn | (int)(val / ldexp(1.0, -9))); /* subnormal: m */
+  int ev;
+  frexp(val, &ev);
+  const int E = ev - 1; /* val in [2^E, 2^(E+1)) */
+  const int m = (int)(val / ldexp(1.0, E - 3)) - 8;
+  return (uint8_t)(sgn | ((E + 7) << 3) | m);
+}
+
+/* MXFP8 quantization of x [M, K] (bf16 bit patterns, row-major) in blocks of
+ * 32 along K: codes [M, K] E4M3 and scales [M, K/32] E8M0 (reading R8).
+ * K must be a multiple of 32; non-finite inputs are rejected. */
+int orc_mx_quantize(int64_t M, int32_t K, const uint16_t* x, uint8_t* codes, uint8_t* scales) {
+  if (M < 0 || K <= 0 || K % 32) return ORC_EINVAL;
+  for (int64_t r = 0; r < M; ++r)
+    for (int32_t b = 0; b < K / 32; ++b) {
+      const uint16_t* blk = x + r * K + (int64_t)b * 32;
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i) {
+        const double v = bf16_value(blk[i]);
+        if (!isfinite(v)) return ORC_ENAN;
+        if (fabs(v) > amax) amax = fabs(v);
+      }
+      int code = 0;
+      if (amax > 0.0) {
+        int e;
+        frexp(amax, &e);
+        code = (e - 1) - 8 + 127; /* floor(log2(amax)) - 8, biased */
+        if (code < 0) code = 0;
+        if (code > 254) code = 254;
+      }
+      scales[r * (K / 32) + b] = (uint8_t)code;
+      const double inv = ldexp(1.0, 127 - code);
+      for (int i = 0; i < 32; ++i) codes[r * K + (int64_t)b * 32 + i] = e4m3_encode(bf16_value(blk[i]) * inv);
     }
   return ORC_OK;
 }

@@ -552,3 +552,117 @@ def test_layer_router_gradient_matches_finite_differences_of_the_layer_output():
         a2[i, e] -= h
         num = (loss(a1) - loss(a2)) / (2 * h)
         assert abs(num - dwr[i, e]) <= 1e-6 + 1e-5 * abs(num), (i, e, num, dwr[i, e])
+
+
+# ---------------------------------------------------------------- MXFP8 (reading R8 of moe_oracle.c)
+
+def _e4m3_table():
+    return np.array([oracle.e4m3_value(c) for c in range(256)])
+
+
+def _bf16_bits(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_e4m3_code_table_matches_the_format():
+    t = _e4m3_table()
+    pos = t[:0x7F]
+    # OCP E4M3 ("FN"): 1.0 is 0x38, the largest finite value 448 is 0x7e, the smallest subnormal is 2^-9
+    # (0x01), the smallest normal 2^-6 (0x08); 0x7f / 0xff are NaN; the negative half mirrors the positive
+    assert t[0x38] == 1.0 and t[0x7E] == 448.0 and t[0x01] == 2.0 ** -9 and t[0x08] == 2.0 ** -6
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    assert np.array_equal(t[0x80:0xFF], -pos) and np.signbit(t[0x80])
+    assert np.all(np.diff(pos) > 0)  # codes in magnitude order
+    # eight values per binade above 2^-6, spacing 2^-9 below it
+    for e in range(-6, 9):
+        assert np.count_nonzero((pos >= 2.0 ** e) & (pos < 2.0 ** (e + 1))) == (7 if e == 8 else 8)
+    assert np.allclose(np.diff(pos[:9]), 2.0 ** -9)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_mx_quantize_picks_the_nearest_code_by_search(seed):
+    rng = np.random.default_rng(seed)
+    M, K = 24, 96
+    x = rng.standard_normal((M, K)) * np.exp(rng.uniform(-12, 12, (M, 1)))  # a different magnitude per row
+    x[0, :32] = 0.0                      # an all-zero block
+    x[1, 5] = -0.0
+    x[2, :32] = np.linspace(-1, 1, 32)   # exact zero inside a block
+    xb = _bf16_bits(x)
+    xv = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).double().numpy()
+    codes, scales = oracle.mx_quantize(xb)
+    t = _e4m3_table()
+    finite = np.array([c for c in range(256) if not np.isnan(t[c])])
+    for r in range(M):
+        for b in range(K // 32):
+            blk = xv[r, 32 * b: 32 * b + 32]
+            amax = np.abs(blk).max()
+            sc = float(2.0 ** (int(scales[r, b]) - 127))
+            if amax == 0:
+                assert scales[r, b] == 0 and np.all(t[codes[r, 32 * b: 32 * b + 32]] == 0)
+                continue
+            assert 256 <= amax / sc < 512  # scale = 2^(floor(log2 amax) - 8)
+            for i in range(32):
+                v = blk[i] / sc
+                c = int(codes[r, 32 * b + i])
+                d = np.abs(t[finite] - v)
+                best = finite[d == d.min()]
+                if len(best) > 1:  # tie: the even mantissa (for zero, the sign of v)
+                    best = [cc for cc in best if (cc & 1) == 0 and (t[cc] != 0 or np.signbit(t[cc]) == np.signbit(v))]
+                if abs(v) > 448:
+                    best = [0x7E | (0x80 if v < 0 else 0)]
+                assert c in best, (r, b, i, v, c, best)
+                assert np.signbit(t[c]) == np.signbit(v)
+
+
+def test_mx_quantize_round_trips_representable_values_and_bounds_the_error():
+    rng = np.random.default_rng(5)
+    t = _e4m3_table()
+    # values that are E4M3 codes times the block's own scale come back exactly
+    c = rng.choice([cc for cc in range(0x7F) if not np.isnan(t[cc])], (8, 64))
+    c[:, 0] = 0x7E                                   # pins each block's amax to 448 * 2^s
+    c[:, 32] = 0x7E
+    s = rng.integers(100, 150, (8, 1))
+    x = t[c] * np.ldexp(1.0, s - 127)
+    x *= rng.choice([-1.0, 1.0], x.shape)
+    codes, scales = oracle.mx_quantize(_bf16_bits(x))
+    assert np.array_equal(oracle.mx_dequantize(codes, scales), x)
+    # otherwise the error is at most half a grid step: 2^-4 of the value in the normal range, 2^-10 of the
+    # scale below it; a block maximum in [464, 512) x scale (past 448 and its rounding interval) saturates
+    y = rng.standard_normal((16, 128))
+    yb = _bf16_bits(y)
+    yv = torch.from_numpy(yb.view(np.int16)).view(torch.bfloat16).double().numpy()
+    cq, sq = oracle.mx_quantize(yb)
+    dq = oracle.mx_dequantize(cq, sq)
+    scale = np.repeat(np.ldexp(1.0, sq.astype(np.int64) - 127), 32, axis=1)
+    sat = np.abs(yv) >= 464 * scale
+    assert sat.any()  # the sample has some
+    assert np.array_equal(dq[sat], np.sign(yv[sat]) * 448 * scale[sat])
+    normal = (np.abs(yv) >= scale * 2.0 ** -6) & ~sat
+    assert np.all(np.abs(dq - yv)[normal] <= 2.0 ** -4 * np.abs(yv)[normal])
+    assert np.all(np.abs(dq - yv)[~normal & ~sat] <= scale[~normal & ~sat] * 2.0 ** -10)
+
+
+def test_mx_quantize_rejects_non_finite_input():
+    x = np.zeros((1, 32), np.float32)
+    x[0, 3] = np.inf
+    with pytest.raises(RuntimeError):
+        oracle.mx_quantize(_bf16_bits(x))
+
+
+def test_mx_grouped_gemm_on_integer_codes_is_the_integer_product():
+    rng = np.random.default_rng(9)
+    t = _e4m3_table()
+    ints = [cc for cc in range(0x7F) if t[cc] == int(t[cc]) and t[cc] <= 16]  # 0, 1, ..., 16 and a few more
+    M, K, N, E = 40, 64, 24, 3
+    ac = rng.choice(ints, (M, K)).astype(np.uint8) | (rng.integers(0, 2, (M, K)) * 0x80).astype(np.uint8)
+    bc = rng.choice(ints, (E, N, K)).astype(np.uint8)
+    a_s = np.full((M, K // 32), 127, np.uint8)
+    b_s = np.full((E, N, K // 32), 127, np.uint8)
+    off = np.array([0, 7, 7, 40])
+    got = oracle.mx_grouped_gemm_nt(ac, a_s, bc, b_s, off)
+    A = t[ac].astype(np.int64)
+    B = t[bc].astype(np.int64)
+    ref = np.zeros((M, N), np.int64)
+    for e in range(E):
+        ref[off[e]:off[e + 1]] = A[off[e]:off[e + 1]] @ B[e].T
+    assert np.array_equal(got, ref)
