@@ -252,6 +252,38 @@ int moe_route_bwd(const moe_shape_t* shape, const moe_bf16_t* x, const float* wr
                   moe_stream_t stream);
 
 /*
+ * MXFP8 ("[DRAFT][JAX] Optimize MoE block", Changes: MXFP8 quantization in
+ * the MoE block), in the OCP microscaling format: 32 consecutive elements
+ * along the contraction dimension K share a power-of-two scale held as E8M0
+ * (code c is 2^(c-127)), and the elements are FP8 E4M3 (bias 7, largest
+ * finite 448). A block's scale is 2^(floor(log2(amax)) - 8), code clamped to
+ * [0, 254], code 0 for an all-zero block; each element is v / scale rounded
+ * to the nearest E4M3 value, ties to an even mantissa, magnitudes past 448
+ * saturating, the sign kept. Inputs must be finite (otherwise the codes are
+ * unspecified). Layouts, both K-contiguous:
+ *   codes  [rows][K] bytes;
+ *   scales [K/64][rows][4] bytes: bytes 0 and 1 hold the scales of blocks
+ *          2j and 2j+1 of slice j of the row, bytes 2 and 3 are zero.
+ * K must be a multiple of 64.
+ *
+ * moe_mx_quantize_rows -- rows of src [src_rows, K] bf16: output row r is
+ *  source row row_index[r] / row_div (clamped into [0, src_rows)) when
+ *  row_index is given (a gather through sorted_slot with row_div = k builds
+ *  the expert-sorted rows directly), else row r. codes [M, K], scales
+ *  [K/64][M][4].
+ */
+int moe_mx_quantize_rows(const moe_bf16_t* src, int64_t src_rows, int32_t K, const int32_t* row_index,
+                         int32_t row_div, int64_t M, uint8_t* codes, uint8_t* scales, moe_stream_t stream);
+
+/*
+ * moe_mx_quantize_weight -- expert weights w [E, K, N] bf16 (the layout of wi
+ *  and wo) in blocks of 32 along K, transposed to K-contiguous rows:
+ *  codes [E, N, K], scales [E][K/64][N][4].
+ */
+int moe_mx_quantize_weight(const moe_bf16_t* w, int32_t E, int32_t K, int32_t N, uint8_t* codes, uint8_t* scales,
+                           moe_stream_t stream);
+
+/*
  * moe_ffn_fwd -- the whole MoE FFN forward: route, permute, grouped GEMM on
  * the prefused wi [E, emb, 2*mlp] with the SwiGLU epilogue, grouped GEMM on
  * wo [E, mlp, emb], combine. y [T, emb] bf16.

@@ -295,3 +295,31 @@ def ffn_bwd(dy: torch.Tensor, saved: dict, wi: torch.Tensor, wo: torch.Tensor, k
                                       _ptr(g.get("dx")), _ptr(g.get("dwi")), _ptr(g.get("dwo")),
                                       _ptr(g.get("dtopk_w")), _ptr(ws), ws.numel(), _stream(dev)), "moe_ffn_bwd")
     return g
+
+
+def mx_quantize_rows(src: torch.Tensor, row_index: torch.Tensor | None = None, row_div: int = 1,
+                     rows: int | None = None):
+    """MXFP8 of rows of src [R, K] bf16 (see moe_mx_quantize_rows): (codes [M, K] uint8, scales [K/64, M, 4]
+    uint8). With row_index, output row r is source row row_index[r] // row_div."""
+    _need(src, "src", torch.bfloat16)
+    dev = src.device
+    _need(row_index, "row_index", torch.int32, dev)
+    R, K = src.shape
+    M = rows if rows is not None else (row_index.numel() if row_index is not None else R)
+    codes = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    scales = torch.empty((K // 64, M, 4), dtype=torch.uint8, device=dev)
+    _lib.check(_lib.lib().moe_mx_quantize_rows(_ptr(src), R, K, _ptr(row_index), row_div, M, _ptr(codes),
+                                               _ptr(scales), _stream(dev)), "moe_mx_quantize_rows")
+    return codes, scales
+
+
+def mx_quantize_weight(w: torch.Tensor):
+    """MXFP8 of expert weights w [E, K, N] bf16 along K, transposed (see moe_mx_quantize_weight):
+    (codes [E, N, K] uint8, scales [E, K/64, N, 4] uint8)."""
+    _need(w, "w", torch.bfloat16)
+    E, K, N = w.shape
+    codes = torch.empty((E, N, K), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((E, K // 64, N, 4), dtype=torch.uint8, device=w.device)
+    _lib.check(_lib.lib().moe_mx_quantize_weight(_ptr(w), E, K, N, _ptr(codes), _ptr(scales), _stream(w.device)),
+               "moe_mx_quantize_weight")
+    return codes, scales

@@ -39,6 +39,10 @@ hipError_t launch_combine_bwd(int64_t T, int emb, int k, const uint16_t* dy, con
                               const int32_t* slot_row, const float* w, uint16_t* dys, float* dw, hipStream_t stream);
 
 // Router backward, picks held fixed. dl: [T*k] fp32 scratch; wrt: [E, emb] fp32 scratch (used when dx != NULL).
+hipError_t launch_mx_quantize_rows(const uint16_t* src, int64_t src_rows, int K, const int32_t* row_index, int row_div,
+                                   int64_t M, uint8_t* codes, uint8_t* scales, hipStream_t stream);
+hipError_t launch_mx_quantize_weight(const uint16_t* w, int E, int K, int N, uint8_t* codes, uint8_t* scales,
+                                     hipStream_t stream);
 hipError_t launch_route_bwd(int64_t T, int emb, int E, int k, const uint16_t* x, const float* wr,
                             const int32_t* topk_idx, const float* topk_w, const float* dtopk_w,
                             const int32_t* sorted_slot, const int32_t* group_offsets, float* dwr, float* dbias,

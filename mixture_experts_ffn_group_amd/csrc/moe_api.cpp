@@ -342,6 +342,37 @@ int moe_route_bwd(const moe_shape_t* s, const moe_bf16_t* x, const float* wr, co
                     "moe_route_bwd");
 }
 
+int moe_mx_quantize_rows(const moe_bf16_t* src, int64_t src_rows, int32_t K, const int32_t* row_index,
+                         int32_t row_div, int64_t M, uint8_t* codes, uint8_t* scales, moe_stream_t stream) {
+  g_detail[0] = 0;
+  if (M < 0 || src_rows < 0 || K <= 0) return fail(MOE_ERR_SHAPE, "need M, src_rows >= 0 and K > 0");
+  if (K % 64) return fail(MOE_ERR_UNSUPPORTED, "K (%d) is not a multiple of 64", K);
+  if (M * (K / 8) >= (int64_t(1) << 31) * 256) return fail(MOE_ERR_UNSUPPORTED, "M*K too large");
+  if (M == 0) return MOE_OK;
+  if (src_rows == 0) return fail(MOE_ERR_SHAPE, "no source rows for %lld output rows", (long long)M);
+  if (row_index && row_div <= 0) return fail(MOE_ERR_SHAPE, "row_div must be > 0");
+  NEED(src);
+  MAYBE(row_index);
+  NEED(codes);
+  NEED(scales);
+  return hip_status(moe::launch_mx_quantize_rows(src, src_rows, K, row_index, row_index ? row_div : 1, M, codes,
+                                                  scales, (hipStream_t)stream),
+                    "moe_mx_quantize_rows");
+}
+
+int moe_mx_quantize_weight(const moe_bf16_t* w, int32_t E, int32_t K, int32_t N, uint8_t* codes, uint8_t* scales,
+                           moe_stream_t stream) {
+  g_detail[0] = 0;
+  if (E <= 0 || K <= 0 || N <= 0) return fail(MOE_ERR_SHAPE, "need E, K, N > 0");
+  if (K % 64) return fail(MOE_ERR_UNSUPPORTED, "K (%d) is not a multiple of 64", K);
+  if ((int64_t)E * (K / 64) * N >= (int64_t(1) << 31) * 256) return fail(MOE_ERR_UNSUPPORTED, "E*K*N too large");
+  NEED(w);
+  NEED(codes);
+  NEED(scales);
+  return hip_status(moe::launch_mx_quantize_weight(w, E, K, N, codes, scales, (hipStream_t)stream),
+                    "moe_mx_quantize_weight");
+}
+
 int moe_ffn_fwd(const moe_shape_t* s, const moe_bf16_t* x, const float* wr, const float* bias, const float* logits_in,
                 const moe_bf16_t* wi, const moe_bf16_t* wo, moe_bf16_t* y, const moe_saved_t* saved, void* ws,
                 size_t ws_bytes, moe_stream_t stream) {

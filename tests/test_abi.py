@@ -134,6 +134,13 @@ def test_validation_precedes_any_launch(lib):
     partial = _lib.MoeSaved(*([0x1000] * 9 + [0]))
     assert lib.moe_ffn_fwd(C.byref(s), fake, fake, nul, nul, fake, fake, fake, C.byref(partial), fake, 1 << 40,
                            nul) == _lib.MOE_ERR_NULL
+    # MXFP8 quantizers: K must be a multiple of 64, pointers present, gather divisor positive
+    assert lib.moe_mx_quantize_rows(fake, 8, 96, nul, 1, 8, fake, fake, nul) == _lib.MOE_ERR_UNSUPPORTED
+    assert lib.moe_mx_quantize_rows(nul, 8, 128, nul, 1, 8, fake, fake, nul) == _lib.MOE_ERR_NULL
+    assert lib.moe_mx_quantize_rows(fake, 8, 128, fake, 0, 8, fake, fake, nul) == _lib.MOE_ERR_SHAPE
+    assert lib.moe_mx_quantize_rows(fake, 8, 128, nul, 1, 0, nul, nul, nul) == _lib.MOE_OK  # no rows: no-op
+    assert lib.moe_mx_quantize_weight(fake, 2, 96, 64, fake, fake, nul) == _lib.MOE_ERR_UNSUPPORTED
+    assert lib.moe_mx_quantize_weight(fake, 2, 128, 64, nul, fake, nul) == _lib.MOE_ERR_NULL
     # a saved set without h: the backward recomputes it and needs the larger workspace
     ws1, ws2 = lib.moe_workspace_bytes(C.byref(s), 1), lib.moe_workspace_bytes(C.byref(s), 2)
     assert ws2 >= ws1 + s.T * s.k * 2 * s.mlp * 4
