@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_ffn.so")
-SOURCES = ["route.hip", "route_bwd.hip", "permute.hip", "gemm.hip", "combine.hip", "mxfp8.hip", "moe_api.cpp"]
+SOURCES = ["route.hip", "route_bwd.hip", "permute.hip", "gemm.hip", "combine.hip", "mxfp8.hip", "mx_gemm.hip", "moe_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # -packed-fp32-ops: no packed fp32 VALU instructions anywhere (scalar fp32 only).

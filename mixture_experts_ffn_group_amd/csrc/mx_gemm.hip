@@ -1,0 +1,337 @@
+// Grouped GEMM on MXFP8 operands ("[DRAFT][JAX] Optimize MoE block",
+// Changes: MXFP8 quantization in the MoE block; Flowchart: grouped FC1
+// quantize and GEMM), on gfx950's block-scaled matrix cores:
+//   C[r, n] = sum_k A[r, k] * B[e][n, k]   for the rows r of group e,
+// where A and B are E4M3 codes times the E8M0 scale of their 32-element K
+// block (the layouts of mxfp8.hip: codes K-contiguous, scales one dword per
+// row and 64-element slice). Epilogues: none (C [M, N] bf16) or SwiGLU on a
+// prefused [gate | up] weight (C [M, N/2] bf16, gate = columns [0, N/2)).
+//
+// v_mfma_scale_f32_32x32x64_f8f6f4 multiplies 32 x 64 by 64 x 32 with one
+// scale byte per lane and 32-element block. Its operand layout (pinned on the
+// device): lane l holds row l % 32; bytes 0-15 are K elements 16h .. 16h+15
+// and bytes 16-31 are 32+16h .. 32+16h+15, h = l / 32 (the same assignment
+// for both operands), and its scale is that of row l % 32 and block h. The
+// products of one instruction are summed to a precision fixed relative to the
+// largest of them (probes: within 2^-11.8 of the largest product), then added
+// to the fp32 accumulator.
+//
+// The kernel follows the bf16 grouped GEMM: 8 waves as 2 (M) x 4 (N), a
+// 256 x 256 output tile per workgroup, each wave 128 x 64 (4 x 2 MFMA
+// blocks); a persistent XCD-dealt grid over the ragged tile list built from
+// the device group offsets; direct global->LDS copies into four stages. A
+// k-slice is 64 elements (64 bytes per row, one MFMA deep); with it travel
+// the two operands' scale dwords of the tile's 256 rows (waves 0-3 copy the A
+// rows', waves 4-7 the B rows'), so every wave issues 5 copies per k-slice.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int MXT = 512;                        // threads: 8 waves
+constexpr int MXN = 4;                          // LDS stages
+constexpr int kMxOp = 256 * 64;                 // one operand tile per stage: 256 rows x 64 bytes
+constexpr int kMxScl = 256 * 4;                 // one operand's scale dwords per stage
+constexpr int kMxStage = 2 * kMxOp + 2 * kMxScl;  // 34 KB
+enum { MXE_NONE = 0, MXE_SWIGLU = 1 };
+
+struct MxGemmP {
+  const uint8_t* A;   // codes [M][K]
+  const uint8_t* As;  // scales [K/64][M][4]
+  const uint8_t* B;   // codes [E][N][K]
+  const uint8_t* Bs;  // scales [E][K/64][N][4]
+  const int32_t* off;
+  uint16_t* C;
+  int E, M, K, N;
+};
+
+__device__ __forceinline__ void mx_g2lds16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void mx_g2lds4(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"(sbase), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void mx_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void mx_wait_5() { asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); }
+__device__ __forceinline__ void mx_wait_10() { asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); }
+__device__ __forceinline__ uint32_t mx_lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ int mx_opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+template <class T>
+__device__ __forceinline__ const T* mx_uniform(const T* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const T*)(((uint64_t)hi << 32) | lo);
+}
+
+// [row][k] tiles of 64-byte rows, 16-byte chunk c of a row at row*64 + ((c ^ ((row >> 2) & 3)) << 4)
+__device__ __forceinline__ int mx_off(int row, int c) { return row * 64 + ((c ^ ((row >> 2) & 3)) << 4); }
+
+// MFMA operand of tile row `row` for lane half h: chunks h and 2 + h.
+__device__ __forceinline__ i32x8_t mx_frag(const uint8_t* tile, int row, int h) {
+  const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(tile + mx_off(row, h));
+  const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(tile + mx_off(row, 2 + h));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int EPI>
+__device__ __forceinline__ int mx_col(int wn, int f) {
+  if (EPI == MXE_SWIGLU) return f == 0 ? wn * 32 : 128 + wn * 32;
+  return wn * 64 + f * 32;
+}
+
+__device__ __forceinline__ u32x2_t mx_pack4(float a, float b, float c, float d) {
+  u32x2_t v;
+  v[0] = pack_bf16x2(a, b);
+  v[1] = pack_bf16x2(c, d);
+  return v;
+}
+
+template <int NW>
+__device__ __forceinline__ int mx_scan(int v, int* s_wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int n = __shfl_up(v, d);
+    if (lane >= d) v += n;
+  }
+  if (lane == 63) s_wsum[wave] = v;
+  __syncthreads();
+  for (int w2 = 0; w2 < wave; ++w2) v += s_wsum[w2];
+  return v;
+}
+
+template <int EPI>
+__global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[MXN * kMxStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_stage[MXT / 64][2048];
+  __shared__ int s_lo[kMaxExperts + 1], s_pref[kMaxExperts + 1], s_wsum[8];
+  const int mlp = EPI == MXE_SWIGLU ? p.N / 2 : p.N;
+  const int tile_n = EPI == MXE_SWIGLU ? 128 : 256;
+  const int ntn = (mlp + tile_n - 1) / tile_n;
+  {  // ragged tile list: tiles of expert e = ceil(rows_e / 256) * ntn, prefix over experts
+    const int tid = threadIdx.x;
+    int tiles = 0;
+    if (tid <= p.E) s_lo[tid] = min(max(p.off[tid], 0), p.M);
+    if (tid < p.E) {
+      const int lo = min(max(p.off[tid], 0), p.M), hi = min(max(p.off[tid + 1], 0), p.M);
+      const int n = hi > lo ? hi - lo : 0;
+      tiles = ((n + 255) / 256) * ntn;
+    }
+    const int incl = mx_scan<MXT / 64>(tiles, s_wsum);
+    if (tid < p.E) s_pref[tid + 1] = incl;
+    if (tid == 0) s_pref[0] = 0;
+    __syncthreads();
+  }
+  const int total = s_pref[p.E];
+  const int tid = mx_opaque((int)threadIdx.x), lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1, h = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t lds0 = mx_lds_addr(smem);
+  const int nk = p.K / 64;
+  const int nslice_rows = p.M;  // rows of A's scale slices
+  int m0 = 0, m_end = 0, n0 = 0, e = 0;
+  const uint8_t* Bexp = p.B;
+  const uint8_t* Bsexp = p.Bs;
+  uint32_t a_off[2], b_off[2], s_off;
+  auto decode = [&](int64_t it) -> bool {
+    const int64_t tl = xcd_tile(it, blockIdx.x, gridDim.x);
+    if (tl >= total) return false;
+    const int tile = (int)tl;
+    int lo = 0, hi = p.E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_pref[mid] <= tile) lo = mid;
+      else hi = mid;
+    }
+    e = __builtin_amdgcn_readfirstlane(lo);
+    const int local = tile - s_pref[e];
+    const int nmt = (s_pref[e + 1] - s_pref[e]) / ntn;
+    const bool rows_fast = nmt >= 4;
+    const int mt = rows_fast ? local % nmt : local / ntn;
+    const int nt = rows_fast ? local / nmt : local % ntn;
+    m0 = __builtin_amdgcn_readfirstlane(s_lo[e] + mt * 256);
+    m_end = __builtin_amdgcn_readfirstlane(max(s_lo[e + 1], s_lo[e]));
+    n0 = __builtin_amdgcn_readfirstlane(nt * tile_n);
+    Bexp = mx_uniform(p.B + (int64_t)e * p.N * p.K);
+    Bsexp = mx_uniform(p.Bs + (int64_t)e * nk * p.N * 4);
+    // tile rows: block b = 2*wave + j holds rows 16b .. 16b+15; lane L -> row 16b + L/4, physical chunk L%4
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = (wave_u * 2 + j) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      const int r = min(m0 + row, m_end - 1);
+      a_off[j] = (uint32_t)r * (uint32_t)p.K + (uint32_t)c * 16u;
+      int n;
+      if (EPI == MXE_SWIGLU) {
+        const int cc = n0 + (row & 127);
+        n = cc < mlp ? (row < 128 ? cc : mlp + cc) : 0;
+      } else {
+        n = n0 + row < p.N ? n0 + row : p.N - 1;
+      }
+      b_off[j] = (uint32_t)n * (uint32_t)p.K + (uint32_t)c * 16u;
+    }
+    // scale rows: waves 0-3 copy A rows 64*wave + L, waves 4-7 B rows 64*(wave-4) + L
+    {
+      const int row = (wave_u & 3) * 64 + lane;
+      if (wave_u < 4) {
+        s_off = (uint32_t)min(m0 + row, m_end - 1) * 4u;
+      } else {
+        int n;
+        if (EPI == MXE_SWIGLU) {
+          const int cc = n0 + (row & 127);
+          n = cc < mlp ? (row < 128 ? cc : mlp + cc) : 0;
+        } else {
+          n = n0 + row < p.N ? n0 + row : p.N - 1;
+        }
+        s_off = (uint32_t)n * 4u;
+      }
+    }
+    return true;
+  };
+  auto issue_loads = [&](int kt) {
+    const uint32_t st = lds0 + (uint32_t)(kt & (MXN - 1)) * kMxStage;
+    const uint8_t* Ak = p.A + (int64_t)kt * 64;
+    const uint8_t* Bk = Bexp + (int64_t)kt * 64;
+    mx_g2lds16(Ak, a_off[0], st + wave_u * 2048);
+    mx_g2lds16(Ak, a_off[1], st + wave_u * 2048 + 1024);
+    mx_g2lds16(Bk, b_off[0], st + kMxOp + wave_u * 2048);
+    mx_g2lds16(Bk, b_off[1], st + kMxOp + wave_u * 2048 + 1024);
+    if (wave_u < 4) mx_g2lds4(p.As + (int64_t)kt * nslice_rows * 4, s_off, st + 2 * kMxOp + wave_u * 256);
+    else mx_g2lds4(Bsexp + (int64_t)kt * p.N * 4, s_off, st + 2 * kMxOp + kMxScl + (wave_u - 4) * 256);
+  };
+
+  if (!decode(0)) return;
+  for (int s = 0; s < MXN; ++s)
+    if (s < nk) issue_loads(s);
+  for (int64_t it = 0;; ++it) {
+    f32x16_t acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
+
+    mx_wait_all();  // this wave's loads of the first k-slices (and the last tile's stores) are done
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const uint8_t* stg = smem + (kt & (MXN - 1)) * kMxStage;
+      const uint8_t* As_t = stg;
+      const uint8_t* Bs_t = stg + kMxOp;
+      const uint8_t* Asc = stg + 2 * kMxOp;
+      const uint8_t* Bsc = Asc + kMxScl;
+      i32x8_t af[4], bf[2];
+      int sa[4], sb[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = wm * 128 + i * 32 + (lane & 31);
+        af[i] = mx_frag(As_t, row, h);
+        sa[i] = Asc[row * 4 + h];
+      }
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int row = mx_col<EPI>(wn, f) + (lane & 31);
+        bf[f] = mx_frag(Bs_t, row, h);
+        sb[f] = Bsc[row * 4 + h];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+          acc[i][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[f], af[i], acc[i][f], 0, 0, 0, sb[f], 0, sa[i]);
+      // k-slice kt+1 has landed; younger are the copies of k-slices kt+2 and kt+3, where they exist
+      if (kt + 3 < nk) mx_wait_10();
+      else if (kt + 2 < nk) mx_wait_5();
+      else mx_wait_all();
+      __syncthreads();  // every wave has read stage kt (its MFMAs consumed it); k-slice kt+1 is visible
+      if (kt + MXN < nk) issue_loads(kt + MXN);
+    }
+
+    const int cm0 = m0, cm_end = m_end, cn0 = n0;
+    const bool more = decode(it + 1);
+    if (more)
+      for (int s = 0; s < MXN; ++s)
+        if (s < nk) issue_loads(s);
+    // Epilogue through this wave's 2 KB staging area (as the bf16 grouped GEMM): lane holds rows
+    // m = tile row + lane%32 and, per register group q, columns 8q + 4*(lane/32) + 0..3 of a 32-wide block.
+    const int hh = lane >> 5;
+    uint8_t* const stg = s_stage[wave];
+    auto stg64 = [&](int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); };
+    auto stg128 = [&](int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); };
+    const int r = lane & 31;
+    if (EPI == MXE_NONE) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m0r = cm0 + wm * 128 + i * 32;
+        const int n0w = cn0 + wn * 64;
+        const int valid = min(8, (p.N - n0w) >> 3);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          if ((r >> 4) == hf) {
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<u32x2_t*>(stg + stg128(r - 16 * hf, f * 4 + q) + hh * 8) =
+                    mx_pack4(acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]);
+          }
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            const int rr = 8 * kk + (lane >> 3), c = lane & 7;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + stg128(rr, c));
+            const int m = m0r + 16 * hf + rr;
+            if (m < cm_end && c < valid) st16(p.C + (int64_t)m * p.N + n0w + c * 8, v);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m0r = cm0 + wm * 128 + i * 32;
+        const int c0 = cn0 + wn * 32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float a[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) a[u] = silu_f(acc[i][0][4 * q + u]) * acc[i][1][4 * q + u];
+          *reinterpret_cast<u32x2_t*>(stg + stg64(r, q) + hh * 8) = mx_pack4(a[0], a[1], a[2], a[3]);
+        }
+        const int valid = min(4, (mlp - c0) >> 3);
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int rr = 16 * k2 + (lane >> 2), c = lane & 3;
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + stg64(rr, c));
+          const int m = m0r + rr;
+          if (m < cm_end && c < valid) st16(p.C + (int64_t)m * mlp + c0 + c * 8, v);
+        }
+      }
+    }
+    if (!more) break;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_grouped_gemm_mx(int epilogue, const uint8_t* A, const uint8_t* As, const uint8_t* B,
+                                  const uint8_t* Bs, const int32_t* group_offsets, int E, int64_t M, int K, int N,
+                                  uint16_t* C, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  MxGemmP p{A, As, B, Bs, group_offsets, C, E, (int)M, K, N};
+  int g = device_cu_count();
+  g -= g % kNumXcd;
+  if (g < kNumXcd) g = kNumXcd;
+  if (epilogue == MXE_SWIGLU) mx_gemm_kernel<MXE_SWIGLU><<<dim3(g), dim3(MXT), 0, stream>>>(p);
+  else mx_gemm_kernel<MXE_NONE><<<dim3(g), dim3(MXT), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace moe

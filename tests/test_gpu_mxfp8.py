@@ -68,3 +68,77 @@ def test_mx_quantize_weight_bit_exact(E, K, N, seed):
         rc, rs = oracle.mx_quantize(wt[e])
         assert np.array_equal(codes[e].cpu().numpy(), rc)
         assert np.array_equal(scales[e].cpu().numpy(), _oracle_scales_to_device_layout(rs))
+
+
+# ---------------------------------------------------------------- grouped GEMM
+
+def _mx_step_bound(ac, as_, bc, bs, off, epi_width_N):
+    """Per output element: the hardware's in-step summation (up to 2^-10 of the step's largest |product|, 8x the
+    largest seen in probes; bounded here by max|a| * max|b| over the step) summed over the 64-element K steps,
+    plus fp32 accumulation across steps."""
+    A = oracle.mx_dequantize(ac, as_)
+    B = oracle.mx_dequantize(bc, bs)
+    M, K = A.shape
+    N = B.shape[1]
+    step = np.zeros((M, N))
+    mag = np.zeros((M, N))
+    for e in range(B.shape[0]):
+        lo, hi = off[e], off[e + 1]
+        if hi <= lo:
+            continue
+        a, b = np.abs(A[lo:hi]), np.abs(B[e])
+        mag[lo:hi] = a @ b.T
+        for s0 in range(0, K, 64):  # the step's largest product is at most max|a| * max|b| over the step
+            step[lo:hi] += np.outer(a[:, s0:s0 + 64].max(axis=1), b[:, s0:s0 + 64].max(axis=1))
+    return 2.0 ** -10 * step + (K // 64 + 2) * 2.0 ** -24 * mag, mag
+
+
+def _mx_case(M, K, N, E, seed, empty=()):
+    rng = np.random.default_rng(seed)
+    sizes = rng.multinomial(M, rng.dirichlet(np.ones(E) * 2)).astype(np.int64)
+    for e in empty:
+        sizes[(e + 1) % E] += sizes[e]
+        sizes[e] = 0
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    x = _bf16(rng.standard_normal((M, K)))
+    w = _bf16(rng.standard_normal((E, K, N)) * (1.0 / np.sqrt(K)))
+    return x, w, off
+
+
+@pytest.mark.parametrize("M,K,N,E,empty", [(700, 128, 512, 4, (2,)), (1500, 256, 768, 6, (0, 5)),
+                                           (300, 1024, 200, 3, ()), (64, 64, 64, 8, (1, 3, 6)),
+                                           (2600, 512, 1536, 2, ())])
+@pytest.mark.parametrize("epi", ["none", "swiglu"])
+def test_grouped_gemm_mx_matches_oracle(M, K, N, E, empty, epi):
+    if epi == "swiglu" and N % 16:
+        N += 8
+    x, w, off = _mx_case(M, K, N, E, M + K, empty)
+    ac, as_ = moe.mx_quantize_rows(x.to(DEV))
+    bc, bs = moe.mx_quantize_weight(w.to(DEV))
+    offd = torch.from_numpy(off).to(DEV)
+    got = moe.grouped_gemm_mx(ac, as_, bc, bs, offd, epilogue=epi).float().cpu().numpy().astype(np.float64)
+    # oracle layouts: scales [rows, K/32]
+    ac_n = ac.cpu().numpy()
+    as_n = np.stack([as_.cpu().numpy()[:, :, 0].T, as_.cpu().numpy()[:, :, 1].T], axis=2).reshape(M, K // 32)
+    bc_n = bc.cpu().numpy()
+    bs_d = bs.cpu().numpy()
+    bs_n = np.stack([np.transpose(bs_d[:, :, :, 0], (0, 2, 1)), np.transpose(bs_d[:, :, :, 1], (0, 2, 1))],
+                    axis=3).reshape(E, N, K // 32)
+    # the device scales are the oracle's (checked bit for bit above); use them in the reference
+    rc, rs = oracle.mx_quantize(bits(x))
+    assert np.array_equal(ac_n, rc) and np.array_equal(as_n, rs)
+    ref = oracle.mx_grouped_gemm_nt(ac_n, as_n, bc_n, bs_n, off, epi=1 if epi == "swiglu" else 0)
+    bound, mag = _mx_step_bound(ac_n, as_n, bc_n, bs_n, off, N)
+    if epi == "swiglu":
+        # SwiGLU of the two fp32 sums: propagate the bound of gate g and up u through silu(g) * u
+        Cg = oracle.mx_grouped_gemm_nt(ac_n, as_n, bc_n, bs_n, off)
+        g, u = Cg[:, : N // 2], Cg[:, N // 2:]
+        dg, du = bound[:, : N // 2], bound[:, N // 2:]
+        sg = 1.0 / (1.0 + np.exp(-g))
+        dsilu = np.abs(sg * (1.0 + g * (1.0 - sg)))  # |d silu/dg|
+        bound = np.abs(u) * (dsilu * dg + 1e-7 * np.abs(g)) + np.abs(g * sg) * du + dg * du + 1e-6 * np.abs(ref)
+    rows = np.zeros(M, bool)
+    rows[off[0]:off[-1]] = True
+    err = np.abs(got[rows] - ref[rows])
+    tol = bound[rows] + 2.0 ** -8 * np.abs(ref[rows]) + 1e-30  # + half a bf16 ulp of the output
+    assert np.all(err <= tol), (float((err / tol).max()), np.unravel_index(np.argmax(err / tol), err.shape))
