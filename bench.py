@@ -1,7 +1,7 @@
 """Benchmark of the MoE FFN layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gemma4_class]
-                    [--backward [--recompute-h]] [--no-cpu-baseline] [--stage-json PATH]
+                    [--backward [--recompute-h] | --mxfp8] [--no-cpu-baseline] [--stage-json PATH]
 
 One step = one pass of the whole forward hot path over one batch: route,
 permute, grouped GEMM 1 (prefused wi, SwiGLU epilogue), grouped GEMM 2 (wo),
@@ -18,6 +18,10 @@ rows and the fp32 gate/up values for the backward, and the step also runs
 the layer backward (combine-bwd, NT GEMM + SwiGLU-bwd, NT GEMM, permute-bwd,
 wgrad x2) and, where the router is learned, the router backward (logit
 gradients from dtopk_w, dWr, and dx += dlogits . Wr^T onto the layer's dx).
+With --mxfp8 the forward runs its grouped GEMMs on MXFP8 operands: the x rows
+are gathered through sorted_slot and quantized in one pass, the SwiGLU output
+is quantized before GEMM 2, and the expert weights are quantized beforehand
+(weight preparation, outside the timed step).
 With --recompute-h the forward keeps no fp32 gate/up values and the backward
 recomputes them with one more GEMM1 (the saved bytes are reported).
 """
@@ -34,6 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_FP32_MFMA_TFLOPS = 157.3  # dense fp32 matrix cores (the router's fma chains run on them)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -47,6 +52,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gemma4_class")
     ap.add_argument("--backward", action="store_true")
+    ap.add_argument("--mxfp8", action="store_true",
+                    help="forward with MXFP8 grouped GEMMs (activations quantized in the step, weights beforehand)")
     ap.add_argument("--recompute-h", action="store_true",
                     help="with --backward: the forward keeps no h and the backward recomputes it (full remat)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -117,8 +124,37 @@ def main():
     gather = not bwd
     rows = _lib.MoeGemmRows(P(sv["sorted_slot"]), S, k, None) if gather else None
 
+    mx = args.mxfp8 and not bwd
+    if mx:
+        # MXFP8 operands: weights quantized once (weight preparation, outside the timed step), activations in it
+        wiq, wis = moe.mx_quantize_weight(wi)       # [E, 2mlp, emb], [E, emb/64, 2mlp, 4]
+        woq, wos = moe.mx_quantize_weight(wo)       # [E, emb, mlp], [E, mlp/64, emb, 4]
+        xq = torch.empty((T, emb), dtype=torch.uint8, device=dev)   # token rows, read by GEMM 1 through sorted_slot
+        xqs = torch.empty((emb // 64, T, 4), dtype=torch.uint8, device=dev)
+        aq = torch.empty((S, mlp), dtype=torch.uint8, device=dev)
+        aqs = torch.empty((mlp // 64, S, 4), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
     def stage_calls():
         """The forward (and optional backward) as separate library calls, in moe_ffn_fwd order."""
+        if mx:
+            return [
+                ("route", lambda: L.moe_route(C.byref(shp), None if logits is not None else P(x), P(wr), P(bias),
+                                              P(logits), P(sv["topk_idx"]), P(sv["topk_w"]), st)),
+                ("permute", lambda: L.moe_permute(C.byref(shp), P(x), P(sv["topk_idx"]), P(sv["group_sizes"]),
+                                                  P(sv["group_offsets"]), P(sv["sorted_slot"]), P(sv["slot_row"]),
+                                                  None, P(pws), pws.numel(), st)),
+                # each token row quantized once; GEMM 1 reads its codes and scales in place through sorted_slot
+                ("quantize_x", lambda: L.moe_mx_quantize_rows(P(x), T, emb, None, 1, T, P(xq), P(xqs), st)),
+                ("gemm1_swiglu", lambda: L.moe_grouped_gemm_mx(1, P(xq), P(xqs), T, P(sv["sorted_slot"]), k, P(wiq),
+                                                               P(wis), P(sv["group_offsets"]), E, S, emb, 2 * mlp,
+                                                               P(sv["a"]), st)),
+                ("quantize_a", lambda: L.moe_mx_quantize_rows(P(sv["a"]), S, mlp, None, 1, S, P(aq), P(aqs), st)),
+                ("gemm2", lambda: L.moe_grouped_gemm_mx(0, P(aq), P(aqs), S, None, 1, P(woq), P(wos),
+                                                        P(sv["group_offsets"]), E, S, mlp, emb, P(sv["o"]), st)),
+                ("combine", lambda: L.moe_combine(C.byref(shp), P(sv["o"]), P(sv["slot_row"]), P(sv["topk_w"]),
+                                                  P(y), st)),
+            ]
         calls = [
             ("route", lambda: L.moe_route(C.byref(shp), None if logits is not None else P(x), P(wr), P(bias),
                                           P(logits), P(sv["topk_idx"]), P(sv["topk_w"]), st)),
@@ -175,7 +211,7 @@ def main():
 
     # the fused entry point over the same buffers, as a cross-check of the staged timing
     fused_ms = None
-    if not bwd:
+    if not bwd and not mx:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for _ in range(2):
             moe.ffn_fwd(x, wi, wo, k, wr=wr, bias=bias, logits=logits, workspace=ws, out=y)
@@ -197,6 +233,12 @@ def main():
     g2_bytes = S * mlp * 2 + e_nz * mlp * emb * 2 + S * emb * 2
     perm_bytes = 12 * S if gather else T * emb * 2 + S * emb * 2 + 12 * S
     comb_bytes = S * emb * 2 + 8 * S + T * emb * 2
+    gpeak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
+    if mx:  # fp8 operands plus one scale byte per 32 elements (a dword per 64 in the padded layout)
+        g1_bytes = T * emb * 17 // 16 + e_nz * emb * 2 * mlp * 17 // 16 + S * mlp * 2
+        g2_bytes = S * mlp * 17 // 16 + e_nz * mlp * emb * 17 // 16 + S * emb * 2
+        qx_bytes = T * emb * 2 + T * emb * 17 // 16      # x read once, token codes and scales written
+        qa_bytes = S * mlp * 2 + S * mlp * 17 // 16
     route_flop = 0.0 if logits is not None else 2.0 * T * emb * E
     route_bytes = (T * E * 4 if logits is not None else T * emb * 2 + emb * E * 4) + 8 * S
 
@@ -215,14 +257,20 @@ def main():
                         peak=PEAK_HBM_GBS, unit="GB/s", bytes=perm_bytes,
                         rows="index only; GEMM1 gathers the x rows" if gather else "rows copied to xs"),
         "gemm1_swiglu": dict(ms=stage_ms["gemm1_swiglu"], bound="mfma",
-                             achieved=tf(g1_flop, stage_ms["gemm1_swiglu"]), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                             achieved=tf(g1_flop, stage_ms["gemm1_swiglu"]), peak=gpeak, unit="TFLOP/s",
                              flop=g1_flop, bytes=g1_bytes, hbm_gbs=gb(g1_bytes, stage_ms["gemm1_swiglu"])),
         "gemm2": dict(ms=stage_ms["gemm2"], bound="mfma", achieved=tf(g2_flop, stage_ms["gemm2"]),
-                      peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", flop=g2_flop, bytes=g2_bytes,
+                      peak=gpeak, unit="TFLOP/s", flop=g2_flop, bytes=g2_bytes,
                       hbm_gbs=gb(g2_bytes, stage_ms["gemm2"])),
         "combine": dict(ms=stage_ms["combine"], bound="hbm", achieved=gb(comb_bytes, stage_ms["combine"]),
                         peak=PEAK_HBM_GBS, unit="GB/s", bytes=comb_bytes),
     }
+    if mx:
+        stages["permute"]["rows"] = "index only; GEMM1 gathers the quantized x rows"
+        stages["quantize_x"] = dict(ms=stage_ms["quantize_x"], bound="hbm", achieved=gb(qx_bytes, stage_ms["quantize_x"]),
+                                    peak=PEAK_HBM_GBS, unit="GB/s", bytes=qx_bytes)
+        stages["quantize_a"] = dict(ms=stage_ms["quantize_a"], bound="hbm", achieved=gb(qa_bytes, stage_ms["quantize_a"]),
+                                    peak=PEAK_HBM_GBS, unit="GB/s", bytes=qa_bytes)
     if bwd:
         stages["backward"] = dict(ms=stage_ms["backward"], bound="mfma",
                                   achieved=tf(12.0 * S * emb * mlp, stage_ms["backward"]), peak=PEAK_BF16_TFLOPS,
@@ -242,15 +290,16 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         try:
             tr = json.load(open(TRAFFIC_FILE))
-            ent = tr.get(args.workload, {}).get("gemm1_swiglu")
+            ent = None if mx else tr.get(args.workload, {}).get("gemm1_swiglu")
             if ent and ent.get("source_sha") == source_hash(GEMM_SRC):
                 traffic = ent["bytes_per_launch"]
         except Exception:
             traffic = None
     g1 = stages["gemm1_swiglu"]
-    roofline = {"bound": "mfma", "kernel": "gemm_kernel<NN,SWIGLU%s> (grouped GEMM 1 on prefused wi)"
-                % (", row gather" if gather else ""),
-                "achieved": round(g1["achieved"], 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+    kname = ("mx_gemm_kernel<SWIGLU> (MXFP8 grouped GEMM 1 on prefused wi)" if mx else
+             "gemm_kernel<NN,SWIGLU%s> (grouped GEMM 1 on prefused wi)" % (", row gather" if gather else ""))
+    roofline = {"bound": "mfma", "kernel": kname,
+                "achieved": round(g1["achieved"], 2), "peak": gpeak, "unit": "TFLOP/s",
                 "frac": round(g1["frac"], 4), "traffic": traffic,
                 "per_launch_flop": g1_flop, "avg_launch_ms": round(g1["ms"], 5)}
 
@@ -269,15 +318,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp8" if mx else "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "emb": emb, "mlp": mlp, "E": E, "k": k,
                    "pass": "forward+backward" if bwd else "forward", "router_backward": router_bwd,
-                   "recompute_h": remat,
+                   "recompute_h": remat, "gemm_operands": "mxfp8 (e4m3, e8m0 per 32)" if mx else "bf16",
                    "parallelism": "none (1 GPU)"},
         "layer_tflops": round(tf(fwd_flop * (3 if bwd else 1), ms_step), 2),
         "gemm_stage_tflops": round(tf(fwd_flop, gemm_ms), 2),
-        "gemm_stage_frac": round(tf(fwd_flop, gemm_ms) / PEAK_BF16_TFLOPS, 4),
+        "gemm_stage_frac": round(tf(fwd_flop, gemm_ms) / gpeak, 4),
         "fused_entry_ms": None if fused_ms is None else round(fused_ms, 4),
         # activations kept from the forward for the backward (the saved set)
         "saved_bytes": sum(v.numel() * v.element_size() for v in saved.values() if v is not None) if bwd else None,

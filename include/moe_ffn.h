@@ -288,7 +288,11 @@ int moe_mx_quantize_weight(const moe_bf16_t* w, int32_t E, int32_t K, int32_t N,
  *  Optimize MoE block", Flowchart: grouped FC1 quantize and GEMM), on the
  *  block-scaled fp8 matrix cores: C[r, :] = A[r, :] . B[e]^T for the rows r
  *  of group e, A and B being E4M3 codes times their 32-element blocks' E8M0
- *  scales. A: codes [M, K] and scales [K/64][M][4] (moe_mx_quantize_rows);
+ *  scales. A: codes [a_rows, K] and scales [K/64][a_rows][4]
+ *  (moe_mx_quantize_rows); row r of the product reads A row
+ *  row_slot[r] / slot_div (clamped into [0, a_rows)) when row_slot is given
+ *  (token rows quantized once, read in place through sorted_slot with
+ *  slot_div = k), else A row r, and then a_rows must equal M.
  *  B: codes [E, N, K] and scales [E][K/64][N][4] (moe_mx_quantize_weight).
  *  epilogue MOE_EPI_NONE: C [M, N] bf16; MOE_EPI_SWIGLU: B is a prefused
  *  [gate | up] weight and C [M, N/2] bf16 is silu(gate) * up, computed in
@@ -296,11 +300,12 @@ int moe_mx_quantize_weight(const moe_bf16_t* w, int32_t E, int32_t K, int32_t N,
  *  within a step the hardware sums the scaled products to a precision fixed
  *  relative to the largest of them. Rows of C outside [group_offsets[0],
  *  group_offsets[E]) are not written. K % 64 == 0, N % 8 == 0 (N % 16 for
- *  SWIGLU), E <= 256, M*K and N*K below 2^32.
+ *  SWIGLU), E <= 256, a_rows*K and N*K below 2^32.
  */
-int moe_grouped_gemm_mx(int32_t epilogue, const uint8_t* A, const uint8_t* A_scales, const uint8_t* B,
-                        const uint8_t* B_scales, const int32_t* group_offsets, int32_t E, int64_t M, int32_t K,
-                        int32_t N, moe_bf16_t* C, moe_stream_t stream);
+int moe_grouped_gemm_mx(int32_t epilogue, const uint8_t* A, const uint8_t* A_scales, int64_t a_rows,
+                        const int32_t* row_slot, int32_t slot_div, const uint8_t* B, const uint8_t* B_scales,
+                        const int32_t* group_offsets, int32_t E, int64_t M, int32_t K, int32_t N, moe_bf16_t* C,
+                        moe_stream_t stream);
 
 /*
  * moe_ffn_fwd -- the whole MoE FFN forward: route, permute, grouped GEMM on

@@ -326,20 +326,25 @@ def mx_quantize_weight(w: torch.Tensor):
 
 
 def grouped_gemm_mx(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor, b_scales: torch.Tensor,
-                    group_offsets: torch.Tensor, epilogue: str = "none", out: torch.Tensor | None = None):
-    """Grouped GEMM on MXFP8 operands (see moe_grouped_gemm_mx): a_codes [M, K] with a_scales [K/64, M, 4] from
-    mx_quantize_rows, b_codes [E, N, K] with b_scales [E, K/64, N, 4] from mx_quantize_weight. Returns C [M, N]
-    bf16, or [M, N/2] for epilogue "swiglu"."""
+                    group_offsets: torch.Tensor, epilogue: str = "none", out: torch.Tensor | None = None,
+                    row_slot: torch.Tensor | None = None, slot_div: int = 1, rows: int | None = None):
+    """Grouped GEMM on MXFP8 operands (see moe_grouped_gemm_mx): a_codes [a_rows, K] with a_scales
+    [K/64, a_rows, 4] from mx_quantize_rows, b_codes [E, N, K] with b_scales [E, K/64, N, 4] from
+    mx_quantize_weight. With row_slot, output row r reads A row row_slot[r] // slot_div (rows = number of
+    output rows, default row_slot's length). Returns C [M, N] bf16, or [M, N/2] for epilogue "swiglu"."""
     dev = a_codes.device
     for t, n in ((a_codes, "a_codes"), (a_scales, "a_scales"), (b_codes, "b_codes"), (b_scales, "b_scales")):
         _need(t, n, torch.uint8, dev)
     _need(group_offsets, "group_offsets", torch.int32, dev)
-    M, K = a_codes.shape
+    _need(row_slot, "row_slot", torch.int32, dev)
+    a_rows, K = a_codes.shape
+    M = a_rows if row_slot is None else (rows if rows is not None else row_slot.numel())
     E, N, _ = b_codes.shape
     epi = {"none": 0, "swiglu": 1}[epilogue]
     width = N if epi == 0 else N // 2
     C_ = out if out is not None else torch.empty((M, width), dtype=torch.bfloat16, device=dev)
-    _lib.check(_lib.lib().moe_grouped_gemm_mx(epi, _ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales),
-                                              _ptr(group_offsets), E, M, K, N, _ptr(C_), _stream(dev)),
+    _lib.check(_lib.lib().moe_grouped_gemm_mx(epi, _ptr(a_codes), _ptr(a_scales), a_rows, _ptr(row_slot), slot_div,
+                                              _ptr(b_codes), _ptr(b_scales), _ptr(group_offsets), E, M, K, N,
+                                              _ptr(C_), _stream(dev)),
                "moe_grouped_gemm_mx")
     return C_

@@ -373,9 +373,10 @@ int moe_mx_quantize_weight(const moe_bf16_t* w, int32_t E, int32_t K, int32_t N,
                     "moe_mx_quantize_weight");
 }
 
-int moe_grouped_gemm_mx(int32_t epilogue, const uint8_t* A, const uint8_t* A_scales, const uint8_t* B,
-                        const uint8_t* B_scales, const int32_t* group_offsets, int32_t E, int64_t M, int32_t K,
-                        int32_t N, moe_bf16_t* C, moe_stream_t stream) {
+int moe_grouped_gemm_mx(int32_t epilogue, const uint8_t* A, const uint8_t* A_scales, int64_t a_rows,
+                        const int32_t* row_slot, int32_t slot_div, const uint8_t* B, const uint8_t* B_scales,
+                        const int32_t* group_offsets, int32_t E, int64_t M, int32_t K, int32_t N, moe_bf16_t* C,
+                        moe_stream_t stream) {
   g_detail[0] = 0;
   if (epilogue != MOE_EPI_NONE && epilogue != MOE_EPI_SWIGLU)
     return fail(MOE_ERR_UNSUPPORTED, "the MXFP8 GEMM has the NONE and SWIGLU epilogues");
@@ -384,8 +385,10 @@ int moe_grouped_gemm_mx(int32_t epilogue, const uint8_t* A, const uint8_t* A_sca
   if (K % 64) return fail(MOE_ERR_UNSUPPORTED, "K (%d) is not a multiple of 64", K);
   if (N % 8) return fail(MOE_ERR_UNSUPPORTED, "N (%d) is not a multiple of 8", N);
   if (epilogue == MOE_EPI_SWIGLU && N % 16) return fail(MOE_ERR_UNSUPPORTED, "SWIGLU needs (N/2) %% 8 == 0");
-  if (M * K >= (int64_t(1) << 32) || (int64_t)N * K >= (int64_t(1) << 32))
-    return fail(MOE_ERR_UNSUPPORTED, "M*K and N*K must be below 2^32 bytes");
+  if (!row_slot && a_rows != M) return fail(MOE_ERR_SHAPE, "without row_slot, a_rows must equal M");
+  if (row_slot && (a_rows <= 0 || slot_div <= 0)) return fail(MOE_ERR_SHAPE, "row gather needs a_rows, slot_div > 0");
+  if (a_rows * K >= (int64_t(1) << 32) || (int64_t)N * K >= (int64_t(1) << 32))
+    return fail(MOE_ERR_UNSUPPORTED, "a_rows*K and N*K must be below 2^32 bytes");
   if (M >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "M >= 2^31");
   const int64_t ntn = epilogue == MOE_EPI_SWIGLU ? (N / 2 + 127) / 128 : (N + 255) / 256;
   if ((M / 256 + E) * ntn >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "tile count too large");
@@ -396,9 +399,10 @@ int moe_grouped_gemm_mx(int32_t epilogue, const uint8_t* A, const uint8_t* A_sca
     NEED(A);
     NEED(A_scales);
     NEED(C);
+    MAYBE(row_slot);
   }
-  return hip_status(moe::launch_grouped_gemm_mx(epilogue, A, A_scales, B, B_scales, group_offsets, E, M, K, N, C,
-                                                 (hipStream_t)stream),
+  return hip_status(moe::launch_grouped_gemm_mx(epilogue, A, A_scales, a_rows, row_slot, row_slot ? slot_div : 1, B,
+                                                 B_scales, group_offsets, E, M, K, N, C, (hipStream_t)stream),
                     "moe_grouped_gemm_mx");
 }
 

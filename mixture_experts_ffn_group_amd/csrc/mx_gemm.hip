@@ -6,6 +6,8 @@
 // block (the layouts of mxfp8.hip: codes K-contiguous, scales one dword per
 // row and 64-element slice). Epilogues: none (C [M, N] bf16) or SwiGLU on a
 // prefused [gate | up] weight (C [M, N/2] bf16, gate = columns [0, N/2)).
+// With a slot index the A rows (codes and scales) are read in place through
+// it, so token rows quantized once serve all k of their expert rows.
 //
 // v_mfma_scale_f32_32x32x64_f8f6f4 multiplies 32 x 64 by 64 x 32 with one
 // scale byte per lane and 32-element block. Its operand layout (pinned on the
@@ -40,13 +42,15 @@ constexpr int kMxStage = 2 * kMxOp + 2 * kMxScl;  // 34 KB
 enum { MXE_NONE = 0, MXE_SWIGLU = 1 };
 
 struct MxGemmP {
-  const uint8_t* A;   // codes [M][K]
-  const uint8_t* As;  // scales [K/64][M][4]
+  const uint8_t* A;   // codes [a_rows][K]
+  const uint8_t* As;  // scales [K/64][a_rows][4]
+  const int32_t* row_slot;  // optional: A row of output row r is row_slot[r] / slot_div
   const uint8_t* B;   // codes [E][N][K]
   const uint8_t* Bs;  // scales [E][K/64][N][4]
   const int32_t* off;
   uint16_t* C;
   int E, M, K, N;
+  int a_rows, slot_div;
 };
 
 __device__ __forceinline__ void mx_g2lds16(const void* sbase, uint32_t voff, uint32_t lds) {
@@ -109,7 +113,7 @@ __device__ __forceinline__ int mx_scan(int v, int* s_wsum) {
   return v;
 }
 
-template <int EPI>
+template <int EPI, bool GATHER>
 __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[MXN * kMxStage];
   __shared__ __attribute__((aligned(16))) uint8_t s_stage[MXT / 64][2048];
@@ -137,7 +141,13 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds0 = mx_lds_addr(smem);
   const int nk = p.K / 64;
-  const int nslice_rows = p.M;  // rows of A's scale slices
+  const int nslice_rows = p.a_rows;  // rows of A's scale slices
+  // A row of output row r: the token row through the slot index, or r itself
+  auto a_row = [&](int r) -> int {
+    if (!GATHER) return r;
+    const int t = p.row_slot[r] / p.slot_div;
+    return t < 0 ? 0 : (t >= p.a_rows ? p.a_rows - 1 : t);
+  };
   int m0 = 0, m_end = 0, n0 = 0, e = 0;
   const uint8_t* Bexp = p.B;
   const uint8_t* Bsexp = p.Bs;
@@ -168,7 +178,7 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
     for (int j = 0; j < 2; ++j) {
       const int row = (wave_u * 2 + j) * 16 + (lane >> 2);
       const int c = (lane & 3) ^ ((row >> 2) & 3);
-      const int r = min(m0 + row, m_end - 1);
+      const int r = a_row(min(m0 + row, m_end - 1));
       a_off[j] = (uint32_t)r * (uint32_t)p.K + (uint32_t)c * 16u;
       int n;
       if (EPI == MXE_SWIGLU) {
@@ -183,7 +193,7 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
     {
       const int row = (wave_u & 3) * 64 + lane;
       if (wave_u < 4) {
-        s_off = (uint32_t)min(m0 + row, m_end - 1) * 4u;
+        s_off = (uint32_t)a_row(min(m0 + row, m_end - 1)) * 4u;
       } else {
         int n;
         if (EPI == MXE_SWIGLU) {
@@ -321,16 +331,23 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
 
 }  // namespace
 
-hipError_t launch_grouped_gemm_mx(int epilogue, const uint8_t* A, const uint8_t* As, const uint8_t* B,
-                                  const uint8_t* Bs, const int32_t* group_offsets, int E, int64_t M, int K, int N,
-                                  uint16_t* C, hipStream_t stream) {
+hipError_t launch_grouped_gemm_mx(int epilogue, const uint8_t* A, const uint8_t* As, int64_t a_rows,
+                                  const int32_t* row_slot, int slot_div, const uint8_t* B, const uint8_t* Bs,
+                                  const int32_t* group_offsets, int E, int64_t M, int K, int N, uint16_t* C,
+                                  hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  MxGemmP p{A, As, B, Bs, group_offsets, C, E, (int)M, K, N};
+  MxGemmP p{A, As, row_slot, B, Bs, group_offsets, C, E, (int)M, K, N, (int)a_rows, slot_div};
   int g = device_cu_count();
   g -= g % kNumXcd;
   if (g < kNumXcd) g = kNumXcd;
-  if (epilogue == MXE_SWIGLU) mx_gemm_kernel<MXE_SWIGLU><<<dim3(g), dim3(MXT), 0, stream>>>(p);
-  else mx_gemm_kernel<MXE_NONE><<<dim3(g), dim3(MXT), 0, stream>>>(p);
+  const dim3 grid(g), block(MXT);
+  if (epilogue == MXE_SWIGLU) {
+    if (row_slot) mx_gemm_kernel<MXE_SWIGLU, true><<<grid, block, 0, stream>>>(p);
+    else mx_gemm_kernel<MXE_SWIGLU, false><<<grid, block, 0, stream>>>(p);
+  } else {
+    if (row_slot) mx_gemm_kernel<MXE_NONE, true><<<grid, block, 0, stream>>>(p);
+    else mx_gemm_kernel<MXE_NONE, false><<<grid, block, 0, stream>>>(p);
+  }
   return hipGetLastError();
 }
 

@@ -142,3 +142,23 @@ def test_grouped_gemm_mx_matches_oracle(M, K, N, E, empty, epi):
     err = np.abs(got[rows] - ref[rows])
     tol = bound[rows] + 2.0 ** -8 * np.abs(ref[rows]) + 1e-30  # + half a bf16 ulp of the output
     assert np.all(err <= tol), (float((err / tol).max()), np.unravel_index(np.argmax(err / tol), err.shape))
+
+
+@pytest.mark.parametrize("epi", ["none", "swiglu"])
+def test_grouped_gemm_mx_row_gather_equals_sorted_rows_bitwise(epi):
+    """Token rows quantized once and read through sorted_slot give the same bits as the expert-sorted rows
+    quantized one by one (the same codes and scales reach the same kernel arithmetic)."""
+    T, K, N, E, k = 500, 256, 320, 6, 3
+    rng = np.random.default_rng(17)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    gs, off, ss, sr = oracle.dispatch(idx, E)
+    x = _bf16(rng.standard_normal((T, K)))
+    w = _bf16(rng.standard_normal((E, K, N)) * (1.0 / np.sqrt(K)))
+    bc, bs = moe.mx_quantize_weight(w.to(DEV))
+    offd = torch.from_numpy(off.astype(np.int32)).to(DEV)
+    ssd = torch.from_numpy(ss.astype(np.int32)).to(DEV)
+    tq, ts = moe.mx_quantize_rows(x.to(DEV))                        # T token rows
+    got = moe.grouped_gemm_mx(tq, ts, bc, bs, offd, epilogue=epi, row_slot=ssd, slot_div=k)
+    sq, sqs = moe.mx_quantize_rows(x.to(DEV), ssd, k)               # T*k sorted rows
+    ref = moe.grouped_gemm_mx(sq, sqs, bc, bs, offd, epilogue=epi)
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
