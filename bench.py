@@ -18,10 +18,11 @@ rows and the fp32 gate/up values for the backward, and the step also runs
 the layer backward (combine-bwd, NT GEMM + SwiGLU-bwd, NT GEMM, permute-bwd,
 wgrad x2) and, where the router is learned, the router backward (logit
 gradients from dtopk_w, dWr, and dx += dlogits . Wr^T onto the layer's dx).
-With --mxfp8 the forward runs its grouped GEMMs on MXFP8 operands: the x rows
-are gathered through sorted_slot and quantized in one pass, the SwiGLU output
-is quantized before GEMM 2, and the expert weights are quantized beforehand
-(weight preparation, outside the timed step).
+With --mxfp8 the forward runs its grouped GEMMs on MXFP8 operands: each token
+row of x is quantized once and GEMM 1 reads the codes through sorted_slot,
+GEMM 1's SwiGLU epilogue writes its output as MXFP8 for GEMM 2, and the
+expert weights are quantized beforehand (weight preparation, outside the
+timed step).
 With --recompute-h the forward keeps no fp32 gate/up values and the backward
 recomputes them with one more GEMM1 (the saved bytes are reported).
 """
@@ -146,12 +147,13 @@ def main():
                                                   None, P(pws), pws.numel(), st)),
                 # each token row quantized once; GEMM 1 reads its codes and scales in place through sorted_slot
                 ("quantize_x", lambda: L.moe_mx_quantize_rows(P(x), T, emb, None, 1, T, P(xq), P(xqs), st)),
+                # GEMM 1 writes its SwiGLU output as MXFP8 directly (the operand of GEMM 2); no bf16 copy
                 ("gemm1_swiglu", lambda: L.moe_grouped_gemm_mx(1, P(xq), P(xqs), T, P(sv["sorted_slot"]), k, P(wiq),
                                                                P(wis), P(sv["group_offsets"]), E, S, emb, 2 * mlp,
-                                                               P(sv["a"]), st)),
-                ("quantize_a", lambda: L.moe_mx_quantize_rows(P(sv["a"]), S, mlp, None, 1, S, P(aq), P(aqs), st)),
+                                                               None, P(aq), P(aqs), st)),
                 ("gemm2", lambda: L.moe_grouped_gemm_mx(0, P(aq), P(aqs), S, None, 1, P(woq), P(wos),
-                                                        P(sv["group_offsets"]), E, S, mlp, emb, P(sv["o"]), st)),
+                                                        P(sv["group_offsets"]), E, S, mlp, emb, P(sv["o"]), None,
+                                                        None, st)),
                 ("combine", lambda: L.moe_combine(C.byref(shp), P(sv["o"]), P(sv["slot_row"]), P(sv["topk_w"]),
                                                   P(y), st)),
             ]
@@ -235,10 +237,9 @@ def main():
     comb_bytes = S * emb * 2 + 8 * S + T * emb * 2
     gpeak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
     if mx:  # fp8 operands plus one scale byte per 32 elements (a dword per 64 in the padded layout)
-        g1_bytes = T * emb * 17 // 16 + e_nz * emb * 2 * mlp * 17 // 16 + S * mlp * 2
+        g1_bytes = T * emb * 17 // 16 + e_nz * emb * 2 * mlp * 17 // 16 + S * mlp * 17 // 16
         g2_bytes = S * mlp * 17 // 16 + e_nz * mlp * emb * 17 // 16 + S * emb * 2
         qx_bytes = T * emb * 2 + T * emb * 17 // 16      # x read once, token codes and scales written
-        qa_bytes = S * mlp * 2 + S * mlp * 17 // 16
     route_flop = 0.0 if logits is not None else 2.0 * T * emb * E
     route_bytes = (T * E * 4 if logits is not None else T * emb * 2 + emb * E * 4) + 8 * S
 
@@ -269,8 +270,6 @@ def main():
         stages["permute"]["rows"] = "index only; GEMM1 gathers the quantized x rows"
         stages["quantize_x"] = dict(ms=stage_ms["quantize_x"], bound="hbm", achieved=gb(qx_bytes, stage_ms["quantize_x"]),
                                     peak=PEAK_HBM_GBS, unit="GB/s", bytes=qx_bytes)
-        stages["quantize_a"] = dict(ms=stage_ms["quantize_a"], bound="hbm", achieved=gb(qa_bytes, stage_ms["quantize_a"]),
-                                    peak=PEAK_HBM_GBS, unit="GB/s", bytes=qa_bytes)
     if bwd:
         stages["backward"] = dict(ms=stage_ms["backward"], bound="mfma",
                                   achieved=tf(12.0 * S * emb * mlp, stage_ms["backward"]), peak=PEAK_BF16_TFLOPS,

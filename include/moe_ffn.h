@@ -296,7 +296,12 @@ int moe_mx_quantize_weight(const moe_bf16_t* w, int32_t E, int32_t K, int32_t N,
  *  B: codes [E, N, K] and scales [E][K/64][N][4] (moe_mx_quantize_weight).
  *  epilogue MOE_EPI_NONE: C [M, N] bf16; MOE_EPI_SWIGLU: B is a prefused
  *  [gate | up] weight and C [M, N/2] bf16 is silu(gate) * up, computed in
- *  fp32 and rounded once. Accumulation is fp32 across 64-element K steps;
+ *  fp32 and rounded once. With SWIGLU the output can also (or instead: C may
+ *  then be NULL) be written as MXFP8, C_codes [M, N/2] and C_scales
+ *  [N/128][M][4], the operand of the next MXFP8 GEMM: the bf16-rounded values
+ *  quantized as moe_mx_quantize_rows would (bytes 2 and 3 of the scale dwords
+ *  are left unwritten; (N/2) % 64 == 0). C_codes and C_scales are both given
+ *  or both NULL. Accumulation is fp32 across 64-element K steps;
  *  within a step the hardware sums the scaled products to a precision fixed
  *  relative to the largest of them. Rows of C outside [group_offsets[0],
  *  group_offsets[E]) are not written. K % 64 == 0, N % 8 == 0 (N % 16 for
@@ -305,7 +310,7 @@ int moe_mx_quantize_weight(const moe_bf16_t* w, int32_t E, int32_t K, int32_t N,
 int moe_grouped_gemm_mx(int32_t epilogue, const uint8_t* A, const uint8_t* A_scales, int64_t a_rows,
                         const int32_t* row_slot, int32_t slot_div, const uint8_t* B, const uint8_t* B_scales,
                         const int32_t* group_offsets, int32_t E, int64_t M, int32_t K, int32_t N, moe_bf16_t* C,
-                        moe_stream_t stream);
+                        uint8_t* C_codes, uint8_t* C_scales, moe_stream_t stream);
 
 /*
  * moe_ffn_fwd -- the whole MoE FFN forward: route, permute, grouped GEMM on

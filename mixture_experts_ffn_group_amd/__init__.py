@@ -327,11 +327,13 @@ def mx_quantize_weight(w: torch.Tensor):
 
 def grouped_gemm_mx(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor, b_scales: torch.Tensor,
                     group_offsets: torch.Tensor, epilogue: str = "none", out: torch.Tensor | None = None,
-                    row_slot: torch.Tensor | None = None, slot_div: int = 1, rows: int | None = None):
+                    row_slot: torch.Tensor | None = None, slot_div: int = 1, rows: int | None = None,
+                    mx_out: bool = False, bf16_out: bool = True):
     """Grouped GEMM on MXFP8 operands (see moe_grouped_gemm_mx): a_codes [a_rows, K] with a_scales
     [K/64, a_rows, 4] from mx_quantize_rows, b_codes [E, N, K] with b_scales [E, K/64, N, 4] from
     mx_quantize_weight. With row_slot, output row r reads A row row_slot[r] // slot_div (rows = number of
-    output rows, default row_slot's length). Returns C [M, N] bf16, or [M, N/2] for epilogue "swiglu"."""
+    output rows, default row_slot's length). Returns C [M, N] bf16, or [M, N/2] for epilogue "swiglu"; with
+    mx_out (SwiGLU only) returns (C or None, codes [M, N/2], scales [N/128, M, 4]) of the MXFP8 output."""
     dev = a_codes.device
     for t, n in ((a_codes, "a_codes"), (a_scales, "a_scales"), (b_codes, "b_codes"), (b_scales, "b_scales")):
         _need(t, n, torch.uint8, dev)
@@ -342,9 +344,12 @@ def grouped_gemm_mx(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torc
     E, N, _ = b_codes.shape
     epi = {"none": 0, "swiglu": 1}[epilogue]
     width = N if epi == 0 else N // 2
-    C_ = out if out is not None else torch.empty((M, width), dtype=torch.bfloat16, device=dev)
+    C_ = (out if out is not None else torch.empty((M, width), dtype=torch.bfloat16, device=dev)) if bf16_out \
+        else None
+    cq = torch.empty((M, width), dtype=torch.uint8, device=dev) if mx_out else None
+    cqs = torch.zeros((width // 64, M, 4), dtype=torch.uint8, device=dev) if mx_out else None
     _lib.check(_lib.lib().moe_grouped_gemm_mx(epi, _ptr(a_codes), _ptr(a_scales), a_rows, _ptr(row_slot), slot_div,
                                               _ptr(b_codes), _ptr(b_scales), _ptr(group_offsets), E, M, K, N,
-                                              _ptr(C_), _stream(dev)),
+                                              _ptr(C_), _ptr(cq), _ptr(cqs), _stream(dev)),
                "moe_grouped_gemm_mx")
-    return C_
+    return (C_, cq, cqs) if mx_out else C_

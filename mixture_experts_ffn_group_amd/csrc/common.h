@@ -48,4 +48,31 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t it, int w, int G) {
   return it * G + (int64_t)(w % kNumXcd) * (G / kNumXcd) + w / kNumXcd;
 }
 
+// MXFP8 element and scale encodings (OCP microscaling, E4M3 elements with an
+// E8M0 scale per 32-element block; see mxfp8.hip).
+// E8M0 code of a block whose largest magnitude has fp32 bits amax_bits:
+// 2^(floor(log2(amax)) - 8) biased by 127, clamped to [0, 254], 0 for zero.
+__device__ __forceinline__ int mx_e8m0_code(uint32_t amax_bits) {
+  if (amax_bits == 0) return 0;
+  const int e = (int)(amax_bits >> 23) - 127;  // floor(log2(amax)); fp32 subnormals give -127 (clamped below)
+  const int c = e - 8 + 127;
+  return c < 0 ? 0 : (c > 254 ? 254 : c);
+}
+// E4M3 code of v (finite, below 512 in magnitude): nearest value, ties to an
+// even mantissa, magnitudes past 448 saturating, the sign kept.
+__device__ __forceinline__ uint32_t mx_e4m3_code(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sgn = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a >= 0x43e00000u) return sgn | 0x7eu;  // |v| >= 448
+  if (a < 0x3c800000u) {                     // |v| < 2^-6: multiples of 2^-9, nearest-even
+    const uint32_t m = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);  // 0..8; 8 is code 0x08
+    return sgn | m;
+  }
+  // keep 3 mantissa bits, round half to even on bit 20; a carry moves into the exponent
+  const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;  // (biased fp32 exponent << 3) | mantissa
+  const uint32_t c = r - ((127u - 7u) << 3);
+  return sgn | (c > 0x7eu ? 0x7eu : c);
+}
+
 }  // namespace moe

@@ -46,7 +46,7 @@ hipError_t launch_mx_quantize_weight(const uint16_t* w, int E, int K, int N, uin
 hipError_t launch_grouped_gemm_mx(int epilogue, const uint8_t* A, const uint8_t* As, int64_t a_rows,
                                   const int32_t* row_slot, int slot_div, const uint8_t* B, const uint8_t* Bs,
                                   const int32_t* group_offsets, int E, int64_t M, int K, int N, uint16_t* C,
-                                  hipStream_t stream);
+                                  uint8_t* Cq, uint8_t* Cqs, hipStream_t stream);
 hipError_t launch_route_bwd(int64_t T, int emb, int E, int k, const uint16_t* x, const float* wr,
                             const int32_t* topk_idx, const float* topk_w, const float* dtopk_w,
                             const int32_t* sorted_slot, const int32_t* group_offsets, float* dwr, float* dbias,

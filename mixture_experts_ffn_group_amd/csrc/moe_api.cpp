@@ -376,8 +376,11 @@ int moe_mx_quantize_weight(const moe_bf16_t* w, int32_t E, int32_t K, int32_t N,
 int moe_grouped_gemm_mx(int32_t epilogue, const uint8_t* A, const uint8_t* A_scales, int64_t a_rows,
                         const int32_t* row_slot, int32_t slot_div, const uint8_t* B, const uint8_t* B_scales,
                         const int32_t* group_offsets, int32_t E, int64_t M, int32_t K, int32_t N, moe_bf16_t* C,
-                        moe_stream_t stream) {
+                        uint8_t* C_codes, uint8_t* C_scales, moe_stream_t stream) {
   g_detail[0] = 0;
+  if ((C_codes != nullptr) != (C_scales != nullptr)) return fail(MOE_ERR_NULL, "C_codes and C_scales go together");
+  if (C_codes && epilogue != MOE_EPI_SWIGLU) return fail(MOE_ERR_UNSUPPORTED, "an MXFP8 output needs SWIGLU");
+  if (C_codes && (N / 2) % 64) return fail(MOE_ERR_UNSUPPORTED, "an MXFP8 output needs (N/2) %% 64 == 0");
   if (epilogue != MOE_EPI_NONE && epilogue != MOE_EPI_SWIGLU)
     return fail(MOE_ERR_UNSUPPORTED, "the MXFP8 GEMM has the NONE and SWIGLU epilogues");
   if (M < 0 || K <= 0 || N <= 0 || E <= 0) return fail(MOE_ERR_SHAPE, "need M >= 0 and K, N, E > 0");
@@ -398,11 +401,18 @@ int moe_grouped_gemm_mx(int32_t epilogue, const uint8_t* A, const uint8_t* A_sca
   if (M > 0) {
     NEED(A);
     NEED(A_scales);
-    NEED(C);
     MAYBE(row_slot);
+    if (C_codes) {
+      MAYBE(C);
+      NEED(C_codes);
+      NEED(C_scales);
+    } else {
+      NEED(C);
+    }
   }
   return hip_status(moe::launch_grouped_gemm_mx(epilogue, A, A_scales, a_rows, row_slot, row_slot ? slot_div : 1, B,
-                                                 B_scales, group_offsets, E, M, K, N, C, (hipStream_t)stream),
+                                                 B_scales, group_offsets, E, M, K, N, C, C_codes, C_scales,
+                                                 (hipStream_t)stream),
                     "moe_grouped_gemm_mx");
 }
 

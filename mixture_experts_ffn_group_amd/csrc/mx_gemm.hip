@@ -7,7 +7,9 @@
 // row and 64-element slice). Epilogues: none (C [M, N] bf16) or SwiGLU on a
 // prefused [gate | up] weight (C [M, N/2] bf16, gate = columns [0, N/2)).
 // With a slot index the A rows (codes and scales) are read in place through
-// it, so token rows quantized once serve all k of their expert rows.
+// it, so token rows quantized once serve all k of their expert rows. The
+// SwiGLU epilogue can also write its output as MXFP8 (the operand of the next
+// GEMM): each wave's 32 output columns are one block of each row.
 //
 // v_mfma_scale_f32_32x32x64_f8f6f4 multiplies 32 x 64 by 64 x 32 with one
 // scale byte per lane and 32-element block. Its operand layout (pinned on the
@@ -48,7 +50,9 @@ struct MxGemmP {
   const uint8_t* B;   // codes [E][N][K]
   const uint8_t* Bs;  // scales [E][K/64][N][4]
   const int32_t* off;
-  uint16_t* C;
+  uint16_t* C;    // bf16 output, or NULL
+  uint8_t* Cq;    // SwiGLU only: MXFP8 codes of the output [M][N/2], or NULL
+  uint8_t* Cqs;   // and its scales [N/128][M][4] (bytes 0 and 1 of each dword)
   int E, M, K, N;
   int a_rows, slot_div;
 };
@@ -308,20 +312,57 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
       for (int i = 0; i < 4; ++i) {
         const int m0r = cm0 + wm * 128 + i * 32;
         const int c0 = cn0 + wn * 32;
+        u32x2_t pk[4];  // this lane's 16 outputs, rounded to bf16: columns 8q + 4*hh + 0..3
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float a[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u) a[u] = silu_f(acc[i][0][4 * q + u]) * acc[i][1][4 * q + u];
-          *reinterpret_cast<u32x2_t*>(stg + stg64(r, q) + hh * 8) = mx_pack4(a[0], a[1], a[2], a[3]);
+          pk[q] = mx_pack4(a[0], a[1], a[2], a[3]);
         }
-        const int valid = min(4, (mlp - c0) >> 3);
+        if (p.C) {
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const int rr = 16 * k2 + (lane >> 2), c = lane & 3;
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + stg64(rr, c));
-          const int m = m0r + rr;
-          if (m < cm_end && c < valid) st16(p.C + (int64_t)m * mlp + c0 + c * 8, v);
+          for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x2_t*>(stg + stg64(r, q) + hh * 8) = pk[q];
+          const int valid = min(4, (mlp - c0) >> 3);
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const int rr = 16 * k2 + (lane >> 2), c = lane & 3;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + stg64(rr, c));
+            const int m = m0r + rr;
+            if (m < cm_end && c < valid) st16(p.C + (int64_t)m * mlp + c0 + c * 8, v);
+          }
+        }
+        if (p.Cq && c0 < mlp) {
+          // The wave's 32 columns are one MXFP8 block of each row (c0 is a multiple of 32 and mlp of 64):
+          // quantize the bf16-rounded outputs, the same values moe_mx_quantize_rows would read back.
+          float v[16];
+          uint32_t am = 0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[4 * q] = bf16_lo(pk[q][0]);
+            v[4 * q + 1] = bf16_hi(pk[q][0]);
+            v[4 * q + 2] = bf16_lo(pk[q][1]);
+            v[4 * q + 3] = bf16_hi(pk[q][1]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) am = max(am, __float_as_uint(v[4 * q + u]) & 0x7fffffffu);
+          }
+          am = max(am, (uint32_t)__shfl_xor((int)am, 32));  // the row's other 16 columns
+          const int sc = mx_e8m0_code(am);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) word |= mx_e4m3_code(ldexpf(v[4 * q + u], 127 - sc)) << (8 * u);
+            *reinterpret_cast<uint32_t*>(stg + 1024 + r * 32 + 8 * q + 4 * hh) = word;  // [32 rows][32 codes]
+          }
+          {
+            const int rr = lane >> 1, c = lane & 1;
+            const u32x4_t w = *reinterpret_cast<const u32x4_t*>(stg + 1024 + rr * 32 + c * 16);
+            const int m = m0r + rr;
+            if (m < cm_end) st16(p.Cq + (int64_t)m * mlp + c0 + c * 16, w);
+          }
+          const int m = m0r + r;
+          if (hh == 0 && m < cm_end) p.Cqs[((int64_t)(c0 >> 6) * p.M + m) * 4 + ((c0 >> 5) & 1)] = (uint8_t)sc;
         }
       }
     }
@@ -334,9 +375,9 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
 hipError_t launch_grouped_gemm_mx(int epilogue, const uint8_t* A, const uint8_t* As, int64_t a_rows,
                                   const int32_t* row_slot, int slot_div, const uint8_t* B, const uint8_t* Bs,
                                   const int32_t* group_offsets, int E, int64_t M, int K, int N, uint16_t* C,
-                                  hipStream_t stream) {
+                                  uint8_t* Cq, uint8_t* Cqs, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  MxGemmP p{A, As, row_slot, B, Bs, group_offsets, C, E, (int)M, K, N, (int)a_rows, slot_div};
+  MxGemmP p{A, As, row_slot, B, Bs, group_offsets, C, Cq, Cqs, E, (int)M, K, N, (int)a_rows, slot_div};
   int g = device_cu_count();
   g -= g % kNumXcd;
   if (g < kNumXcd) g = kNumXcd;

@@ -21,30 +21,6 @@
 namespace moe {
 namespace {
 
-// E8M0 code of a block whose largest magnitude is amax (fp32 bits of |x|).
-__device__ __forceinline__ int mx_scale_code(uint32_t amax_bits) {
-  if (amax_bits == 0) return 0;
-  const int e = (int)(amax_bits >> 23) - 127;  // floor(log2(amax)); fp32 subnormals give -127 (clamped below)
-  const int c = e - 8 + 127;
-  return c < 0 ? 0 : (c > 254 ? 254 : c);
-}
-
-// E4M3 code of v, which is finite and (by the choice of scale) below 512 in magnitude.
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sgn = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  if (a >= 0x43e00000u) return sgn | 0x7eu;  // |v| >= 448
-  if (a < 0x3c800000u) {                     // |v| < 2^-6: multiples of 2^-9, nearest-even
-    const uint32_t m = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);  // 0..8; 8 is code 0x08
-    return sgn | m;
-  }
-  // keep 3 mantissa bits, round half to even on bit 20; a carry moves into the exponent
-  const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;  // (biased fp32 exponent << 3) | mantissa
-  const uint32_t c = r - ((127u - 7u) << 3);
-  return sgn | (c > 0x7eu ? 0x7eu : c);
-}
-
 // Rows: thread (row r, 8 consecutive elements); 8 threads cover one 64-element slice of a row.
 // Source row of output row r: row_index ? row_index[r] / row_div : r (clamped into the source).
 __global__ __launch_bounds__(256) void mxq_rows_kernel(const uint16_t* __restrict__ src, int64_t src_rows, int K,
@@ -73,12 +49,12 @@ __global__ __launch_bounds__(256) void mxq_rows_kernel(const uint16_t* __restric
   // block of 32 = 4 consecutive threads (aligned in the wave: per_row and c8 are multiples of 8 per slice)
   am = max(am, (uint32_t)__shfl_xor((int)am, 1));
   am = max(am, (uint32_t)__shfl_xor((int)am, 2));
-  const int sc = mx_scale_code(am);
+  const int sc = mx_e8m0_code(am);
   uint32_t lo = 0, hi = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lo |= e4m3_code(ldexpf(x[i], 127 - sc)) << (8 * i);
+  for (int i = 0; i < 4; ++i) lo |= mx_e4m3_code(ldexpf(x[i], 127 - sc)) << (8 * i);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) hi |= e4m3_code(ldexpf(x[4 + i], 127 - sc)) << (8 * i);
+  for (int i = 0; i < 4; ++i) hi |= mx_e4m3_code(ldexpf(x[4 + i], 127 - sc)) << (8 * i);
   u32x2_t out;
   out[0] = lo;
   out[1] = hi;
@@ -114,7 +90,7 @@ __global__ __launch_bounds__(256) void mxq_weight_kernel(const uint16_t* __restr
       x[i] = __uint_as_float((uint32_t)col[(int64_t)(32 * b + i) * N] << 16);
       am = max(am, __float_as_uint(x[i]) & 0x7fffffffu);
     }
-    const int sc = mx_scale_code(am);
+    const int sc = mx_e8m0_code(am);
     sc2[b] = sc;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
@@ -123,7 +99,7 @@ __global__ __launch_bounds__(256) void mxq_weight_kernel(const uint16_t* __restr
       for (int d = 0; d < 4; ++d) {
         uint32_t word = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) word |= e4m3_code(ldexpf(x[16 * g + 4 * d + i], 127 - sc)) << (8 * i);
+        for (int i = 0; i < 4; ++i) word |= mx_e4m3_code(ldexpf(x[16 * g + 4 * d + i], 127 - sc)) << (8 * i);
         o[d] = word;
       }
       st16(dst + 32 * b + 16 * g, o);

@@ -162,3 +162,20 @@ def test_grouped_gemm_mx_row_gather_equals_sorted_rows_bitwise(epi):
     sq, sqs = moe.mx_quantize_rows(x.to(DEV), ssd, k)               # T*k sorted rows
     ref = moe.grouped_gemm_mx(sq, sqs, bc, bs, offd, epilogue=epi)
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("M,K,N,E,empty", [(700, 128, 512, 4, (2,)), (1500, 256, 768, 6, (0, 5)),
+                                           (2600, 512, 1536, 2, ())])
+def test_grouped_gemm_mx_swiglu_writes_the_mxfp8_of_its_bf16_output(M, K, N, E, empty):
+    """The SwiGLU epilogue's MXFP8 output is the quantization of its own bf16 output, bit for bit, and it does
+    not depend on whether the bf16 output is written too."""
+    x, w, off = _mx_case(M, K, N, E, M + 2 * K, empty)
+    ac, as_ = moe.mx_quantize_rows(x.to(DEV))
+    bc, bs = moe.mx_quantize_weight(w.to(DEV))
+    offd = torch.from_numpy(off).to(DEV)
+    c, cq, cqs = moe.grouped_gemm_mx(ac, as_, bc, bs, offd, epilogue="swiglu", mx_out=True)
+    rq, rqs = moe.mx_quantize_rows(c)
+    assert torch.equal(cq, rq)
+    assert torch.equal(cqs[:, :, :2], rqs[:, :, :2])
+    _, cq2, cqs2 = moe.grouped_gemm_mx(ac, as_, bc, bs, offd, epilogue="swiglu", mx_out=True, bf16_out=False)
+    assert torch.equal(cq2, cq) and torch.equal(cqs2[:, :, :2], cqs[:, :, :2])
