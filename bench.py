@@ -213,6 +213,18 @@ def main():
 
     # the fused entry point over the same buffers, as a cross-check of the staged timing
     fused_ms = None
+    if mx:
+        wq = dict(wi_codes=wiq, wi_scales=wis, wo_codes=woq, wo_scales=wos, mlp=mlp)
+        mws = torch.empty(int(L.moe_workspace_bytes_mx(C.byref(shp))), dtype=torch.uint8, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(2):
+            moe.ffn_fwd_mx(x, wq, k, wr=wr, bias=bias, logits=logits, workspace=mws, out=y)
+        e0.record(stream)
+        for _ in range(args.steps):
+            moe.ffn_fwd_mx(x, wq, k, wr=wr, bias=bias, logits=logits, workspace=mws, out=y)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fused_ms = e0.elapsed_time(e1) / args.steps
     if not bwd and not mx:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for _ in range(2):

@@ -313,6 +313,23 @@ int moe_grouped_gemm_mx(int32_t epilogue, const uint8_t* A, const uint8_t* A_sca
                         uint8_t* C_codes, uint8_t* C_scales, moe_stream_t stream);
 
 /*
+ * moe_ffn_fwd_mx -- the MoE FFN forward with MXFP8 grouped GEMMs (inference):
+ *  route and index-only permute as in moe_ffn_fwd; each token row of x
+ *  quantized once (moe_mx_quantize_rows); GEMM 1 on the prefused weight reads
+ *  the token codes through sorted_slot and writes its SwiGLU output as MXFP8;
+ *  GEMM 2; combine into y [T, emb] bf16. The expert weights come quantized:
+ *  wi_codes [E, 2*mlp, emb] and wi_scales [E][emb/64][2*mlp][4] from
+ *  moe_mx_quantize_weight(wi), wo_codes [E, emb, mlp] and wo_scales
+ *  [E][mlp/64][emb][4] from moe_mx_quantize_weight(wo). mlp % 64 == 0;
+ *  T*emb and T*k*mlp below 2^32. Router inputs as in moe_route.
+ *  ws: at least moe_workspace_bytes_mx(shape) bytes (0: unsupported shape).
+ */
+size_t moe_workspace_bytes_mx(const moe_shape_t* shape);
+int moe_ffn_fwd_mx(const moe_shape_t* shape, const moe_bf16_t* x, const float* wr, const float* bias,
+                   const float* logits_in, const uint8_t* wi_codes, const uint8_t* wi_scales, const uint8_t* wo_codes,
+                   const uint8_t* wo_scales, moe_bf16_t* y, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
  * moe_ffn_fwd -- the whole MoE FFN forward: route, permute, grouped GEMM on
  * the prefused wi [E, emb, 2*mlp] with the SwiGLU epilogue, grouped GEMM on
  * wo [E, mlp, emb], combine. y [T, emb] bf16.

@@ -353,3 +353,36 @@ def grouped_gemm_mx(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torc
                                               _ptr(C_), _ptr(cq), _ptr(cqs), _stream(dev)),
                "moe_grouped_gemm_mx")
     return (C_, cq, cqs) if mx_out else C_
+
+
+def mx_quantize_expert_weights(wi: torch.Tensor, wo: torch.Tensor) -> dict:
+    """Weight preparation for ffn_fwd_mx: the MXFP8 codes and scales of wi and wo along their K."""
+    wic, wis = mx_quantize_weight(wi)
+    woc, wos = mx_quantize_weight(wo)
+    return dict(wi_codes=wic, wi_scales=wis, wo_codes=woc, wo_scales=wos, mlp=wi.shape[2] // 2)
+
+
+def ffn_fwd_mx(x: torch.Tensor, wq: dict, k: int, wr: torch.Tensor | None = None, bias: torch.Tensor | None = None,
+               logits: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """MoE FFN forward with MXFP8 grouped GEMMs (see moe_ffn_fwd_mx); wq from mx_quantize_expert_weights."""
+    _need(x, "x", torch.bfloat16)
+    dev = x.device
+    for t, n, d in ((wr, "wr", torch.float32), (bias, "bias", torch.float32), (logits, "logits", torch.float32)):
+        _need(t, n, d, dev)
+    T, emb = x.shape
+    E = wq["wi_codes"].shape[0]
+    mlp = wq["mlp"]
+    s = _lib.shape(T, emb, mlp, E, k)
+    ws_n = int(_lib.lib().moe_workspace_bytes_mx(C.byref(s)))
+    if ws_n == 0:
+        _lib.check(_lib.lib().moe_query_support(C.byref(s)), "ffn_fwd_mx")
+        raise _lib.MoeError(_lib.MOE_ERR_UNSUPPORTED, "ffn_fwd_mx", "mlp must be a multiple of 64")
+    ws = workspace if workspace is not None and workspace.numel() >= ws_n else \
+        torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    y = out if out is not None else torch.empty((T, emb), dtype=torch.bfloat16, device=dev)
+    _lib.check(_lib.lib().moe_ffn_fwd_mx(C.byref(s), _ptr(x), _ptr(wr), _ptr(bias), _ptr(logits),
+                                         _ptr(wq["wi_codes"]), _ptr(wq["wi_scales"]), _ptr(wq["wo_codes"]),
+                                         _ptr(wq["wo_scales"]), _ptr(y), _ptr(ws), ws.numel(), _stream(dev)),
+               "moe_ffn_fwd_mx")
+    return y

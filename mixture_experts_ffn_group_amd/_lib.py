@@ -56,6 +56,8 @@ SIGNATURES = {
     "moe_combine_bwd": ([_SHP, _p, _p, _p, _p, _p, _p, _p], C.c_int),
     "moe_ffn_fwd": ([_SHP, _p, _p, _p, _p, _p, _p, _p, C.POINTER(MoeSaved), _p, _sz, _p], C.c_int),
     "moe_ffn_bwd": ([_SHP, _p, C.POINTER(MoeSaved), _p, _p, _p, _p, _p, _p, _p, _sz, _p], C.c_int),
+    "moe_workspace_bytes_mx": ([_SHP], _sz),
+    "moe_ffn_fwd_mx": ([_SHP, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p], C.c_int),
     "moe_grouped_gemm_mx": ([_i32, _p, _p, _i64, _p, _i32, _p, _p, _p, _i32, _i64, _i32, _i32, _p, _p, _p, _p],
                             C.c_int),
     "moe_mx_quantize_rows": ([_p, _i64, _i32, _p, _i32, _i64, _p, _p, _p], C.c_int),

@@ -172,6 +172,20 @@ size_t moe_workspace_bytes(const moe_shape_t* shape, int with_backward) {
   return with_backward == 2 ? bwd_remat_ws(shape) : with_backward ? bwd_ws(shape) : fwd_ws(shape);
 }
 
+// MXFP8 forward: permute scratch, routing and indices, token codes/scales, SwiGLU output codes/scales, o.
+size_t fwd_mx_ws(const moe_shape_t* s) {
+  const size_t S = (size_t)s->T * s->k, T = (size_t)s->T;
+  return permute_ws(s) + round_up(S * 4) * 2 /*topk idx, w*/ + round_up(s->E * 4) + round_up((s->E + 1) * 4) +
+         round_up(S * 4) * 2 /*sorted_slot, slot_row*/ + round_up(T * s->emb) + round_up(T * s->emb / 16) +
+         round_up(S * s->mlp) + round_up(S * s->mlp / 16) + round_up(S * s->emb * 2) /*o*/;
+}
+
+size_t moe_workspace_bytes_mx(const moe_shape_t* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  if (shape->mlp % 64) return 0;
+  return fwd_mx_ws(shape);
+}
+
 // per-slot logit gradients, then Wr transposed
 size_t route_bwd_ws(const moe_shape_t* s) {
   return 3 * round_up(4 * (size_t)s->T * s->k) + 2 * round_up(4 * (size_t)s->E * s->emb);
@@ -414,6 +428,73 @@ int moe_grouped_gemm_mx(int32_t epilogue, const uint8_t* A, const uint8_t* A_sca
                                                  B_scales, group_offsets, E, M, K, N, C, C_codes, C_scales,
                                                  (hipStream_t)stream),
                     "moe_grouped_gemm_mx");
+}
+
+int moe_ffn_fwd_mx(const moe_shape_t* s, const moe_bf16_t* x, const float* wr, const float* bias,
+                   const float* logits_in, const uint8_t* wi_codes, const uint8_t* wi_scales, const uint8_t* wo_codes,
+                   const uint8_t* wo_scales, moe_bf16_t* y, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  g_detail[0] = 0;
+  if (int rc = check_shape(s)) return rc;
+  if (s->mlp % 64) return fail(MOE_ERR_UNSUPPORTED, "the MXFP8 forward needs mlp %% 64 == 0");
+  if ((int64_t)s->T * s->emb >= (int64_t(1) << 32) || (int64_t)s->T * s->k * s->mlp >= (int64_t(1) << 32))
+    return fail(MOE_ERR_UNSUPPORTED, "T*emb and T*k*mlp must be below 2^32");
+  const bool any = s->T > 0;
+  if (any) {
+    NEED(x);
+    NEED(y);
+  }
+  NEED(wi_codes);
+  NEED(wi_scales);
+  NEED(wo_codes);
+  NEED(wo_scales);
+  if (logits_in) {
+    if (wr || bias) return fail(MOE_ERR_SHAPE, "with logits_in, wr and bias must be NULL");
+    MAYBE(logits_in);
+  } else {
+    NEED(wr);
+    MAYBE(bias);
+  }
+  NEED(ws);
+  if (ws_bytes < fwd_mx_ws(s)) return fail(MOE_ERR_WORKSPACE, "need %zu workspace bytes", fwd_mx_ws(s));
+  if (!any) return MOE_OK;
+  const int64_t T = s->T, S = T * s->k;
+  const int emb = s->emb, mlp = s->mlp, E = s->E, k = s->k;
+  const hipStream_t st = (hipStream_t)stream;
+  Carver c{static_cast<char*>(ws)};
+  uint64_t* masks = c.take<uint64_t>(((T + moe::kPermuteBlock - 1) / moe::kPermuteBlock) * E);
+  int32_t* base = c.take<int32_t>(((T + moe::kPermuteBlock - 1) / moe::kPermuteBlock) * E);
+  int32_t* topk_idx = c.take<int32_t>(S);
+  float* topk_w = c.take<float>(S);
+  int32_t* group_sizes = c.take<int32_t>(E);
+  int32_t* group_offsets = c.take<int32_t>(E + 1);
+  int32_t* sorted_slot = c.take<int32_t>(S);
+  int32_t* slot_row = c.take<int32_t>(S);
+  uint8_t* xq = c.take<uint8_t>(T * emb);
+  uint8_t* xqs = c.take<uint8_t>(T * emb / 16);
+  uint8_t* aq = c.take<uint8_t>(S * mlp);
+  uint8_t* aqs = c.take<uint8_t>(S * mlp / 16);
+  moe_bf16_t* o = c.take<moe_bf16_t>(S * emb);
+  if (int rc = hip_status(moe::launch_route(T, emb, E, k, logits_in ? nullptr : x, wr, bias, logits_in, topk_idx,
+                                            topk_w, st),
+                          "route"))
+    return rc;
+  if (int rc = hip_status(moe::launch_permute(T, emb, E, k, x, topk_idx, group_sizes, group_offsets, sorted_slot,
+                                              slot_row, nullptr, masks, base, st),
+                          "permute"))
+    return rc;
+  // each token row quantized once; GEMM 1 reads its codes and scales through sorted_slot
+  if (int rc = hip_status(moe::launch_mx_quantize_rows(x, T, emb, nullptr, 1, T, xq, xqs, st), "quantize x"))
+    return rc;
+  if (int rc = hip_status(moe::launch_grouped_gemm_mx(MOE_EPI_SWIGLU, xq, xqs, T, sorted_slot, k, wi_codes,
+                                                      wi_scales, group_offsets, E, S, emb, 2 * mlp, nullptr, aq, aqs,
+                                                      st),
+                          "gemm1"))
+    return rc;
+  if (int rc = hip_status(moe::launch_grouped_gemm_mx(MOE_EPI_NONE, aq, aqs, S, nullptr, 1, wo_codes, wo_scales,
+                                                      group_offsets, E, S, mlp, emb, o, nullptr, nullptr, st),
+                          "gemm2"))
+    return rc;
+  return hip_status(moe::launch_combine(T, emb, k, o, slot_row, topk_w, y, st), "combine");
 }
 
 int moe_ffn_fwd(const moe_shape_t* s, const moe_bf16_t* x, const float* wr, const float* bias, const float* logits_in,

@@ -141,6 +141,12 @@ def test_validation_precedes_any_launch(lib):
     assert lib.moe_mx_quantize_rows(fake, 8, 128, nul, 1, 0, nul, nul, nul) == _lib.MOE_OK  # no rows: no-op
     assert lib.moe_mx_quantize_weight(fake, 2, 96, 64, fake, fake, nul) == _lib.MOE_ERR_UNSUPPORTED
     assert lib.moe_mx_quantize_weight(fake, 2, 128, 64, nul, fake, nul) == _lib.MOE_ERR_NULL
+    # MXFP8 layer forward: workspace query, NULL inputs, small workspace
+    assert lib.moe_workspace_bytes_mx(C.byref(s)) > 0
+    assert lib.moe_ffn_fwd_mx(C.byref(s), nul, fake, nul, nul, fake, fake, fake, fake, fake, fake, 1 << 40,
+                              nul) == _lib.MOE_ERR_NULL
+    assert lib.moe_ffn_fwd_mx(C.byref(s), fake, fake, nul, nul, fake, fake, fake, fake, fake, fake, 16,
+                              nul) == _lib.MOE_ERR_WORKSPACE
     # a saved set without h: the backward recomputes it and needs the larger workspace
     ws1, ws2 = lib.moe_workspace_bytes(C.byref(s), 1), lib.moe_workspace_bytes(C.byref(s), 2)
     assert ws2 >= ws1 + s.T * s.k * 2 * s.mlp * 4

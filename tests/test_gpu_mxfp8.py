@@ -179,3 +179,63 @@ def test_grouped_gemm_mx_swiglu_writes_the_mxfp8_of_its_bf16_output(M, K, N, E, 
     assert torch.equal(cqs[:, :, :2], rqs[:, :, :2])
     _, cq2, cqs2 = moe.grouped_gemm_mx(ac, as_, bc, bs, offd, epilogue="swiglu", mx_out=True, bf16_out=False)
     assert torch.equal(cq2, cq) and torch.equal(cqs2[:, :, :2], cqs[:, :, :2])
+
+
+# ---------------------------------------------------------------- MXFP8 layer forward
+
+import workloads  # noqa: E402
+
+
+def _mx_layer_inputs(name):
+    h = workloads.make_inputs(workloads.WORKLOADS[name])
+    d = {kk: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for kk, v in h.items()}
+    return h, d
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid_skewed"])
+def test_ffn_fwd_mx_equals_its_stages_bitwise(name):
+    h, d = _mx_layer_inputs(name)
+    wl = h["workload"]
+    T, k = wl.T, wl.k
+    wq = moe.mx_quantize_expert_weights(d["wi"], d["wo"])
+    y = moe.ffn_fwd_mx(d["x"], wq, k, wr=d["wr"], bias=d["bias"])
+    idx, w = moe.route(k, x=d["x"], wr=d["wr"], bias=d["bias"])
+    perm = moe.permute(d["x"], idx, wl.E, rows=False)
+    xq, xqs = moe.mx_quantize_rows(d["x"])
+    _, aq, aqs = moe.grouped_gemm_mx(xq, xqs, wq["wi_codes"], wq["wi_scales"], perm["group_offsets"],
+                                     epilogue="swiglu", row_slot=perm["sorted_slot"], slot_div=k, mx_out=True,
+                                     bf16_out=False)
+    o = moe.grouped_gemm_mx(aq, aqs, wq["wo_codes"], wq["wo_scales"], perm["group_offsets"])
+    y_ref = moe.combine(o, perm["slot_row"], w, T, k)
+    assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid_skewed"])
+def test_ffn_fwd_mx_matches_the_oracle_composition(name):
+    """Each stage from the oracle: routing, token quantization, float64 GEMM 1 on the dequantized operands,
+    SwiGLU rounded to bf16 and quantized, float64 GEMM 2, bf16 rounding, combine. The device and the oracle
+    quantize the same token rows and weights bit for bit; the SwiGLU output can round to a neighbouring bf16
+    value on either side and then to a neighbouring code, which the layer tolerance covers."""
+    from parity_util import assert_close, to_np
+    h, d = _mx_layer_inputs(name)
+    wl = h["workload"]
+    T, emb, mlp, E, k = wl.T, wl.emb, wl.mlp, wl.E, wl.k
+    wq = moe.mx_quantize_expert_weights(d["wi"], d["wo"])
+    y = moe.ffn_fwd_mx(d["x"], wq, k, wr=d["wr"], bias=d["bias"])
+    xb = bits(h["x"])
+    idx, w, _ = oracle.route(xb, h["wr"].numpy(), None if h["bias"] is None else h["bias"].numpy(), k)
+    gs, off, ss, sr = oracle.dispatch(idx, E)
+    xc, xs_ = oracle.mx_quantize(xb)
+    wi_t = np.ascontiguousarray(np.transpose(bits(h["wi"]), (0, 2, 1)))   # [E, 2mlp, emb]
+    wo_t = np.ascontiguousarray(np.transpose(bits(h["wo"]), (0, 2, 1)))   # [E, emb, mlp]
+    wic = np.stack([oracle.mx_quantize(wi_t[e])[0] for e in range(E)])
+    wis = np.stack([oracle.mx_quantize(wi_t[e])[1] for e in range(E)])
+    woc = np.stack([oracle.mx_quantize(wo_t[e])[0] for e in range(E)])
+    wos = np.stack([oracle.mx_quantize(wo_t[e])[1] for e in range(E)])
+    a = oracle.mx_grouped_gemm_nt(xc[ss // k], xs_[ss // k], wic, wis, off, epi=1)
+    a_b = bits(torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16))
+    ac, as_ = oracle.mx_quantize(a_b)
+    o = oracle.mx_grouped_gemm_nt(ac, as_, woc, wos, off)
+    o_b = bits(torch.from_numpy(o.astype(np.float32)).to(torch.bfloat16))
+    y_ref = oracle.combine(o_b, sr, w, T, k)
+    assert_close(to_np(y), y_ref, "y")
