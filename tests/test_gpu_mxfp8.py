@@ -192,14 +192,17 @@ def _mx_layer_inputs(name):
     return h, d
 
 
-@pytest.mark.parametrize("name", ["tiny", "mid_skewed"])
+@pytest.mark.parametrize("name", ["tiny", "mid_skewed", "sweep_zipf_T1024"])
 def test_ffn_fwd_mx_equals_its_stages_bitwise(name):
     h, d = _mx_layer_inputs(name)
     wl = h["workload"]
     T, k = wl.T, wl.k
     wq = moe.mx_quantize_expert_weights(d["wi"], d["wo"])
-    y = moe.ffn_fwd_mx(d["x"], wq, k, wr=d["wr"], bias=d["bias"])
-    idx, w = moe.route(k, x=d["x"], wr=d["wr"], bias=d["bias"])
+    y = moe.ffn_fwd_mx(d["x"], wq, k, wr=d["wr"], bias=d["bias"], logits=d["logits_in"])
+    if d["logits_in"] is not None:
+        idx, w = moe.route(k, logits=d["logits_in"])
+    else:
+        idx, w = moe.route(k, x=d["x"], wr=d["wr"], bias=d["bias"])
     perm = moe.permute(d["x"], idx, wl.E, rows=False)
     xq, xqs = moe.mx_quantize_rows(d["x"])
     _, aq, aqs = moe.grouped_gemm_mx(xq, xqs, wq["wi_codes"], wq["wi_scales"], perm["group_offsets"],
@@ -239,3 +242,10 @@ def test_ffn_fwd_mx_matches_the_oracle_composition(name):
     o_b = bits(torch.from_numpy(o.astype(np.float32)).to(torch.bfloat16))
     y_ref = oracle.combine(o_b, sr, w, T, k)
     assert_close(to_np(y), y_ref, "y")
+
+
+def test_ffn_fwd_mx_with_no_tokens_is_a_no_op():
+    h, d = _mx_layer_inputs("tiny")
+    wq = moe.mx_quantize_expert_weights(d["wi"], d["wo"])
+    y = moe.ffn_fwd_mx(d["x"][:0], wq, h["workload"].k, wr=d["wr"])
+    assert y.shape == (0, d["x"].shape[1])
