@@ -381,7 +381,8 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
       }
     }
     const bool more = decode(it + 1);
-    if (more)
+    // (the SwiGLU backward uses the operand ring in its epilogue and issues these afterwards)
+    if (EPI != EPI_SWIGLU_BWD && more)
       for (int s = 0; s < NST; ++s)
         if (s < nk) issue_loads(s);
     // Epilogue. Lane holds rows m = tile row + lane%32 and, per register group q,
@@ -471,35 +472,84 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
         }
       }
     } else {
+      // EPI_SWIGLU_BWD: N = mlp, aux = saved h [M, 2N] fp32, C = dh [M, 2N] bf16.
+      // Work unit (i, f): the 32 x 32 accumulator block acc[i][f]. Its gate and
+      // up values (32 fp32 columns of each, 128 bytes per row) are copied by
+      // direct loads, eight lanes per 128-byte row segment, into one half of
+      // this wave's 16 KB share of the operand ring, which is idle until the
+      // next tile's loads go out; the copy of unit u + 1 is in flight while
+      // unit u is computed. Reading h straight from the accumulator layout
+      // would fetch 16 bytes from each of 32 rows per instruction. Region
+      // layout: [gate | up] x [32 rows][128 B], 16-byte chunk c of row r at
+      // r*128 + ((c ^ ((r >> 1) & 7)) << 4), so the accumulator-layout reads
+      // (16 rows at one chunk per 16 lanes) hit distinct banks. dgate and dup
+      // leave through the 2 KB staging area as 64-byte row segments.
+      __syncthreads();  // every wave has read its last fragments from the ring
+      const int wm_u = wave_u & 1, wn_u = wave_u >> 1;
+      const int nunits = 2 * min(4, max(0, (cm_end - (cm0 + wm_u * 128) + 31) / 32));  // wave-uniform
+      const uint32_t hreg = lds_addr(smem) + wave_u * 16384;
+      auto issue_h = [&](int u) {
+        const int m0r = cm0 + wm_u * 128 + (u >> 1) * 32;
+        const int cf = cn0 + wn_u * 64 + (u & 1) * 32;
+        const float* rowbase = uniform_ptr(p.aux_in + (int64_t)m0r * 2 * p.N);
+        const uint32_t dst = hreg + (u & 1) * 8192;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = cm0 + wm * 128 + i * 32 + (lane & 31);
-      if (m >= cm_end) continue;
-      const float sc = sc4[i];
-      {  // EPI_SWIGLU_BWD: N = mlp, aux = saved h [M, 2N] fp32, C = dh [M, 2N]
-        const float* hrow = p.aux_in + (int64_t)m * 2 * p.N;
-        uint16_t* drow = p.C + (int64_t)m * 2 * p.N;
+        for (int j = 0; j < 4; ++j) {
+          const int row = 8 * j + (lane >> 3);
+          const int lc = (lane & 7) ^ ((row >> 1) & 7);
+          const int rl = min(m0r + row, cm_end - 1) - m0r;
+          int col = cf + 4 * lc;
+          col = col < p.N ? col : 0;  // columns past N feed outputs that are never stored
+          const uint32_t voff = (uint32_t)(rl * 2 * p.N + col) * 4u;
+          g2lds16(rowbase, voff, dst + j * 1024);
+          g2lds16(rowbase, voff + (uint32_t)p.N * 4u, dst + 4096 + j * 1024);
+        }
+      };
+      if (nunits > 0) issue_h(0);
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
+      for (int u = 0; u < 8; ++u) {
+        if (u < nunits) {
+          if (u + 1 < nunits) {
+            issue_h(u + 1);
+            wait_vm_8();  // unit u's copies (older than unit u + 1's eight) have landed
+          } else {
+            wait_vm_all();
+          }
+          const int i = u >> 1, f = u & 1;
+          const float sc = sc4[i];
+          const int m0r = cm0 + wm * 128 + i * 32;
+          const int cf = cn0 + wn * 64 + f * 32;
+          const uint8_t* hb = smem + wave_u * 16384 + (u & 1) * 8192;
+          u32x2_t dgp[4], dup[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int n = cn0 + wn * 64 + f * 32 + 8 * q + 4 * hh;
-            if (n >= p.N) continue;
-            const f32x4_t g = *reinterpret_cast<const f32x4_t*>(hrow + n);
-            const f32x4_t u = *reinterpret_cast<const f32x4_t*>(hrow + p.N + n);
+            const int off = r * 128 + (((2 * q + hh) ^ ((r >> 1) & 7)) << 4);
+            const f32x4_t g = *reinterpret_cast<const f32x4_t*>(hb + off);
+            const f32x4_t uu = *reinterpret_cast<const f32x4_t*>(hb + 4096 + off);
             float dg[4], du[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float da = sc * acc[i][f][4 * q + r];
-              const float s = sigmoid_f(g[r]);
-              dg[r] = da * u[r] * s * (1.0f + g[r] * (1.0f - s));
-              du[r] = da * g[r] * s;
+            for (int e = 0; e < 4; ++e) {
+              const float da = sc * acc[i][f][4 * q + e];
+              const float s = sigmoid_f(g[e]);
+              dg[e] = da * uu[e] * s * (1.0f + g[e] * (1.0f - s));
+              du[e] = da * g[e] * s;
             }
-            st8(drow + n, pack4(dg[0], dg[1], dg[2], dg[3]));
-            st8(drow + p.N + n, pack4(du[0], du[1], du[2], du[3]));
+            dgp[q] = pack4(dg[0], dg[1], dg[2], dg[3]);
+            dup[q] = pack4(du[0], du[1], du[2], du[3]);
           }
+          const int valid = min(4, (p.N - cf) >> 3);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x2_t*>(stg + stg64(r, q) + hh * 8) = dgp[q];
+          drain(m0r, [&](int m) { return (void*)(p.C + (int64_t)m * 2 * p.N + cf); }, valid);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x2_t*>(stg + stg64(r, q) + hh * 8) = dup[q];
+          drain(m0r, [&](int m) { return (void*)(p.C + (int64_t)m * 2 * p.N + p.N + cf); }, valid);
+        }
       }
-    }
+      __syncthreads();  // every wave is done with its share of the ring
+      if (more)
+        for (int s = 0; s < NST; ++s)
+          if (s < nk) issue_loads(s);
     }
     if (!more) break;
   }
