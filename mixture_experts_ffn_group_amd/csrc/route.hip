@@ -24,6 +24,27 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kBK = 32;  // emb slice staged in LDS per step
 
+// Direct global->LDS copy, 16 bytes per lane: lane L's 16 bytes at sbase + voff
+// land at LDS byte address lds + 16 L (global_load_lds_dwordx4, M0 = lds).
+// Issued from inline asm, so the kernel counts vmcnt itself before the barrier
+// that publishes a stage.
+__device__ __forceinline__ void g2lds16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm_n() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+template <class T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const T*)(((uint64_t)hi << 32) | lo);
+}
+
 // Order-preserving key of a logit: larger logit -> larger key. -0 maps like +0;
 // NaN maps to 0, below every number.
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -36,21 +57,86 @@ __device__ __forceinline__ float key_value(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) {
-    uint32_t lo = __shfl_xor((unsigned int)(uint32_t)v, s);
-    uint32_t hi = __shfl_xor((unsigned int)(uint32_t)(v >> 32), s);
-    uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+// Wave-wide reductions on DPP lane moves (GFX9 controls): the two quad
+// permutations and row rotations by 4 and 8 reduce each 16-lane row, and the
+// row broadcasts of lanes 15 and 31 carry the rows into lane 63, which is
+// then read as a scalar. A few cycles per step, where a cross-lane shuffle
+// through the LDS crossbar waits on its result every step.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xb1, 0xf>(v));   // quad_perm [1,0,3,2]
+  v = max(v, dpp_u32<0x4e, 0xf>(v));   // quad_perm [2,3,0,1]
+  v = max(v, dpp_u32<0x124, 0xf>(v));  // row_ror:4
+  v = max(v, dpp_u32<0x128, 0xf>(v));  // row_ror:8
+  v = max(v, dpp_u32<0x142, 0xa>(v));  // row_bcast:15 into rows 1, 3
+  v = max(v, dpp_u32<0x143, 0xc>(v));  // row_bcast:31 into rows 2, 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  auto add = [](float a, uint32_t b) { return a + __uint_as_float(b); };
+  v = add(v, dpp_u32<0xb1, 0xf>(__float_as_uint(v)));
+  v = add(v, dpp_u32<0x4e, 0xf>(__float_as_uint(v)));
+  v = add(v, dpp_u32<0x124, 0xf>(__float_as_uint(v)));
+  v = add(v, dpp_u32<0x128, 0xf>(__float_as_uint(v)));
+  // rows 1 and 3 add the previous row's total; row 3 then adds rows 0 + 1 (carried by lane 31)
+  const uint32_t b15 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), 0x142, 0xa, 0xf, false);
+  v = v + __uint_as_float(b15);
+  const uint32_t b31 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), 0x143, 0xc, 0xf, false);
+  v = v + __uint_as_float(b31);
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 63));
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
+// Top-k of the logits of a workgroup's TB tokens, held in LDS as [TB][EP].
+template <int TB, int EP>
+__device__ __forceinline__ void route_topk(const float* s_l, int64_t T, int64_t t0, int E, int k,
+                                           int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  constexpr int EQ = EP / 64;     // experts per lane
+  constexpr int TPW = TB / kWaves;  // tokens per wave
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // Top-k per token: k rounds of a wave-wide max over (key(logit), -expert).
+  // Picked and padding experts hold candidate 0, which no real expert reaches.
+#pragma unroll 1
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int tok = wave * TPW + tt;
+    const int64_t t = t0 + tok;
+    if (t >= T) break;  // wave-uniform
+    uint64_t cand[EQ];
 #pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s);
-  return v;
+    for (int q = 0; q < EQ; ++q) {
+      const int e = lane + 64 * q;
+      const float l = s_l[tok * EP + e];
+      cand[q] = e < E ? (((uint64_t)order_key(l) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e)) : 0ull;
+    }
+    int my_e = 0;
+    float my_l = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      uint64_t best = 0ull;
+#pragma unroll
+      for (int q = 0; q < EQ; ++q) best = cand[q] > best ? cand[q] : best;
+      // the wave's largest (key, -expert): the largest key, then the lowest expert holding it
+      const uint32_t key = wave_max_u32((uint32_t)(best >> 32));
+      const uint32_t low = wave_max_u32((uint32_t)(best >> 32) == key ? (uint32_t)best : 0u);
+      const int e = min(max((int)(0xffffffffu - low), 0), E - 1);
+      const float l = key_value(key);
+#pragma unroll
+      for (int q = 0; q < EQ; ++q)
+        if (e == lane + 64 * q) cand[q] = 0ull;
+      if (lane == j) {
+        my_e = e;
+        my_l = l;
+      }
+    }
+    const float l0 = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(my_l), 0));
+    const float ex = lane < k ? expf(my_l - l0) : 0.0f;
+    const float s = wave_sum(ex);
+    if (lane < k) {
+      topk_idx[t * k + lane] = my_e;
+      topk_w[t * k + lane] = ex / s;
+    }
+  }
 }
 
 // Output layout of v_mfma_f32_32x32x1_2b_f32 (measured): lane l, register r ->
@@ -68,8 +154,6 @@ __global__ __launch_bounds__(256) void route_kernel(int64_t T, int emb, int E, i
                                                     float* __restrict__ topk_w) {
   constexpr int TB = MODE == 0 ? 64 : 32;  // tokens per workgroup
   constexpr int EP = MODE == 0 ? 128 : 256;  // expert columns (logit row stride)
-  constexpr int EQ = EP / 64;              // experts per lane in the top-k
-  constexpr int TPW = TB / kWaves;         // tokens per wave in the top-k
   static_assert(TB <= 2 * kBK, "the two w buffers must hold the logits of a workgroup's tokens");
   __shared__ __attribute__((aligned(16))) float s_x[2][kBK][TB];
   __shared__ __attribute__((aligned(16))) float s_w[2][kBK][EP];
@@ -167,45 +251,138 @@ __global__ __launch_bounds__(256) void route_kernel(int64_t T, int emb, int E, i
   }
   __syncthreads();
 
-  // Top-k per token: k rounds of a wave-wide max over (key(logit), -expert).
-  // Picked and padding experts hold candidate 0, which no real expert reaches.
-#pragma unroll 1
-  for (int tt = 0; tt < TPW; ++tt) {
-    const int tok = wave * TPW + tt;
-    const int64_t t = t0 + tok;
-    if (t >= T) break;  // wave-uniform
-    uint64_t cand[EQ];
+  route_topk<TB, EP>(s_l, T, t0, E, k, topk_idx, topk_w);
+}
+
+
+// The same logits with the operands copied global -> LDS by direct loads
+// (global_load_lds_dwordx4) into a ring of NS stages, NS slices ahead of the
+// one multiplied, so the latency of x (read once, from HBM) is covered
+// by several slices of MFMAs rather than one. The x slice keeps its bf16 bits
+// in LDS ([TB tokens][32] with 64-byte rows, 16-byte chunk c of token t at
+// chunk c ^ ((t >> 2) & 3)) and is widened to fp32 (exact) as it is read;
+// the Wr slice is [32][EP] fp32, as Wr is laid out. Each slice's operands
+// are read into registers during the previous slice's MFMAs. Needs
+// E % 4 == 0: a 16-byte copy of Wr holds four experts of one row.
+template <int MODE>
+__global__ __launch_bounds__(256) void route_ring_kernel(int64_t T, int emb, int E, int k,
+                                                         const uint16_t* __restrict__ x, const float* __restrict__ wr,
+                                                         const float* __restrict__ bias, int32_t* __restrict__ topk_idx,
+                                                         float* __restrict__ topk_w) {
+  constexpr int TB = MODE == 0 ? 64 : 32;
+  constexpr int EP = MODE == 0 ? 128 : 256;
+  constexpr int NS = MODE == 0 ? 3 : 4;  // two workgroups per CU in MODE 0, one in MODE 1
+  constexpr int kXS = TB * kBK * 2;      // x stage: 4 KB / 2 KB
+  constexpr int kWS = kBK * EP * 4;      // Wr stage: 16 KB / 32 KB
+  constexpr int kWI = kWS / 1024 / kWaves;  // 1 KB Wr copies per wave per slice: 4 / 8
+  constexpr int nL = 1 + kWI;            // copies per wave per slice
+  static_assert(NS * (kXS + kWS) >= TB * EP * 4, "the logits reuse the ring");
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[NS * (kXS + kWS)];
+  uint8_t* const s_xr = s_ring;              // NS x stages
+  uint8_t* const s_wr = s_ring + NS * kXS;   // NS Wr stages
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int64_t t0 = (int64_t)blockIdx.x * TB;
+  const int ns = emb / kBK;  // even: emb % 64 == 0
+
+  // Per-lane copy offsets. x: MODE 0 wave w copies tokens 16w..16w+15 (1 KB),
+  // MODE 1 tokens 8w..8w+7 (512 B, lanes 0-31); lane L -> token, physical
+  // chunk L % 4 holding logical chunk (L % 4) ^ ((token >> 2) & 3). Tokens
+  // past T read the last token (their logits are never used).
+  const int xtok = (MODE == 0 ? 16 : 8) * wave + (lane >> 2);
+  const int xlc = (lane & 3) ^ ((xtok >> 2) & 3);
+  const uint16_t* const xbase = x + t0 * emb;
+  const uint32_t xoff = (uint32_t)(((int64_t)min<int64_t>(xtok, T - 1 - t0) * emb + 8 * xlc) * 2);
+  // Wr: copy j of wave w is 1 KB of the [32][EP] slice at byte (w * kWI + j) * 1024;
+  // experts past E read expert 0 (never used).
+  uint32_t woff[kWI];
 #pragma unroll
-    for (int q = 0; q < EQ; ++q) {
-      const int e = lane + 64 * q;
-      const float l = s_l[tok * EP + e];
-      cand[q] = e < E ? (((uint64_t)order_key(l) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e)) : 0ull;
-    }
-    int my_e = 0;
-    float my_l = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      uint64_t best = 0ull;
+  for (int j = 0; j < kWI; ++j) {
+    const int byte = (wave * kWI + j) * 1024 + lane * 16;
+    const int row = byte / (EP * 4), e = (byte % (EP * 4)) / 4;
+    woff[j] = (uint32_t)((row * E + (e < E ? e : 0)) * 4);
+  }
+  const uint32_t lds_x = lds_addr(s_xr) + wave_u * (MODE == 0 ? 1024 : 512);
+  const uint32_t lds_w = lds_addr(s_wr) + wave_u * kWI * 1024;
+  auto issue = [&](int sl) {
+    const int st = sl % NS;
+    const uint16_t* xs = uniform_ptr(xbase + sl * kBK);
+    if (MODE == 0 || lane < 32) g2lds16(xs, xoff, lds_x + st * kXS);
+    const float* ws = uniform_ptr(wr + (int64_t)sl * kBK * E);
 #pragma unroll
-      for (int q = 0; q < EQ; ++q) best = cand[q] > best ? cand[q] : best;
-      best = wave_max_u64(best);
-      const int e = (int)(0xffffffffu - (uint32_t)best);
-      const float l = key_value((uint32_t)(best >> 32));
+    for (int j = 0; j < kWI; ++j) g2lds16(ws, woff[j], lds_w + st * kWS + j * 1024);
+  };
+  // Wait until the copies of slice sl have landed, given that `later` slices were issued after it.
+  auto wait_slice = [&](int later) {
+    if (later >= 3) wait_vm_n<3 * nL>();
+    else if (later == 2) wait_vm_n<2 * nL>();
+    else if (later == 1) wait_vm_n<nL>();
+    else wait_vm_n<0>();
+  };
+
+  const int tok_a = MODE == 0 ? lane : (lane & 31);  // A operand: this lane's token
+  const int exp_b = MODE == 0 ? 32 * wave + (lane & 31) : 64 * wave + lane;  // B operand: its expert
+  const bool busy = (MODE == 0 ? 32 : 64) * wave < E;  // wave-uniform
+  f32x32_t acc;
 #pragma unroll
-      for (int q = 0; q < EQ; ++q)
-        if (e == lane + 64 * q) cand[q] = 0ull;
-      if (lane == j) {
-        my_e = e;
-        my_l = l;
+  for (int r = 0; r < 32; ++r) acc[r] = 0.0f;
+  u32x4_t xq[2][4];
+  float wv[2][kBK];
+  auto read_ops = [&](int sl, int set) {
+    const int st = sl % NS;
+    const uint8_t* xt = s_xr + st * kXS;
+    const float* wt = reinterpret_cast<const float*>(s_wr + st * kWS);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      xq[set][c] = *reinterpret_cast<const u32x4_t*>(xt + tok_a * 64 + ((c ^ ((tok_a >> 2) & 3)) << 4));
+#pragma unroll
+    for (int ii = 0; ii < kBK; ++ii) wv[set][ii] = wt[ii * EP + exp_b];
+  };
+  auto chain = [&](int set) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const uint32_t v = xq[set][c][h];
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(__uint_as_float(v << 16), wv[set][8 * c + 2 * h], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(__uint_as_float(v & 0xffff0000u), wv[set][8 * c + 2 * h + 1],
+                                                   acc, 0, 0, 0);
       }
-    }
-    const float l0 = __shfl(my_l, 0);
-    const float ex = lane < k ? expf(my_l - l0) : 0.0f;
-    const float s = wave_sum(ex);
-    if (lane < k) {
-      topk_idx[t * k + lane] = my_e;
-      topk_w[t * k + lane] = ex / s;
+  };
+  // Slice j: wait for slice j + 1's copies, barrier (every wave has also
+  // finished reading slice j into registers, so its stage takes slice j + NS),
+  // read slice j + 1's operands, then multiply slice j.
+  for (int sl = 0; sl < NS && sl < ns; ++sl) issue(sl);
+  wait_slice(min(NS - 1, ns - 1));
+  __syncthreads();
+  if (busy) read_ops(0, 0);
+  for (int j = 0; j < ns; j += 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int jj = j + h;
+      if (jj + 1 < ns) {
+        wait_slice(min(NS - 2, ns - 2 - jj));
+        __syncthreads();
+        if (jj + NS < ns) issue(jj + NS);
+        if (busy) read_ops(jj + 1, h ^ 1);
+      }
+      if (busy) chain(h);
     }
   }
+  __syncthreads();  // the ring now takes the logits
+  float* const s_l = reinterpret_cast<float*>(s_ring);
+  if (busy) {
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      const int blk = r >> 4, rr = r & 15;
+      const int row = (rr >> 2) * 8 + (lane >> 5) * 4 + (rr & 3), col = lane & 31;
+      const int tok = MODE == 0 ? 32 * blk + row : row;
+      const int e = MODE == 0 ? 32 * wave + col : 64 * wave + 32 * blk + col;
+      if (e < E) s_l[tok * EP + e] = bias ? acc[r] + bias[e] : acc[r];
+    }
+  }
+  __syncthreads();
+  route_topk<TB, EP>(s_l, T, t0, E, k, topk_idx, topk_w);
 }
 
 }  // namespace
@@ -214,7 +391,14 @@ hipError_t launch_route(int64_t T, int emb, int E, int k, const uint16_t* x, con
                         const float* logits_in, int32_t* topk_idx, float* topk_w, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const dim3 block(256);
-  if (E <= 128) {
+  if (!logits_in && (E & 3) == 0) {
+    if (E <= 128)
+      route_ring_kernel<0><<<dim3((unsigned)((T + 63) / 64)), block, 0, stream>>>(T, emb, E, k, x, wr, bias, topk_idx,
+                                                                                 topk_w);
+    else
+      route_ring_kernel<1><<<dim3((unsigned)((T + 31) / 32)), block, 0, stream>>>(T, emb, E, k, x, wr, bias, topk_idx,
+                                                                                 topk_w);
+  } else if (E <= 128) {
     route_kernel<0><<<dim3((unsigned)((T + 63) / 64)), block, 0, stream>>>(T, emb, E, k, x, wr, bias, logits_in,
                                                                           topk_idx, topk_w);
   } else {
