@@ -89,7 +89,76 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 63));
 }
 
-// Top-k of the logits of a workgroup's TB tokens, held in LDS as [TB][EP].
+// 16-lane (row) reductions with symmetric exchanges: quad swaps, then the
+// half-row and row mirrors. Every lane combines its value with a partner's
+// in the same association, so all 16 lanes end with the identical result.
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xb1, 0xf>(v));   // quad_perm [1,0,3,2]
+  v = max(v, dpp_u32<0x4e, 0xf>(v));   // quad_perm [2,3,0,1]
+  v = max(v, dpp_u32<0x141, 0xf>(v));  // row_half_mirror
+  v = max(v, dpp_u32<0x140, 0xf>(v));  // row_mirror
+  return v;
+}
+__device__ __forceinline__ float row_sum(float v) {
+  v = v + __uint_as_float(dpp_u32<0xb1, 0xf>(__float_as_uint(v)));
+  v = v + __uint_as_float(dpp_u32<0x4e, 0xf>(__float_as_uint(v)));
+  v = v + __uint_as_float(dpp_u32<0x141, 0xf>(__float_as_uint(v)));
+  v = v + __uint_as_float(dpp_u32<0x140, 0xf>(__float_as_uint(v)));
+  return v;
+}
+
+// Top-k for k <= 16, four tokens at a time per wave: token g of the group on
+// lanes 16g..16g+15, lane r holding experts r + 16q. Same picks as the
+// one-token-per-wave form below: the largest (key, -expert) each round.
+template <int TB, int EP>
+__device__ __forceinline__ void route_topk16(const float* s_l, int64_t T, int64_t t0, int E, int k,
+                                             int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  constexpr int EQ = EP / 16;       // experts per lane
+  constexpr int TPW = TB / kWaves;  // tokens per wave (a multiple of 4)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r = lane & 15;
+#pragma unroll 1
+  for (int t4 = 0; t4 < TPW; t4 += 4) {
+    if (t0 + wave * TPW + t4 >= T) break;  // wave-uniform: no token of the group exists
+    const int tok = wave * TPW + t4 + g;
+    const int64_t t = t0 + tok;
+    uint64_t cand[EQ];
+#pragma unroll
+    for (int q = 0; q < EQ; ++q) {
+      const int e = r + 16 * q;
+      const float l = s_l[tok * EP + e];
+      cand[q] = e < E ? (((uint64_t)order_key(l) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e)) : 0ull;
+    }
+    int my_e = 0;
+    float my_l = 0.0f, l0 = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      uint64_t best = 0ull;
+#pragma unroll
+      for (int q = 0; q < EQ; ++q) best = cand[q] > best ? cand[q] : best;
+      const uint32_t key = row_max_u32((uint32_t)(best >> 32));
+      const uint32_t low = row_max_u32((uint32_t)(best >> 32) == key ? (uint32_t)best : 0u);
+      const int e = min(max((int)(0xffffffffu - low), 0), E - 1);
+      const float l = key_value(key);
+      if (j == 0) l0 = l;
+#pragma unroll
+      for (int q = 0; q < EQ; ++q)
+        if (e == r + 16 * q) cand[q] = 0ull;
+      if (r == j) {
+        my_e = e;
+        my_l = l;
+      }
+    }
+    const float ex = r < k ? expf(my_l - l0) : 0.0f;
+    const float sum = row_sum(ex);
+    if (r < k && t < T) {
+      topk_idx[t * k + r] = my_e;
+      topk_w[t * k + r] = ex / sum;
+    }
+  }
+}
+
+// Top-k of the logits of a workgroup's TB tokens, held in LDS as [TB][EP]:
+// one token per wave at a time (any k <= 64).
 template <int TB, int EP>
 __device__ __forceinline__ void route_topk(const float* s_l, int64_t T, int64_t t0, int E, int k,
                                            int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
@@ -251,7 +320,8 @@ __global__ __launch_bounds__(256) void route_kernel(int64_t T, int emb, int E, i
   }
   __syncthreads();
 
-  route_topk<TB, EP>(s_l, T, t0, E, k, topk_idx, topk_w);
+  if (k <= 16) route_topk16<TB, EP>(s_l, T, t0, E, k, topk_idx, topk_w);
+  else route_topk<TB, EP>(s_l, T, t0, E, k, topk_idx, topk_w);
 }
 
 
@@ -304,20 +374,12 @@ __global__ __launch_bounds__(256) void route_ring_kernel(int64_t T, int emb, int
   }
   const uint32_t lds_x = lds_addr(s_xr) + wave_u * (MODE == 0 ? 1024 : 512);
   const uint32_t lds_w = lds_addr(s_wr) + wave_u * kWI * 1024;
-  auto issue = [&](int sl) {
-    const int st = sl % NS;
+  auto issue = [&](int sl, int st) {  // slice sl's copies into stage st
     const uint16_t* xs = uniform_ptr(xbase + sl * kBK);
     if (MODE == 0 || lane < 32) g2lds16(xs, xoff, lds_x + st * kXS);
     const float* ws = uniform_ptr(wr + (int64_t)sl * kBK * E);
 #pragma unroll
     for (int j = 0; j < kWI; ++j) g2lds16(ws, woff[j], lds_w + st * kWS + j * 1024);
-  };
-  // Wait until the copies of slice sl have landed, given that `later` slices were issued after it.
-  auto wait_slice = [&](int later) {
-    if (later >= 3) wait_vm_n<3 * nL>();
-    else if (later == 2) wait_vm_n<2 * nL>();
-    else if (later == 1) wait_vm_n<nL>();
-    else wait_vm_n<0>();
   };
 
   const int tok_a = MODE == 0 ? lane : (lane & 31);  // A operand: this lane's token
@@ -351,24 +413,36 @@ __global__ __launch_bounds__(256) void route_ring_kernel(int64_t T, int emb, int
   };
   // Slice j: wait for slice j + 1's copies, barrier (every wave has also
   // finished reading slice j into registers, so its stage takes slice j + NS),
-  // read slice j + 1's operands, then multiply slice j.
-  for (int sl = 0; sl < NS && sl < ns; ++sl) issue(sl);
-  wait_slice(min(NS - 1, ns - 1));
+  // read slice j + 1's operands under slice j's MFMAs, one read per MFMA.
+  // Every step issues one slice's copies (past the end, a repeat of the last
+  // slice into the free stage, whose data is never read), so every wait has
+  // the same count.
+  auto step = [&](int jj, int set) {
+    wait_vm_n<(NS - 2) * nL>();
+    __syncthreads();
+    issue(min(jj + NS, ns - 1), jj % NS);
+    if (busy) {
+      read_ops(jj + 1, set ^ 1);
+      chain(set);
+#pragma unroll
+      for (int i = 0; i < 2 * kBK / 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    }
+  };
+  for (int sl = 0; sl < NS; ++sl) issue(min(sl, ns - 1), sl);
+  wait_vm_n<(NS - 1) * nL>();
   __syncthreads();
   if (busy) read_ops(0, 0);
-  for (int j = 0; j < ns; j += 2) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int jj = j + h;
-      if (jj + 1 < ns) {
-        wait_slice(min(NS - 2, ns - 2 - jj));
-        __syncthreads();
-        if (jj + NS < ns) issue(jj + NS);
-        if (busy) read_ops(jj + 1, h ^ 1);
-      }
-      if (busy) chain(h);
-    }
+  for (int j = 0; j + 2 < ns; j += 2) {
+    step(j, 0);
+    step(j + 1, 1);
   }
+  step(ns - 2, 0);
+  if (busy) chain(1);
+  wait_vm_n<0>();   // the repeated copies past the end
   __syncthreads();  // the ring now takes the logits
   float* const s_l = reinterpret_cast<float*>(s_ring);
   if (busy) {
@@ -382,7 +456,8 @@ __global__ __launch_bounds__(256) void route_ring_kernel(int64_t T, int emb, int
     }
   }
   __syncthreads();
-  route_topk<TB, EP>(s_l, T, t0, E, k, topk_idx, topk_w);
+  if (k <= 16) route_topk16<TB, EP>(s_l, T, t0, E, k, topk_idx, topk_w);
+  else route_topk<TB, EP>(s_l, T, t0, E, k, topk_idx, topk_w);
 }
 
 }  // namespace

@@ -33,7 +33,9 @@ def _route_case(T, emb, E, k, seed, bias=None):
 
 @pytest.mark.parametrize("T,emb,E,k,seed", [(64, 128, 8, 2, 1), (1000, 256, 32, 4, 2), (333, 512, 128, 8, 3),
                                             (130, 64, 256, 8, 4), (77, 128, 192, 6, 8), (70, 128, 5, 5, 5),
-                                            (17, 64, 64, 1, 6), (0, 64, 8, 2, 7)])
+                                            (17, 64, 64, 1, 6), (0, 64, 8, 2, 7),
+                                            # k > 16: one token per wave in the top-k (E % 4 != 0: register-staged kernel)
+                                            (100, 128, 64, 20, 9), (50, 64, 256, 24, 10), (40, 64, 37, 17, 11)])
 def test_route_bit_exact(T, emb, E, k, seed):
     x, wr, _ = _route_case(T, emb, E, k, seed)
     idx, w = moe.route(k, x=x.to(DEV), wr=wr.to(DEV))
