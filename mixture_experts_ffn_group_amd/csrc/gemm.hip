@@ -221,11 +221,42 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
   const int tid = opaque((int)threadIdx.x), lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const uint32_t lds_a = lds_addr(As0) + wave_u * 2 * 1024, lds_b = lds_addr(Bs0) + wave_u * 2 * 1024;
+  // Roles (every epilogue but the SwiGLU backward, which copies h through the
+  // ring): waves 0-3 issue all operand copies and no global store; waves 4-7
+  // issue all global stores (their own output, and that of waves 0-3 after
+  // it crosses one LDS stage) and no copy. vmcnt counts a wave's loads and
+  // stores together, so in a wave that does both, the wait for a k-slice
+  // issued after the previous tile's stores also waits for those stores: all
+  // workgroups store at about the same moment, and that burst held up the
+  // next tile (measured: the stores cost the wo GEMM half its time on the
+  // 32768-token workload). With the roles split, the copying waves' waits
+  // cover copies only and the stores drain while the next tile computes.
+  constexpr bool SPLIT = EPI != EPI_SWIGLU_BWD;
+  constexpr int LPW = SPLIT ? 4 : 2;  // 1 KB copies per operand, k-slice and copying wave
+  const bool loader = !SPLIT || wave_u < 4;
+  const uint32_t lds_a = lds_addr(As0) + wave_u * LPW * 1024, lds_b = lds_addr(Bs0) + wave_u * LPW * 1024;
   const int nk = p.K / GBK;
   int m0, m_end, n0;
   const uint16_t *Ab, *Bexp;
-  uint32_t a_off[2], b_off[2];
+  uint32_t a_off[LPW], b_off[LPW];
+  // the copies of a k-slice have landed once at most those of the n k-slices
+  // issued after it are outstanding (2 * LPW per k-slice); any stores in
+  // between would only make the wait longer
+  auto wait_loads_after = [](int n) {
+    if (LPW == 4) {
+      if (n >= 3) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+      else if (n == 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      else if (n == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      if (n >= 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else if (n == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+  };
+  // workgroup barrier after this wave's LDS reads have completed; unlike
+  // __syncthreads it does not wait for the wave's outstanding global stores
+  auto kbarrier = []() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
   // Tile `it` of this workgroup -> m0, m_end, n0, operand bases and per-lane offsets.
   auto decode = [&](int64_t it) -> bool {
     const int64_t tl = xcd_tile(it, blockIdx.x, gridDim.x);
@@ -254,9 +285,10 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
     n0 = __builtin_amdgcn_readfirstlane(nt * tile_n);
     Bexp = uniform_ptr(p.B + (int64_t)__builtin_amdgcn_readfirstlane(e) * p.K * p.N);
     Ab = GATHER ? p.A : uniform_ptr(p.A + (int64_t)m0 * p.K);
+    if (!loader) return true;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int row = (wave_u * 2 + j) * 16 + (lane >> 2);
+    for (int j = 0; j < LPW; ++j) {
+      const int row = (wave_u * LPW + j) * 16 + (lane >> 2);
       const int c = (lane & 3) ^ ((row >> 2) & 3);
       const int r = min(m0 + row, m_end - 1);
       if (GATHER) {
@@ -267,13 +299,13 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
       }
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < LPW; ++j) {
       if (OP == OP_NT) {
-        const int row = (wave_u * 2 + j) * 16 + (lane >> 2);
+        const int row = (wave_u * LPW + j) * 16 + (lane >> 2);
         const int c = (lane & 3) ^ ((row >> 2) & 3);
         b_off[j] = (uint32_t)(min(n0 + row, p.N - 1) * p.K + c * 8) * 2u;
       } else {
-        const int krow = (wave_u * 2 + j) * 2 + (lane >> 5);
+        const int krow = (wave_u * LPW + j) * 2 + (lane >> 5);
         const int c = (lane & 31) ^ ((krow & 3) << 2);
         int col;
         if (EPI == EPI_SWIGLU) {
@@ -289,14 +321,15 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
     return true;
   };
   auto issue_loads = [&](int kt) {
+    if (!loader) return;
     const int k0 = kt * GBK;
     const uint16_t* Ak = Ab + k0;
     const uint16_t* Bk = OP == OP_NT ? Bexp + k0 : Bexp + (int64_t)k0 * p.N;
     const uint32_t st = (uint32_t)(kt & (NST - 1)) * kOpStage;
-    g2lds16(Ak, a_off[0], lds_a + st);
-    g2lds16(Ak, a_off[1], lds_a + st + 1024);
-    g2lds16(Bk, b_off[0], lds_b + st);
-    g2lds16(Bk, b_off[1], lds_b + st + 1024);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) g2lds16(Ak, a_off[j], lds_a + st + j * 1024);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) g2lds16(Bk, b_off[j], lds_b + st + j * 1024);
   };
 
   // The first NST k-slices of a tile are issued before the previous tile's
@@ -342,8 +375,13 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
       }
     };
 
-    wait_vm_all();    // this wave's loads of the first k-slices (and the last tile's stores) are done
-    __syncthreads();
+    if (SPLIT) {
+      if (loader) wait_loads_after(min(nk, NST) - 1);  // the tile's first k-slice has landed
+      kbarrier();
+    } else {
+      wait_vm_all();  // this wave's loads of the first k-slices (and the last tile's stores) are done
+      __syncthreads();
+    }
     read_frags(0, 0, 0);
     // k-slice kt on stage kt % NST. On entry its first 16-wide sub-slice is in
     // fragment set 0. The barrier sits before the second sub-slice: every wave
@@ -358,10 +396,15 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
       mfmas(0);
       interleave();
       // loads issued after those of k-slice kt+1: k-slices kt+2 and kt+3, where they exist
-      if (kt + 3 < nk) wait_vm_8();
-      else if (kt + 2 < nk) wait_vm_4();
-      else wait_vm_all();
-      __syncthreads();
+      if (SPLIT) {
+        if (loader) wait_loads_after(kt + 3 < nk ? 2 : (kt + 2 < nk ? 1 : 0));
+        kbarrier();
+      } else {
+        if (kt + 3 < nk) wait_vm_8();
+        else if (kt + 2 < nk) wait_vm_4();
+        else wait_vm_all();
+        __syncthreads();
+      }
       if (kt + NST < nk) issue_loads(kt + NST);
       read_frags((kt + 1) & (NST - 1), 0, 0);
       mfmas(1);
@@ -381,10 +424,17 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
       }
     }
     const bool more = decode(it + 1);
-    // (the SwiGLU backward uses the operand ring in its epilogue and issues these afterwards)
-    if (EPI != EPI_SWIGLU_BWD && more)
-      for (int s = 0; s < NST; ++s)
+    // The last stage carries the copying waves' output to the storing waves
+    // and is loaded after the epilogue (the SwiGLU backward uses the whole
+    // ring in its epilogue and issues all of these afterwards).
+    if (SPLIT && more)
+      for (int s = 0; s < NST - 1; ++s)
         if (s < nk) issue_loads(s);
+    // Copying wave w's output crosses in an 8 KB region of stage NST-1 (w < 2:
+    // the A half, else the B half); storing wave w + 4 moves it to memory.
+    const int src = wave_u & 3;  // the copying wave whose output this wave handles
+    uint8_t* const xr = (src < 2 ? As0 : Bs0) + (NST - 1) * kOpStage + (src & 1) * 8192;
+    const int wm_s = src & 1, wn_s = src >> 1;
     // Epilogue. Lane holds rows m = tile row + lane%32 and, per register group q,
     // four consecutive columns 8q + 4*(lane/32) + 0..3 of each 32-wide fragment.
     // NONE and SWIGLU pass their output through this wave's 2 KB LDS staging
@@ -409,34 +459,75 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
         if (m < cm_end && c < valid_chunks) st16(reinterpret_cast<uint16_t*>(row_ptr(m)) + c * 8, v);
       }
     };
+    // A copying wave's output crosses as [rows][bytes] in its region xr, 16-byte
+    // chunk c of row rr at rr*128 + ((c ^ ((rr >> 1) & 7)) << 4) for the plain
+    // output (64 rows of 128 B per phase) and rr*64 + ((c ^ ((rr >> 2) & 3)) << 4)
+    // for the SwiGLU output (128 rows of 64 B); each storing wave reads it back
+    // in whole row segments.
+    auto xoff128 = [](int rr, int c) { return rr * 128 + ((c ^ ((rr >> 1) & 7)) << 4); };
+    auto xoff64 = [](int rr, int c) { return rr * 64 + ((c ^ ((rr >> 2) & 3)) << 4); };
     if (EPI == EPI_NONE) {
-      // Both 32-column fragments of the wave form 128-byte row segments: stage
-      // 16 rows x 128 B per round and store whole 128-byte lines, 8 lanes per row.
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float sc = sc4[i];
-        const int m0r = cm0 + wm * 128 + i * 32;
-        const int n0w = cn0 + wn * 64;
-        const int valid = min(8, (p.N - n0w) >> 3);
+      for (int ph = 0; ph < 2; ++ph) {
+        if (loader) {
+          // rows 64ph .. 64ph + 63 of this wave's 128 x 64 output block
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          if ((r >> 4) == h) {
+          for (int ii = 0; ii < 2; ++ii) {
+            const int i = 2 * ph + ii;
+            const float sc = sc4[i];
+            const int rr = ii * 32 + r;
 #pragma unroll
             for (int f = 0; f < 2; ++f)
 #pragma unroll
               for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<u32x2_t*>(stg + stg128(r - 16 * h, f * 4 + q) + hh * 8) =
+                *reinterpret_cast<u32x2_t*>(xr + xoff128(rr, f * 4 + q) + hh * 8) =
                     pack4(sc * acc[i][f][4 * q], sc * acc[i][f][4 * q + 1], sc * acc[i][f][4 * q + 2],
                           sc * acc[i][f][4 * q + 3]);
           }
+        } else if (ph == 0) {
+          // the storing wave's own output: both 32-column fragments form
+          // 128-byte row segments, staged 16 rows at a time, 8 lanes per row
 #pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            const int rr = 8 * kk + (lane >> 3), c = lane & 7;
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + stg128(rr, c));
-            const int m = m0r + 16 * h + rr;
+          for (int i = 0; i < 4; ++i) {
+            const float sc = sc4[i];
+            const int m0r = cm0 + wm * 128 + i * 32;
+            const int n0w = cn0 + wn * 64;
+            const int valid = min(8, (p.N - n0w) >> 3);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              if ((r >> 4) == h) {
+#pragma unroll
+                for (int f = 0; f < 2; ++f)
+#pragma unroll
+                  for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<u32x2_t*>(stg + stg128(r - 16 * h, f * 4 + q) + hh * 8) =
+                        pack4(sc * acc[i][f][4 * q], sc * acc[i][f][4 * q + 1], sc * acc[i][f][4 * q + 2],
+                              sc * acc[i][f][4 * q + 3]);
+              }
+#pragma unroll
+              for (int kk = 0; kk < 2; ++kk) {
+                const int rr = 8 * kk + (lane >> 3), c = lane & 7;
+                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + stg128(rr, c));
+                const int m = m0r + 16 * h + rr;
+                if (m < cm_end && c < valid) st16(p.C + (int64_t)m * p.N + n0w + c * 8, v);
+              }
+            }
+          }
+        }
+        kbarrier();  // the copying waves' rows are in LDS
+        if (!loader) {
+          const int m0r = cm0 + wm_s * 128 + ph * 64;
+          const int n0w = cn0 + wn_s * 64;
+          const int valid = min(8, (p.N - n0w) >> 3);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int rr = 8 * j + (lane >> 3), c = lane & 7;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xr + xoff128(rr, c));
+            const int m = m0r + rr;
             if (m < cm_end && c < valid) st16(p.C + (int64_t)m * p.N + n0w + c * 8, v);
           }
         }
+        kbarrier();  // read back: the region may be written again
       }
     } else if (EPI == EPI_SWIGLU) {
 #pragma unroll
@@ -454,9 +545,11 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
             uv[q][u] = sc * acc[i][1][4 * q + u];
             a[u] = silu_f(gv[q][u]) * uv[q][u];
           }
-          *reinterpret_cast<u32x2_t*>(stg + stg64(r, q) + hh * 8) = pack4(a[0], a[1], a[2], a[3]);
+          const u32x2_t pk = pack4(a[0], a[1], a[2], a[3]);
+          if (loader) *reinterpret_cast<u32x2_t*>(xr + xoff64(i * 32 + r, q) + hh * 8) = pk;
+          else *reinterpret_cast<u32x2_t*>(stg + stg64(r, q) + hh * 8) = pk;
         }
-        drain(m0r, [&](int m) { return (void*)(p.C + (int64_t)m * mlp + c0); }, min(4, (mlp - c0) >> 3));
+        if (!loader) drain(m0r, [&](int m) { return (void*)(p.C + (int64_t)m * mlp + c0); }, min(4, (mlp - c0) >> 3));
         if (p.aux_out) {  // h kept in fp32 for the backward: the gate/up values the SwiGLU used, unrounded
 #pragma unroll
           for (int part = 0; part < 4; ++part) {  // gate cols 0-15, 16-31, then up cols 0-15, 16-31
@@ -471,6 +564,20 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
           }
         }
       }
+      kbarrier();  // the copying waves' rows are in LDS
+      if (!loader) {
+        const int m0r = cm0 + wm_s * 128;
+        const int c0 = cn0 + wn_s * 32;
+        const int valid = min(4, (mlp - c0) >> 3);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int rr = 16 * j + (lane >> 2), c = lane & 3;
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xr + xoff64(rr, c));
+          const int m = m0r + rr;
+          if (m < cm_end && c < valid) st16(p.C + (int64_t)m * mlp + c0 + c * 8, v);
+        }
+      }
+      kbarrier();  // read back: the stage may be loaded
     } else {
       // EPI_SWIGLU_BWD: N = mlp, aux = saved h [M, 2N] fp32, C = dh [M, 2N] bf16.
       // Work unit (i, f): the 32 x 32 accumulator block acc[i][f]. Its gate and
@@ -551,6 +658,7 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
         for (int s = 0; s < NST; ++s)
           if (s < nk) issue_loads(s);
     }
+    if (SPLIT && more && NST - 1 < nk) issue_loads(NST - 1);
     if (!more) break;
   }
 }
