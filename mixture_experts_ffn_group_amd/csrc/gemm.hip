@@ -219,7 +219,11 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
   // valid column: both only feed outputs that are never stored. With a row
   // gather, A rows are read in place through the slot index.
   const int tid = opaque((int)threadIdx.x), lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  // Wave w owns rows 128 * (w / 4) and columns 64 * (w % 4) of the tile
+  // (wave-to-SIMD placement is w % 4), so every SIMD holds one wave of each
+  // row half; a wave whose 128 rows all lie past the group end skips its
+  // MFMAs, which halves the matrix work of each SIMD on such a tile.
+  const int wm = wave >> 2, wn = wave & 3;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   // Roles (every epilogue but the SwiGLU backward, which copies h through the
   // ring): waves 0-3 issue all operand copies and no global store; waves 4-7
@@ -382,7 +386,9 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
       wait_vm_all();  // this wave's loads of the first k-slices (and the last tile's stores) are done
       __syncthreads();
     }
-    read_frags(0, 0, 0);
+    // this wave's rows hold outputs of this tile (wave-uniform)
+    const bool active = m0 + (wave_u >> 2) * 128 < m_end;
+    if (active) read_frags(0, 0, 0);
     // k-slice kt on stage kt % NST. On entry its first 16-wide sub-slice is in
     // fragment set 0. The barrier sits before the second sub-slice: every wave
     // then holds all of stage kt % NST in registers, so the loads of k-slice
@@ -390,12 +396,8 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
     // ago) must have landed. The next stage's first fragments are read under
     // the second sub-slice's MFMAs (also on the last k-slice, where they go
     // unused: it keeps the body one basic block).
-    for (int kt = 0; kt < nk; ++kt) {
-      const int st = kt & (NST - 1);
-      read_frags(st, 1, 1);
-      mfmas(0);
-      interleave();
-      // loads issued after those of k-slice kt+1: k-slices kt+2 and kt+3, where they exist
+    // wait for k-slice kt+1 (the loads issued after it: k-slices kt+2 and kt+3, where they exist), then barrier
+    auto kwait = [&](int kt) {
       if (SPLIT) {
         if (loader) wait_loads_after(kt + 3 < nk ? 2 : (kt + 2 < nk ? 1 : 0));
         kbarrier();
@@ -405,10 +407,25 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
         else wait_vm_all();
         __syncthreads();
       }
-      if (kt + NST < nk) issue_loads(kt + NST);
-      read_frags((kt + 1) & (NST - 1), 0, 0);
-      mfmas(1);
-      interleave();
+    };
+    if (active) {
+      for (int kt = 0; kt < nk; ++kt) {
+        const int st = kt & (NST - 1);
+        read_frags(st, 1, 1);
+        mfmas(0);
+        interleave();
+        kwait(kt);
+        if (kt + NST < nk) issue_loads(kt + NST);
+        read_frags((kt + 1) & (NST - 1), 0, 0);
+        mfmas(1);
+        interleave();
+      }
+    } else {
+      // no output rows: keep the copies and barriers of the k-loop only
+      for (int kt = 0; kt < nk; ++kt) {
+        kwait(kt);
+        if (kt + NST < nk) issue_loads(kt + NST);
+      }
     }
 
     // Next tile's first loads go out now; this tile's rows and columns are kept for the epilogue.
@@ -434,7 +451,7 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
     // the A half, else the B half); storing wave w + 4 moves it to memory.
     const int src = wave_u & 3;  // the copying wave whose output this wave handles
     uint8_t* const xr = (src < 2 ? As0 : Bs0) + (NST - 1) * kOpStage + (src & 1) * 8192;
-    const int wm_s = src & 1, wn_s = src >> 1;
+    const int wm_s = src >> 2, wn_s = src & 3;
     // Epilogue. Lane holds rows m = tile row + lane%32 and, per register group q,
     // four consecutive columns 8q + 4*(lane/32) + 0..3 of each 32-wide fragment.
     // NONE and SWIGLU pass their output through this wave's 2 KB LDS staging
@@ -600,7 +617,7 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
       // (16 rows at one chunk per 16 lanes) hit distinct banks. dgate and dup
       // leave through the 2 KB staging area as 64-byte row segments.
       __syncthreads();  // every wave has read its last fragments from the ring
-      const int wm_u = wave_u & 1, wn_u = wave_u >> 1;
+      const int wm_u = wave_u >> 2, wn_u = wave_u & 3;
       const int nunits = 2 * min(4, max(0, (cm_end - (cm0 + wm_u * 128) + 31) / 32));  // wave-uniform
       const uint32_t hreg = lds_addr(smem) + wave_u * 16384;
       auto issue_h = [&](int u) {
