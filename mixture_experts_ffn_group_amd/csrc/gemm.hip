@@ -352,30 +352,35 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
         for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
 
     bf16x8_t af[2][4], bf[2][2];
-    auto read_frags = [&](int stage, int ks, int set) {
+    // NI: the 32-row blocks of the wave that are multiplied (4, or 2 when the
+    // wave's rows past the first 64 are all past the group end)
+    auto read_frags = [&](auto NIc, int stage, int ks, int set) {
+      constexpr int NI = decltype(NIc)::value;
       const uint8_t* As = As0 + stage * kOpStage;
       const uint8_t* Bs = Bs0 + stage * kOpStage;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[set][i] = frag_k4(As, lane, ks * 16, wm * 128 + i * 32);
+      for (int i = 0; i < NI; ++i) af[set][i] = frag_k4(As, lane, ks * 16, wm * 128 + i * 32);
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
         if (OP == OP_NT) bf[set][f] = frag_k4(Bs, lane, ks * 16, frag_col8<EPI>(wn, f));
         else bf[set][f] = frag_tr(Bs, lane, ks * 16, frag_col8<EPI>(wn, f));
       }
     };
-    auto mfmas = [&](int set) {
+    auto mfmas = [&](auto NIc, int set) {
+      constexpr int NI = decltype(NIc)::value;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int f = 0; f < 2; ++f) acc[i][f] = mfma(bf[set][f], af[set][i], acc[i][f]);
     };
     // Issue order inside a 16-wide sub-slice: one MFMA, then one LDS read of the
-    // next sub-slice's fragments.
-    auto interleave = [&]() {
+    // next sub-slice's fragments (two per MFMA with two row blocks).
+    auto interleave = [&](auto NIc) {
+      constexpr int NI = decltype(NIc)::value;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 2 * NI; ++j) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, NI == 4 ? 1 : 2, 0);
       }
     };
 
@@ -386,9 +391,10 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
       wait_vm_all();  // this wave's loads of the first k-slices (and the last tile's stores) are done
       __syncthreads();
     }
-    // this wave's rows hold outputs of this tile (wave-uniform)
-    const bool active = m0 + (wave_u >> 2) * 128 < m_end;
-    if (active) read_frags(0, 0, 0);
+    // rows of this tile that hold outputs, from this wave's first row (wave-uniform)
+    const int wrows = m_end - (m0 + (wave_u >> 2) * 128);
+    using NI4 = std::integral_constant<int, 4>;
+    using NI2 = std::integral_constant<int, 2>;
     // k-slice kt on stage kt % NST. On entry its first 16-wide sub-slice is in
     // fragment set 0. The barrier sits before the second sub-slice: every wave
     // then holds all of stage kt % NST in registers, so the loads of k-slice
@@ -408,18 +414,24 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
         __syncthreads();
       }
     };
-    if (active) {
+    auto kloop = [&](auto NIc) {
+      read_frags(NIc, 0, 0, 0);
       for (int kt = 0; kt < nk; ++kt) {
         const int st = kt & (NST - 1);
-        read_frags(st, 1, 1);
-        mfmas(0);
-        interleave();
+        read_frags(NIc, st, 1, 1);
+        mfmas(NIc, 0);
+        interleave(NIc);
         kwait(kt);
         if (kt + NST < nk) issue_loads(kt + NST);
-        read_frags((kt + 1) & (NST - 1), 0, 0);
-        mfmas(1);
-        interleave();
+        read_frags(NIc, (kt + 1) & (NST - 1), 0, 0);
+        mfmas(NIc, 1);
+        interleave(NIc);
       }
+    };
+    if (wrows > 64) {
+      kloop(NI4{});
+    } else if (wrows > 0) {
+      kloop(NI2{});  // blocks 2 and 3 keep their zero accumulators; their rows are not stored
     } else {
       // no output rows: keep the copies and barriers of the k-loop only
       for (int kt = 0; kt < nk; ++kt) {
