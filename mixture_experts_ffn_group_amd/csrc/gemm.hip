@@ -741,7 +741,18 @@ __global__ __launch_bounds__(GTHR, 1) void wgrad_kernel(WgradP p) {
   const int tid = opaque((int)threadIdx.x), lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const uint32_t lds_a = lds_addr(As0) + wave_u * 2 * 1024, lds_d = lds_addr(Ds0) + wave_u * 2 * 1024;
+  // Copying waves 0-3 and storing waves 4-7, as in gemm_kernel: the output
+  // (dW, several times the operands) leaves through waves that never wait
+  // on vmcnt, and the copying waves' waits cover copies only.
+  const bool loader = wave_u < 4;
+  const uint32_t lds_a = lds_addr(As0) + wave_u * 4 * 1024, lds_d = lds_addr(Ds0) + wave_u * 4 * 1024;
+  auto wait_loads_after = [](int n) {  // 8 copies per k-slice and copying wave
+    if (n >= 3) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+    else if (n == 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if (n == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  auto kbarrier = []() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
   // Per tile: expert e, output block (p0, q0), the group's rows [lo, lo + n), nk k-slices.
   // Loader (both operands [k][n] tiles of 32 rows x 512 bytes): block b = 2*wave + j
@@ -749,6 +760,9 @@ __global__ __launch_bounds__(GTHR, 1) void wgrad_kernel(WgradP p) {
   // logical chunk (L%32) ^ ((k-row & 3) << 2). Columns past P or Q read other
   // bytes of the slice (or zeros) and only feed outputs that are never stored.
   int e = 0, p0 = 0, q0 = 0, lo = 0, n = 0, nk = 0;
+  // copy j of a k-slice covers k-rows 8*wave + 2j + {0, 1}; copies j and j + 2
+  // share the chunk swizzle ((2j + lane/32) & 3 repeats with period 2) and lie
+  // 4 k-rows apart, so only j = 0, 1 are kept
   uint32_t a_off[2], d_off[2];
   // Tiles are dealt by expert: XCD x (workgroups w with w % 8 == x) takes
   // experts x, x + 8, ..., each expert's tiles in turn over its G / 8
@@ -772,9 +786,10 @@ __global__ __launch_bounds__(GTHR, 1) void wgrad_kernel(WgradP p) {
     lo = __builtin_amdgcn_readfirstlane(l0);
     n = __builtin_amdgcn_readfirstlane(h0 > l0 ? h0 - l0 : 0);
     nk = (n + GBK - 1) / GBK;
+    if (!loader) return true;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int krow = (wave_u * 2 + j) * 2 + (lane >> 5);
+      const int krow = (wave_u * 4 + j) * 2 + (lane >> 5);
       const int c = (lane & 31) ^ ((krow & 3) << 2);
       a_off[j] = (uint32_t)(krow * p.P + p0 + c * 8) * 2u;
       d_off[j] = (uint32_t)(krow * p.Q + q0 + c * 8) * 2u;
@@ -782,14 +797,15 @@ __global__ __launch_bounds__(GTHR, 1) void wgrad_kernel(WgradP p) {
     return true;
   };
   auto issue_loads = [&](int kt) {
+    if (!loader) return;
     const int r0 = lo + kt * GBK, rows = min(GBK, n - kt * GBK);
     const i32x4_t ra = buffer_rsrc(p.A + (int64_t)r0 * p.P, (uint32_t)(rows * p.P * 2));
     const i32x4_t rd = buffer_rsrc(p.D + (int64_t)r0 * p.Q, (uint32_t)(rows * p.Q * 2));
     const uint32_t st = (uint32_t)(kt & (NST - 1)) * kOpStage;
-    b2lds16(ra, a_off[0], lds_a + st);
-    b2lds16(ra, a_off[1], lds_a + st + 1024);
-    b2lds16(rd, d_off[0], lds_d + st);
-    b2lds16(rd, d_off[1], lds_d + st + 1024);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b2lds16(ra, a_off[j & 1] + (uint32_t)((j >> 1) * 8 * p.P), lds_a + st + j * 1024);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b2lds16(rd, d_off[j & 1] + (uint32_t)((j >> 1) * 8 * p.Q), lds_d + st + j * 1024);
   };
 
   if (!decode(0)) return;
@@ -833,8 +849,8 @@ __global__ __launch_bounds__(GTHR, 1) void wgrad_kernel(WgradP p) {
       }
     };
 
-    wait_vm_all();    // this wave's loads of the first k-slices (and the last tile's stores) are done
-    __syncthreads();
+    if (loader) wait_loads_after(min(nk, NST) - 1);  // the tile's first k-slice has landed
+    kbarrier();
     read_frags(0, 0, 0);
     // same k-slice schedule as gemm_kernel
     for (int kt = 0; kt < nk; ++kt) {
@@ -842,10 +858,8 @@ __global__ __launch_bounds__(GTHR, 1) void wgrad_kernel(WgradP p) {
       read_frags(st, 1, 1);
       mfmas(0);
       interleave();
-      if (kt + 3 < nk) wait_vm_8();
-      else if (kt + 2 < nk) wait_vm_4();
-      else wait_vm_all();
-      __syncthreads();
+      if (loader) wait_loads_after(kt + 3 < nk ? 2 : (kt + 2 < nk ? 1 : 0));
+      kbarrier();
       if (kt + NST < nk) issue_loads(kt + NST);
       read_frags((kt + 1) & (NST - 1), 0, 0);
       mfmas(1);
@@ -854,41 +868,79 @@ __global__ __launch_bounds__(GTHR, 1) void wgrad_kernel(WgradP p) {
 
     const int ce = e, cp0 = p0, cq0 = q0;
     const bool more = decode(it + 1);
+    // the last stage carries the copying waves' output; it is loaded after the epilogue
     if (more)
-      for (int s = 0; s < NST; ++s)
+      for (int s = 0; s < NST - 1; ++s)
         if (s < nk) issue_loads(s);
-    // Epilogue through this wave's staging area, 16 rows x 128 bytes at a time (as in gemm_kernel).
+    // Epilogue: 128-byte row segments (a wave's 64 columns), non-temporal: the
+    // output is several times the operands and is not read back here, so it
+    // streams past L2 instead of evicting the operand panels the next tiles read.
     const int hh = lane >> 5, r = lane & 31;
     uint8_t* const stg = s_stage[wave];
     auto stg128 = [&](int rr, int c) { return rr * 128 + ((c ^ ((rr >> 1) & 7)) << 4); };
     uint16_t* const Ce = p.C + (int64_t)ce * p.P * p.Q;
-    const int qw = cq0 + wn * 64;
-    const int valid = min(8, (p.Q - qw) >> 3);
+    // copying wave src's output crosses in 8 KB of stage NST-1, 64 rows x 128 B per phase
+    const int src = wave_u & 3;
+    uint8_t* const xr = (src < 2 ? As0 : Ds0) + (NST - 1) * kOpStage + (src & 1) * 8192;
+    const int wm_s = src & 1, wn_s = src >> 1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int pr0 = cp0 + wm * 128 + i * 32;
+    for (int ph = 0; ph < 2; ++ph) {
+      if (loader) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if ((r >> 4) == h) {
+        for (int ii = 0; ii < 2; ++ii) {
+          const int i = 2 * ph + ii, rr = ii * 32 + r;
 #pragma unroll
           for (int f = 0; f < 2; ++f)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              *reinterpret_cast<u32x2_t*>(stg + stg128(r - 16 * h, f * 4 + q) + hh * 8) =
+              *reinterpret_cast<u32x2_t*>(xr + stg128(rr, f * 4 + q) + hh * 8) =
                   pack4(acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]);
         }
+      } else if (ph == 0) {
+        // the storing wave's own output, staged 16 rows x 128 B at a time
+        const int qw = cq0 + wn * 64;
+        const int valid = min(8, (p.Q - qw) >> 3);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int rr = 8 * kk + (lane >> 3), c = lane & 7;
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + stg128(rr, c));
-          const int pr = pr0 + 16 * h + rr;
-          // non-temporal: the output is several times the operands and is not read back here, so it
-          // streams past L2 instead of evicting the operand panels the next tiles read
+        for (int i = 0; i < 4; ++i) {
+          const int pr0 = cp0 + wm * 128 + i * 32;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            if ((r >> 4) == h) {
+#pragma unroll
+              for (int f = 0; f < 2; ++f)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                  *reinterpret_cast<u32x2_t*>(stg + stg128(r - 16 * h, f * 4 + q) + hh * 8) =
+                      pack4(acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]);
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+              const int rr = 8 * kk + (lane >> 3), c = lane & 7;
+              const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + stg128(rr, c));
+              const int pr = pr0 + 16 * h + rr;
+              if (pr < p.P && c < valid)
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(Ce + (int64_t)pr * p.Q + qw + c * 8));
+            }
+          }
+        }
+      }
+      kbarrier();  // the copying waves' rows are in LDS
+      if (!loader) {
+        const int pr0 = cp0 + wm_s * 128 + ph * 64;
+        const int qw = cq0 + wn_s * 64;
+        const int valid = min(8, (p.Q - qw) >> 3);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int rr = 8 * j + (lane >> 3), c = lane & 7;
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xr + stg128(rr, c));
+          const int pr = pr0 + rr;
           if (pr < p.P && c < valid)
             __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(Ce + (int64_t)pr * p.Q + qw + c * 8));
         }
       }
+      kbarrier();  // read back: the region may be written again
     }
+    if (more && NST - 1 < nk) issue_loads(NST - 1);
     if (!more) break;
   }
 }
