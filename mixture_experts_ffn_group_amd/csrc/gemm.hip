@@ -38,6 +38,11 @@
 //    on a contiguous run of tiles that share A and B panels in its L2; the
 //    first k-slices of a workgroup's next tile are loaded during the epilogue
 //    of the current one.
+//  - Waves 0-3 issue all operand copies and waves 4-7 all output stores
+//    (non-temporal), so no wave's vmcnt waits cover stores; the copying
+//    waves' output reaches the storing waves through the last ring stage.
+//  - A wave whose 128 rows lie past the group end skips its MFMAs, and one
+//    with at most 64 output rows multiplies only its first two 32-row blocks.
 #include <type_traits>
 
 #include "common.h"
