@@ -236,6 +236,24 @@ def main():
         torch.cuda.synchronize()
         fused_ms = e0.elapsed_time(e1) / args.steps
 
+    # The combine again, alone, with the 256 MB MALL (Infinity Cache) flushed before each launch: in the step
+    # it reads o right after GEMM 2 wrote it, so part of o may still be in the MALL there. The flush writes a
+    # 512 MB buffer and then reads it back, so that its own dirty lines are written back before the launch.
+    comb_call = dict(calls)["combine"]
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+    for c0, c1 in cold_evs:
+        flush.fill_(1)
+        flush.view(torch.int32).sum()
+        c0.record(stream)
+        rc = comb_call()
+        c1.record(stream)
+        if rc != 0:
+            raise _lib.MoeError(rc, "combine", L.moe_last_error_detail().decode())
+    torch.cuda.synchronize()
+    comb_cold_ms = float(np.mean([c0.elapsed_time(c1) for c0, c1 in cold_evs]))
+    del flush
+
     gs = saved["group_sizes"].cpu().numpy()
     e_nz = int((gs > 0).sum())
     ms_step = wall * 1e3 / args.steps
@@ -276,7 +294,9 @@ def main():
                       peak=gpeak, unit="TFLOP/s", flop=g2_flop, bytes=g2_bytes,
                       hbm_gbs=gb(g2_bytes, stage_ms["gemm2"])),
         "combine": dict(ms=stage_ms["combine"], bound="hbm", achieved=gb(comb_bytes, stage_ms["combine"]),
-                        peak=PEAK_HBM_GBS, unit="GB/s", bytes=comb_bytes),
+                        peak=PEAK_HBM_GBS, unit="GB/s", bytes=comb_bytes,
+                        mall_flushed=dict(ms=round(comb_cold_ms, 5), achieved=round(gb(comb_bytes, comb_cold_ms), 2),
+                                          frac=round(gb(comb_bytes, comb_cold_ms) / PEAK_HBM_GBS, 4))),
     }
     if mx:
         stages["permute"]["rows"] = "index only; GEMM1 gathers the quantized x rows"
