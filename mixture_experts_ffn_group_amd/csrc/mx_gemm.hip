@@ -27,6 +27,8 @@
 // k-slice is 64 elements (64 bytes per row, one MFMA deep); with it travel
 // the two operands' scale dwords of the tile's 256 rows (waves 0-3 copy the A
 // rows', waves 4-7 the B rows'), so every wave issues 5 copies per k-slice.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -141,7 +143,10 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
   }
   const int total = s_pref[p.E];
   const int tid = mx_opaque((int)threadIdx.x), lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1, h = lane >> 5;
+  // Wave w owns row half w / 4 and column quarter w % 4 (SIMD w % 4 holds one
+  // wave of each row half), so a wave whose rows lie past the group end can
+  // skip its MFMAs, as in the bf16 grouped GEMM.
+  const int wm = wave >> 2, wn = wave & 3, h = lane >> 5;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds0 = mx_lds_addr(smem);
   const int nk = p.K / 64;
@@ -237,37 +242,56 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
 
     mx_wait_all();  // this wave's loads of the first k-slices (and the last tile's stores) are done
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const uint8_t* stg = smem + (kt & (MXN - 1)) * kMxStage;
-      const uint8_t* As_t = stg;
-      const uint8_t* Bs_t = stg + kMxOp;
-      const uint8_t* Asc = stg + 2 * kMxOp;
-      const uint8_t* Bsc = Asc + kMxScl;
-      i32x8_t af[4], bf[2];
-      int sa[4], sb[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wm * 128 + i * 32 + (lane & 31);
-        af[i] = mx_frag(As_t, row, h);
-        sa[i] = Asc[row * 4 + h];
-      }
-#pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        const int row = mx_col<EPI>(wn, f) + (lane & 31);
-        bf[f] = mx_frag(Bs_t, row, h);
-        sb[f] = Bsc[row * 4 + h];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int f = 0; f < 2; ++f)
-          acc[i][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[f], af[i], acc[i][f], 0, 0, 0, sb[f], 0, sa[i]);
-      // k-slice kt+1 has landed; younger are the copies of k-slices kt+2 and kt+3, where they exist
+    // k-slice kt+1 has landed (younger are the copies of k-slices kt+2 and kt+3, where they exist);
+    // every wave has read stage kt (its MFMAs consumed it) and k-slice kt+1 is visible
+    auto kwait = [&](int kt) {
       if (kt + 3 < nk) mx_wait_10();
       else if (kt + 2 < nk) mx_wait_5();
       else mx_wait_all();
-      __syncthreads();  // every wave has read stage kt (its MFMAs consumed it); k-slice kt+1 is visible
+      __syncthreads();
       if (kt + MXN < nk) issue_loads(kt + MXN);
+    };
+    // NI: the 32-row blocks of the wave that are multiplied (4, or 2 when its
+    // rows past the first 64 are all past the group end)
+    auto kloop = [&](auto NIc) {
+      constexpr int NI = decltype(NIc)::value;
+      for (int kt = 0; kt < nk; ++kt) {
+        const uint8_t* stg = smem + (kt & (MXN - 1)) * kMxStage;
+        const uint8_t* As_t = stg;
+        const uint8_t* Bs_t = stg + kMxOp;
+        const uint8_t* Asc = stg + 2 * kMxOp;
+        const uint8_t* Bsc = Asc + kMxScl;
+        i32x8_t af[NI], bf[2];
+        int sa[NI], sb[2];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int row = wm * 128 + i * 32 + (lane & 31);
+          af[i] = mx_frag(As_t, row, h);
+          sa[i] = Asc[row * 4 + h];
+        }
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const int row = mx_col<EPI>(wn, f) + (lane & 31);
+          bf[f] = mx_frag(Bs_t, row, h);
+          sb[f] = Bsc[row * 4 + h];
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int f = 0; f < 2; ++f)
+            acc[i][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[f], af[i], acc[i][f], 0, 0, 0, sb[f], 0,
+                                                                          sa[i]);
+        kwait(kt);
+      }
+    };
+    // rows of this tile that hold outputs, from this wave's first row (wave-uniform)
+    const int wrows = m_end - (m0 + (wave_u >> 2) * 128);
+    if (wrows > 64) {
+      kloop(std::integral_constant<int, 4>{});
+    } else if (wrows > 0) {
+      kloop(std::integral_constant<int, 2>{});  // blocks 2 and 3 keep zero accumulators; their rows are not stored
+    } else {
+      for (int kt = 0; kt < nk; ++kt) kwait(kt);  // no output rows: the waits, barriers and copies only
     }
 
     const int cm0 = m0, cm_end = m_end, cn0 = n0;

@@ -113,6 +113,28 @@ def test_grouped_gemm_mx_matches_oracle(M, K, N, E, empty, epi):
     if epi == "swiglu" and N % 16:
         N += 8
     x, w, off = _mx_case(M, K, N, E, M + K, empty)
+    _check_mx_gemm(x, w, off, epi)
+
+
+# Groups whose last 256-row tile ends at every 32-row block boundary of either half of the tile, and just past
+# them, plus an empty group: every k-loop form of the tile (four blocks, two blocks, none).
+MX_PARTIAL_SIZES = [1, 32, 33, 64, 65, 128, 129, 160, 224, 255, 256, 257, 300, 543, 0]
+
+
+@pytest.mark.parametrize("epi", ["none", "swiglu"])
+def test_grouped_gemm_mx_partial_tiles_every_block_count(epi):
+    rng = np.random.default_rng(11)
+    sizes = np.array(MX_PARTIAL_SIZES, np.int64)
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M, K, N, E = int(off[-1]), 128, 256, len(sizes)
+    x = _bf16(rng.standard_normal((M, K)))
+    w = _bf16(rng.standard_normal((E, K, N)) * (1.0 / np.sqrt(K)))
+    _check_mx_gemm(x, w, off, epi)
+
+
+def _check_mx_gemm(x, w, off, epi):
+    M, K = x.shape
+    E, _, N = w.shape
     ac, as_ = moe.mx_quantize_rows(x.to(DEV))
     bc, bs = moe.mx_quantize_weight(w.to(DEV))
     offd = torch.from_numpy(off).to(DEV)
