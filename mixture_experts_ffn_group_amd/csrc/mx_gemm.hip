@@ -68,6 +68,8 @@ __device__ __forceinline__ void mx_g2lds4(const void* sbase, uint32_t voff, uint
 __device__ __forceinline__ void mx_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void mx_wait_5() { asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); }
 __device__ __forceinline__ void mx_wait_10() { asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); }
+__device__ __forceinline__ void mx_wait_20() { asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); }
+__device__ __forceinline__ void mx_wait_30() { asm volatile("s_waitcnt vmcnt(30)" ::: "memory"); }
 __device__ __forceinline__ uint32_t mx_lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -148,6 +150,14 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
   // skip its MFMAs, as in the bf16 grouped GEMM.
   const int wm = wave >> 2, wn = wave & 3, h = lane >> 5;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // Plain output (the wo GEMM): waves 0-3 issue every operand and scale copy
+  // and no global store, waves 4-7 every store (non-temporal), as in the bf16
+  // grouped GEMM; the copying waves' output crosses through the last ring
+  // stage. Without its stores this GEMM runs in about half the time on the
+  // 32768-token workload. The SwiGLU form keeps every wave copying and storing.
+  constexpr bool SPLIT = EPI == MXE_NONE;
+  constexpr int LPW = SPLIT ? 4 : 2;  // 1 KB copies per operand, k-slice and copying wave
+  const bool loader = !SPLIT || wave_u < 4;
   const uint32_t lds0 = mx_lds_addr(smem);
   const int nk = p.K / 64;
   const int nslice_rows = p.a_rows;  // rows of A's scale slices
@@ -160,7 +170,7 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
   int m0 = 0, m_end = 0, n0 = 0, e = 0;
   const uint8_t* Bexp = p.B;
   const uint8_t* Bsexp = p.Bs;
-  uint32_t a_off[2], b_off[2], s_off;
+  uint32_t a_off[LPW], b_off[LPW], s_off, s_off2 = 0;
   auto decode = [&](int64_t it) -> bool {
     const int64_t tl = xcd_tile(it, blockIdx.x, gridDim.x);
     if (tl >= total) return false;
@@ -182,10 +192,11 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
     n0 = __builtin_amdgcn_readfirstlane(nt * tile_n);
     Bexp = mx_uniform(p.B + (int64_t)e * p.N * p.K);
     Bsexp = mx_uniform(p.Bs + (int64_t)e * nk * p.N * 4);
-    // tile rows: block b = 2*wave + j holds rows 16b .. 16b+15; lane L -> row 16b + L/4, physical chunk L%4
+    if (!loader) return true;
+    // tile rows: block b = LPW*wave + j holds rows 16b .. 16b+15; lane L -> row 16b + L/4, physical chunk L%4
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int row = (wave_u * 2 + j) * 16 + (lane >> 2);
+    for (int j = 0; j < LPW; ++j) {
+      const int row = (wave_u * LPW + j) * 16 + (lane >> 2);
       const int c = (lane & 3) ^ ((row >> 2) & 3);
       const int r = a_row(min(m0 + row, m_end - 1));
       a_off[j] = (uint32_t)r * (uint32_t)p.K + (uint32_t)c * 16u;
@@ -198,8 +209,13 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
       }
       b_off[j] = (uint32_t)n * (uint32_t)p.K + (uint32_t)c * 16u;
     }
-    // scale rows: waves 0-3 copy A rows 64*wave + L, waves 4-7 B rows 64*(wave-4) + L
-    {
+    // scale rows: waves 0-3 copy A rows 64*wave + L, waves 4-7 B rows 64*(wave-4) + L (with the
+    // roles split, waves 0-3 copy both: s_off for A, s_off2 for B)
+    if (SPLIT) {
+      const int row = wave_u * 64 + lane;
+      s_off = (uint32_t)a_row(min(m0 + row, m_end - 1)) * 4u;
+      s_off2 = (uint32_t)(n0 + row < p.N ? n0 + row : p.N - 1) * 4u;
+    } else {
       const int row = (wave_u & 3) * 64 + lane;
       if (wave_u < 4) {
         s_off = (uint32_t)a_row(min(m0 + row, m_end - 1)) * 4u;
@@ -217,15 +233,33 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
     return true;
   };
   auto issue_loads = [&](int kt) {
+    if (!loader) return;
     const uint32_t st = lds0 + (uint32_t)(kt & (MXN - 1)) * kMxStage;
     const uint8_t* Ak = p.A + (int64_t)kt * 64;
     const uint8_t* Bk = Bexp + (int64_t)kt * 64;
-    mx_g2lds16(Ak, a_off[0], st + wave_u * 2048);
-    mx_g2lds16(Ak, a_off[1], st + wave_u * 2048 + 1024);
-    mx_g2lds16(Bk, b_off[0], st + kMxOp + wave_u * 2048);
-    mx_g2lds16(Bk, b_off[1], st + kMxOp + wave_u * 2048 + 1024);
-    if (wave_u < 4) mx_g2lds4(p.As + (int64_t)kt * nslice_rows * 4, s_off, st + 2 * kMxOp + wave_u * 256);
-    else mx_g2lds4(Bsexp + (int64_t)kt * p.N * 4, s_off, st + 2 * kMxOp + kMxScl + (wave_u - 4) * 256);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) mx_g2lds16(Ak, a_off[j], st + wave_u * LPW * 1024 + j * 1024);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) mx_g2lds16(Bk, b_off[j], st + kMxOp + wave_u * LPW * 1024 + j * 1024);
+    if (SPLIT) {
+      mx_g2lds4(p.As + (int64_t)kt * nslice_rows * 4, s_off, st + 2 * kMxOp + wave_u * 256);
+      mx_g2lds4(Bsexp + (int64_t)kt * p.N * 4, s_off2, st + 2 * kMxOp + kMxScl + wave_u * 256);
+    } else if (wave_u < 4) {
+      mx_g2lds4(p.As + (int64_t)kt * nslice_rows * 4, s_off, st + 2 * kMxOp + wave_u * 256);
+    } else {
+      mx_g2lds4(Bsexp + (int64_t)kt * p.N * 4, s_off, st + 2 * kMxOp + kMxScl + (wave_u - 4) * 256);
+    }
+  };
+  // workgroup barrier after this wave's LDS reads; unlike __syncthreads it
+  // does not wait for the wave's outstanding global stores
+  auto kbarrier = []() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  // the copies of a k-slice have landed once at most those of the n k-slices issued after it are
+  // outstanding (10 per k-slice and copying wave with the roles split)
+  auto wait_after = [](int n) {
+    if (n >= 3) mx_wait_30();
+    else if (n == 2) mx_wait_20();
+    else if (n == 1) mx_wait_10();
+    else mx_wait_all();
   };
 
   if (!decode(0)) return;
@@ -240,15 +274,25 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
 
-    mx_wait_all();  // this wave's loads of the first k-slices (and the last tile's stores) are done
-    __syncthreads();
+    if (SPLIT) {
+      if (loader) wait_after(min(nk, MXN) - 1);  // the tile's first k-slice has landed
+      kbarrier();
+    } else {
+      mx_wait_all();  // this wave's loads of the first k-slices (and the last tile's stores) are done
+      __syncthreads();
+    }
     // k-slice kt+1 has landed (younger are the copies of k-slices kt+2 and kt+3, where they exist);
     // every wave has read stage kt (its MFMAs consumed it) and k-slice kt+1 is visible
     auto kwait = [&](int kt) {
-      if (kt + 3 < nk) mx_wait_10();
-      else if (kt + 2 < nk) mx_wait_5();
-      else mx_wait_all();
-      __syncthreads();
+      if (SPLIT) {
+        if (loader) wait_after(kt + 3 < nk ? 2 : (kt + 2 < nk ? 1 : 0));
+        kbarrier();
+      } else {
+        if (kt + 3 < nk) mx_wait_10();
+        else if (kt + 2 < nk) mx_wait_5();
+        else mx_wait_all();
+        __syncthreads();
+      }
       if (kt + MXN < nk) issue_loads(kt + MXN);
     };
     // NI: the 32-row blocks of the wave that are multiplied (4, or 2 when its
@@ -296,8 +340,9 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
 
     const int cm0 = m0, cm_end = m_end, cn0 = n0;
     const bool more = decode(it + 1);
+    // with the roles split, the last stage carries the copying waves' output and is loaded after the epilogue
     if (more)
-      for (int s = 0; s < MXN; ++s)
+      for (int s = 0; s < (SPLIT ? MXN - 1 : MXN); ++s)
         if (s < nk) issue_loads(s);
     // Epilogue through this wave's 2 KB staging area (as the bf16 grouped GEMM): lane holds rows
     // m = tile row + lane%32 and, per register group q, columns 8q + 4*(lane/32) + 0..3 of a 32-wide block.
@@ -307,30 +352,68 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
     auto stg128 = [&](int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); };
     const int r = lane & 31;
     if (EPI == MXE_NONE) {
+      // Copying wave src's 128 x 64 block crosses in 8 KB of the last stage, 64 rows x 128 B per phase
+      // (16-byte chunk c of row rr at rr*128 + ((c ^ ((rr >> 1) & 7)) << 4)); storing wave src + 4 stores it.
+      const int src = wave_u & 3;
+      uint8_t* const xr = smem + (MXN - 1) * kMxStage + (src < 2 ? 0 : kMxOp) + (src & 1) * 8192;
+      const int wm_s = src >> 2, wn_s = src & 3;
+      auto sto = [](uint16_t* ptr, u32x4_t v) { __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(ptr)); };
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m0r = cm0 + wm * 128 + i * 32;
-        const int n0w = cn0 + wn * 64;
-        const int valid = min(8, (p.N - n0w) >> 3);
+      for (int ph = 0; ph < 2; ++ph) {
+        if (loader) {
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          if ((r >> 4) == hf) {
+          for (int ii = 0; ii < 2; ++ii) {
+            const int i = 2 * ph + ii, rr = ii * 32 + r;
 #pragma unroll
             for (int f = 0; f < 2; ++f)
 #pragma unroll
               for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<u32x2_t*>(stg + stg128(r - 16 * hf, f * 4 + q) + hh * 8) =
+                *reinterpret_cast<u32x2_t*>(xr + stg128(rr, f * 4 + q) + hh * 8) =
                     mx_pack4(acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]);
           }
+        } else if (ph == 0) {
+          // the storing wave's own block, 16 rows x 128 B at a time through its staging area
 #pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            const int rr = 8 * kk + (lane >> 3), c = lane & 7;
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + stg128(rr, c));
-            const int m = m0r + 16 * hf + rr;
-            if (m < cm_end && c < valid) st16(p.C + (int64_t)m * p.N + n0w + c * 8, v);
+          for (int i = 0; i < 4; ++i) {
+            const int m0r = cm0 + wm * 128 + i * 32;
+            const int n0w = cn0 + wn * 64;
+            const int valid = min(8, (p.N - n0w) >> 3);
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+              if ((r >> 4) == hf) {
+#pragma unroll
+                for (int f = 0; f < 2; ++f)
+#pragma unroll
+                  for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<u32x2_t*>(stg + stg128(r - 16 * hf, f * 4 + q) + hh * 8) =
+                        mx_pack4(acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]);
+              }
+#pragma unroll
+              for (int kk = 0; kk < 2; ++kk) {
+                const int rr = 8 * kk + (lane >> 3), c = lane & 7;
+                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + stg128(rr, c));
+                const int m = m0r + 16 * hf + rr;
+                if (m < cm_end && c < valid) sto(p.C + (int64_t)m * p.N + n0w + c * 8, v);
+              }
+            }
           }
         }
+        kbarrier();  // the copying waves' rows are in LDS
+        if (!loader) {
+          const int m0r = cm0 + wm_s * 128 + ph * 64;
+          const int n0w = cn0 + wn_s * 64;
+          const int valid = min(8, (p.N - n0w) >> 3);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int rr = 8 * j + (lane >> 3), c = lane & 7;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xr + stg128(rr, c));
+            const int m = m0r + rr;
+            if (m < cm_end && c < valid) sto(p.C + (int64_t)m * p.N + n0w + c * 8, v);
+          }
+        }
+        kbarrier();  // read back: the region may be written again
       }
+      if (more && MXN - 1 < nk) issue_loads(MXN - 1);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
