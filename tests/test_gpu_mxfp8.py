@@ -274,43 +274,42 @@ def test_ffn_fwd_mx_with_no_tokens_is_a_no_op():
 
 
 @pytest.mark.slow
-def test_ffn_fwd_mx_full_size_sampled():
-    """The 32768-token workload through moe_ffn_fwd_mx (the kernels and launch configuration that the MXFP8
+@pytest.mark.parametrize("name,extra", [("gemma4_class", 22), ("deepseek_v3_shape", 0)])
+def test_ffn_fwd_mx_full_size_sampled(name, extra):
+    """A full-size workload through moe_ffn_fwd_mx (the kernels and launch configuration that the MXFP8
     bench times) against the oracle composition on sampled tokens. Every stage of the reference is the
-    oracle's: routing of all tokens, quantization of the sampled token rows and of the experts' weights,
+    oracle's: routing of the sampled tokens, quantization of their rows and of the picked experts' weights,
     float64 GEMMs on the dequantized operands, the SwiGLU output rounded to bf16 and quantized, bf16
-    rounding of GEMM 2, and the combine."""
+    rounding of GEMM 2, and the combine. Routing, the row quantization and the GEMMs act per token row
+    and per expert, so taking them one sampled token and one expert at a time gives the values the
+    whole-workload computation has for those tokens."""
     from parity_util import assert_close, to_np
-    d = workloads.make_inputs("gemma4_class", device=DEV)  # drawn on the device, copied to the host once
-    h = {kk: (v.cpu() if isinstance(v, torch.Tensor) else v) for kk, v in d.items()}
-    wl = h["workload"]
+    d = workloads.make_inputs(name, device=DEV)
+    wl = d["workload"]
     T, k = wl.T, wl.k
     wq = moe.mx_quantize_expert_weights(d["wi"], d["wo"])
     y = moe.ffn_fwd_mx(d["x"], wq, k, wr=d["wr"], bias=d["bias"])
     torch.cuda.synchronize()
-    xb = bits(h["x"])
-    idx, w, _ = oracle.route(xb, h["wr"].numpy(), None if h["bias"] is None else h["bias"].numpy(), k)
     rng = np.random.default_rng(wl.seed)
-    toks = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 22, replace=False)])).astype(np.int64)
+    toks = np.unique(np.concatenate([[0, T - 1], rng.choice(T, extra, replace=False)])).astype(np.int64)
+    xb = bits(d["x"][torch.from_numpy(toks).to(DEV)])
+    idx, w, _ = oracle.route(xb, d["wr"].cpu().numpy(), None if d["bias"] is None else d["bias"].cpu().numpy(), k)
     # the sampled (token, pick) pairs, ordered by expert (then token), as group rows of the reference GEMMs
-    pairs = sorted(((int(idx[t, j]), i, j) for i, t in enumerate(toks) for j in range(k)))
-    used = sorted({e for e, _, _ in pairs})
-    sizes = np.array([sum(1 for e, _, _ in pairs if e == u) for u in used], np.int64)
-    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
-    xc, xs_ = oracle.mx_quantize(xb[toks])  # per-row quantization: the same as quantizing every row
-    a_codes = np.stack([xc[i] for _, i, _ in pairs])
-    a_scales = np.stack([xs_[i] for _, i, _ in pairs])
-    wi_b, wo_b = bits(h["wi"]), bits(h["wo"])
-    wiq = [oracle.mx_quantize(np.ascontiguousarray(wi_b[u].T)) for u in used]   # [2mlp, emb] rows
-    woq = [oracle.mx_quantize(np.ascontiguousarray(wo_b[u].T)) for u in used]   # [emb, mlp] rows
-    a = oracle.mx_grouped_gemm_nt(a_codes, a_scales, np.stack([q[0] for q in wiq]), np.stack([q[1] for q in wiq]),
-                                  off, epi=1)
-    a_b = bits(torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16))
-    ac, as2 = oracle.mx_quantize(a_b)
-    o = oracle.mx_grouped_gemm_nt(ac, as2, np.stack([q[0] for q in woq]), np.stack([q[1] for q in woq]), off)
-    o_b = bits(torch.from_numpy(o.astype(np.float32)).to(torch.bfloat16))
+    pairs = sorted(((int(idx[i, j]), i, j) for i in range(len(toks)) for j in range(k)))
+    xc, xs_ = oracle.mx_quantize(xb)  # per-row quantization: the same as quantizing every row
+    o_b = np.empty((len(pairs), wl.emb), np.uint16)
+    for u in sorted({e for e, _, _ in pairs}):
+        rows = [r for r, (e, _, _) in enumerate(pairs) if e == u]
+        src = [pairs[r][1] for r in rows]
+        off = np.array([0, len(rows)], np.int32)
+        wic, wis = oracle.mx_quantize(np.ascontiguousarray(bits(d["wi"][u]).T))  # [2mlp, emb] rows
+        woc, wos = oracle.mx_quantize(np.ascontiguousarray(bits(d["wo"][u]).T))  # [emb, mlp] rows
+        a = oracle.mx_grouped_gemm_nt(xc[src], xs_[src], wic[None], wis[None], off, epi=1)
+        ac, as2 = oracle.mx_quantize(bits(torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)))
+        o = oracle.mx_grouped_gemm_nt(ac, as2, woc[None], wos[None], off)
+        o_b[rows] = bits(torch.from_numpy(o.astype(np.float32)).to(torch.bfloat16))
     slot_row = np.empty(len(toks) * k, np.int32)
     for r, (_, i, j) in enumerate(pairs):
         slot_row[i * k + j] = r
-    y_ref = oracle.combine(o_b, slot_row, w[toks], len(toks), k)
+    y_ref = oracle.combine(o_b, slot_row, w, len(toks), k)
     assert_close(to_np(y)[toks], y_ref, "y[sampled]")
