@@ -666,3 +666,66 @@ def test_mx_grouped_gemm_on_integer_codes_is_the_integer_product():
     for e in range(E):
         ref[off[e]:off[e + 1]] = A[off[e]:off[e + 1]] @ B[e].T
     assert np.array_equal(got, ref)
+
+
+def _mx_integer_case(rng, M, K, N, E, t):
+    """Integer-valued E4M3 codes (signed, |v| <= 16) with power-of-two block scales that differ from
+    block to block and from row to row, so every product and every partial sum is exact in float64."""
+    ints = [cc for cc in range(0x7F) if t[cc] == int(t[cc]) and t[cc] <= 16]
+    sign = lambda shape: (rng.integers(0, 2, shape) * 0x80).astype(np.uint8)  # noqa: E731
+    ac = rng.choice(ints, (M, K)).astype(np.uint8) | sign((M, K))
+    bc = rng.choice(ints, (E, N, K)).astype(np.uint8) | sign((E, N, K))
+    a_s = rng.integers(121, 127, (M, K // 32)).astype(np.uint8)
+    b_s = rng.integers(121, 127, (E, N, K // 32)).astype(np.uint8)
+    return ac, a_s, bc, b_s
+
+
+def _mx_exact_product(t, ac, a_s, bc, b_s, off):
+    """float64 C = A . B[e]^T per group, summed one 32-block at a time from exact int64 block sums, each
+    block sum scaled by 2^(sa + sb - 254)."""
+    M, K = ac.shape
+    E, N, _ = bc.shape
+    A = t[ac].astype(np.int64)
+    B = t[bc].astype(np.int64)
+    C_ = np.zeros((M, N), np.float64)
+    for e in range(E):
+        for m in range(off[e], off[e + 1]):
+            for blk in range(K // 32):
+                s = slice(32 * blk, 32 * blk + 32)
+                part = B[e][:, s] @ A[m, s]                       # exact int64, [N]
+                C_[m] += np.ldexp(part.astype(np.float64), a_s[m, blk].astype(np.int64) + b_s[e, :, blk] - 254)
+    return C_
+
+
+def test_mx_grouped_gemm_swiglu_epilogue_on_exact_products():
+    """The MXFP8 SwiGLU reference (epi=1): gate is the first N/2 product columns and up the last N/2
+    ("Gemma4 26B MoE on TPU v6e", Code Review: the split VJP concatenates [grad_gate, grad_up]), and
+    SwiGLU is silu(gate) * up with silu(g) = g * sigmoid(g), applied to the split GMM output ("Keep fused
+    MoE weights intact through FSDP gather", Description) of the MXFP8 MoE block ("[DRAFT][JAX] Optimize
+    MoE block", Changes). The expected value is built from exact integer block
+    sums with scipy's logistic sigmoid; a gate/up swap or a scale applied to the wrong 32-block is far
+    outside the comparison."""
+    rng = np.random.default_rng(21)
+    t = _e4m3_table()
+    M, K, N, E = 48, 128, 32, 4
+    ac, a_s, bc, b_s = _mx_integer_case(rng, M, K, N, E, t)
+    off = np.array([0, 13, 13, 40, 48])                          # an empty group among them
+    got = oracle.mx_grouped_gemm_nt(ac, a_s, bc, b_s, off, epi=1)
+    prod = _mx_exact_product(t, ac, a_s, bc, b_s, off)
+    g, u = prod[:, : N // 2], prod[:, N // 2:]
+    assert 0.5 < np.abs(g).mean() < 50                             # the sigmoid is neither saturated nor linear
+    ref = g * scipy.special.expit(g) * u
+    assert got.shape == (M, N // 2)
+    assert np.allclose(got, ref, rtol=1e-12, atol=0)
+    # the same comparison tells the plausible mistakes apart
+    swapped = u * scipy.special.expit(u) * g
+    assert np.abs(swapped - ref).max() > 1e-2 * np.abs(ref).max()
+    wrong_blk = _mx_exact_product(t, ac, a_s[:, ::-1].copy(), bc, b_s, off)
+    gw, uw = wrong_blk[:, : N // 2], wrong_blk[:, N // 2:]
+    assert np.abs(gw * scipy.special.expit(gw) * uw - ref).max() > 1e-2 * np.abs(ref).max()
+    # a single group covering all rows is the dense SwiGLU of the dequantized operands
+    dense = oracle.mx_grouped_gemm_nt(ac, a_s, bc[:1], b_s[:1], np.array([0, M]), epi=1)
+    A = t[ac] * np.repeat(np.ldexp(1.0, a_s.astype(np.int64) - 127), 32, axis=1)
+    B = t[bc[0]] * np.repeat(np.ldexp(1.0, b_s[0].astype(np.int64) - 127), 32, axis=1)
+    h = A @ B.T
+    assert np.allclose(dense, scipy.special.expit(h[:, : N // 2]) * h[:, : N // 2] * h[:, N // 2:], rtol=1e-12, atol=0)
