@@ -46,7 +46,7 @@ def _lib(real: str) -> C.CDLL:
             "orc_ffn_bwd_tokens": ([_i32, _i32, _i32, _i32, _p, C.c_int, _p, _p, _p, C.c_int, _p, C.c_int,
                                     _p, C.c_int, _i64, _p, _p, _p], C.c_int),
             "orc_ffn_wgrad_expert": ([_i32, _i32, _i32, _i32, _p, C.c_int, _p, _p, _p, C.c_int, _p, C.c_int,
-                                      _p, C.c_int, _i32, _i64, _p, _p, _p], C.c_int),
+                                      _p, C.c_int, _i32, _i64, _p, _p, _p, _i32], C.c_int),
             "orc_grouped_gemm": ([_i32, _i32, _p, C.c_int, _p, C.c_int, _p, C.c_int, _p, _i32, _i64, _i32, _i32,
                                   _i64, _i64, _p], C.c_int),
             "orc_grouped_wgrad": ([_p, C.c_int, _p, C.c_int, _p, _i32, _i64, _i32, _i32, _i32, _p], C.c_int),
@@ -246,10 +246,12 @@ def ffn_bwd_tokens(x, topk_idx, topk_w, wi, wo, dy, tokens=None, real: str = "f3
     return dx, dw
 
 
-def ffn_wgrad_experts(x, topk_idx, topk_w, wi, wo, dy, experts, real: str = "f32", threads: int | None = None):
+def ffn_wgrad_experts(x, topk_idx, topk_w, wi, wo, dy, experts, real: str = "f32", threads: int | None = None,
+                      stored_bf16: bool = False):
     """{e: (dwi_e [emb, 2mlp], dwo_e [mlp, emb])} for the listed experts, routing held fixed.
 
-    Each expert's slots are taken in expert-sorted order (token ascending)."""
+    Each expert's slots are taken in expert-sorted order (token ascending). With stored_bf16, the factors
+    a, do and dh are rounded to bf16 before the products, as the layer stores them (moe_oracle.c, R9)."""
     x = np.ascontiguousarray(x)
     dy = np.ascontiguousarray(dy)
     wi = np.ascontiguousarray(wi)
@@ -273,7 +275,8 @@ def ffn_wgrad_experts(x, topk_idx, topk_w, wi, wo, dy, experts, real: str = "f32
         dwi = np.empty((emb, n2), rt)
         dwo = np.empty((mlp, emb), rt)
         _check(lib.orc_ffn_wgrad_expert(emb, mlp, E, k, xp, xdt, _ptr(topk_idx), _ptr(topk_w), wip, widt, wop, wodt,
-                                        dyp, dydt, int(e), len(slots), _ptr(slots), _ptr(dwi), _ptr(dwo)),
+                                        dyp, dydt, int(e), len(slots), _ptr(slots), _ptr(dwi), _ptr(dwo),
+                                        int(bool(stored_bf16))),
                "ffn_wgrad_expert")
         return dwi, dwo
 

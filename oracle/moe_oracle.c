@@ -66,6 +66,12 @@
  *     power-of-two rescaling) rounded to the nearest E4M3 value, ties to an
  *     even mantissa, magnitudes above 448 saturating to 448, the sign kept
  *     (also on zero).
+ *  R9 the pages fix only fp32 accumulation. Between stages the layer stores
+ *     its activations (a, o, do = w * dy, dh) in bf16, rounded to nearest
+ *     with ties to even. The reference keeps every intermediate in REAL; the
+ *     weight-gradient function can instead round a, do and dh to bf16 where
+ *     the layer stores them (stored_bf16), because each term of dW is a
+ *     product of two such stored factors.
  */
 #include <math.h>
 #include <stdint.h>
@@ -104,6 +110,18 @@ static void load_row(const void* p, int dt, int64_t off, int64_t n, real* dst) {
 }
 
 static int valid_dt(int dt) { return dt == ORC_BF16 || dt == ORC_F32 || dt == ORC_F64; }
+
+/* v rounded to the nearest bf16 value, ties to even (reading R9): the value a bf16 store keeps. A double
+   is first rounded to float. */
+static real round_bf16(real v) {
+  float f = (float)v;
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7f800000u) != 0x7f800000u) u += 0x7fffu + ((u >> 16) & 1u); /* finite: carry into the kept bits */
+  u &= 0xffff0000u;
+  memcpy(&f, &u, 4);
+  return (real)f;
+}
 
 static real silu(real g) { return (real)((double)g / (1.0 + exp(-(double)g))); }
 static real sigmoid(real g) { return (real)(1.0 / (1.0 + exp(-(double)g))); }
@@ -354,11 +372,15 @@ done:
 
 /* Weight gradients of one expert e over its routed slots (slot = t*k + j, listed in
    expert-sorted order): dwi_e [emb, 2mlp] = sum x[t]^T dh, dwo_e [mlp, emb] = sum a^T do.
-   An expert with no slots gets exact zeros. */
+   An expert with no slots gets exact zeros.
+   stored_bf16 != 0 takes the layer's storage reading R9 into the two products: the factors a,
+   do = w * dy and dh, which the layer hands from one stage to the next in bf16, are each rounded to
+   bf16 before they enter the sums (da itself is formed from the unrounded w * dy). The sums stay in
+   REAL. */
 int orc_ffn_wgrad_expert(int32_t emb, int32_t mlp, int32_t E, int32_t k, const void* x, int x_dt,
                          const int32_t* topk_idx, const float* topk_w, const void* wi, int wi_dt, const void* wo,
                          int wo_dt, const void* dy, int dy_dt, int32_t e, int64_t nslots, const int64_t* slots,
-                         real* dwi_e, real* dwo_e) {
+                         real* dwi_e, real* dwo_e, int32_t stored_bf16) {
   int rc = check_common(emb, mlp, E, k, x_dt, wi_dt, wo_dt);
   if (rc) return rc;
   if (!valid_dt(dy_dt) || e < 0 || e >= E || !dwi_e || !dwo_e) return ORC_EINVAL;
@@ -380,6 +402,11 @@ int orc_ffn_wgrad_expert(int32_t emb, int32_t mlp, int32_t E, int32_t k, const v
     real w = (real)topk_w[slot];
     for (int32_t n = 0; n < emb; ++n) s.dov[n] = w * s.dyrow[n];
     expert_backward(&s, e, wi, wi_dt, wo, wo_dt);
+    if (stored_bf16) {
+      for (int32_t c = 0; c < mlp; ++c) s.a[c] = round_bf16(s.a[c]);
+      for (int32_t n = 0; n < emb; ++n) s.dov[n] = round_bf16(s.dov[n]);
+      for (int32_t c = 0; c < n2; ++c) s.dh[c] = round_bf16(s.dh[c]);
+    }
     for (int32_t c = 0; c < mlp; ++c)
       for (int32_t n = 0; n < emb; ++n) dwo_e[(int64_t)c * emb + n] += s.a[c] * s.dov[n];
     for (int32_t i = 0; i < emb; ++i)

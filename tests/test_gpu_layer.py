@@ -14,7 +14,7 @@ import torch
 import mixture_experts_ffn_group_amd as moe
 import oracle
 import workloads
-from parity_util import W_ABS, assert_close, assert_close_wgrad, bits, to_np
+from parity_util import W_ABS, assert_close, bits, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -141,9 +141,11 @@ def test_layer_backward_every_token_and_expert():
     dx, dtw = oracle.ffn_bwd_tokens(x, r_idx, r_w, wi, wo, dy)
     assert_close(to_np(g["dx"]), dx, "dx")
     assert_close(g["dtopk_w"].cpu().numpy(), dtw, "dtopk_w")
-    ref = oracle.ffn_wgrad_experts(x, r_idx, r_w, wi, wo, dy, range(wl.E))
-    assert_close_wgrad(to_np(g["dwi"]), np.stack([ref[e][0] for e in range(wl.E)]), "dwi")
-    assert_close_wgrad(to_np(g["dwo"]), np.stack([ref[e][1] for e in range(wl.E)]), "dwo")
+    # dW = X^T dH multiplies factors the layer stores in bf16 (a, do, dh): the reference rounds them
+    # where the layer stores them and is held to the fixed bound
+    ref = oracle.ffn_wgrad_experts(x, r_idx, r_w, wi, wo, dy, range(wl.E), stored_bf16=True)
+    assert_close(to_np(g["dwi"]), np.stack([ref[e][0] for e in range(wl.E)]), "dwi")
+    assert_close(to_np(g["dwo"]), np.stack([ref[e][1] for e in range(wl.E)]), "dwo")
     # skipping outputs leaves the others unchanged
     g2 = moe.ffn_bwd(d["dy"], saved, d["wi"], d["wo"], wl.k, need=("dx",))
     assert torch.equal(g2["dx"].view(torch.int16), g["dx"].view(torch.int16))
@@ -210,8 +212,15 @@ def test_full_size_deepseek_v3_shape_forward_backward_sampled():
     dx, dtw = oracle.ffn_bwd_tokens(x, r_idx, r_w, wi, wo, dy, tokens=toks)
     assert_close(to_np(g["dx"])[toks], dx, "dx[sampled]")
     assert_close(g["dtopk_w"].cpu().numpy()[toks], dtw, "dtopk_w[sampled]")
-    experts = [int(e) for e in np.argsort(gs, kind="stable")[:2]]
-    ref = oracle.ffn_wgrad_experts(x, r_idx, r_w, wi, wo, dy, experts)
+    # dW on the most- and least-loaded experts (longest and shortest reductions), the median one and six
+    # drawn at random, against the reference with the layer's bf16-stored factors, at the fixed bound
+    order = np.argsort(gs, kind="stable")
+    experts = {int(order[-1]), int(order[0]), int(order[len(order) // 2])}
+    rng = np.random.default_rng(7)
+    while len(experts) < 9:
+        experts.add(int(rng.integers(0, wl.E)))
+    experts = sorted(experts)
+    ref = oracle.ffn_wgrad_experts(x, r_idx, r_w, wi, wo, dy, experts, stored_bf16=True)
     for e in experts:
-        assert_close_wgrad(to_np(g["dwi"][e]), ref[e][0], f"dwi[{e}]")
-        assert_close_wgrad(to_np(g["dwo"][e]), ref[e][1], f"dwo[{e}]")
+        assert_close(to_np(g["dwi"][e]), ref[e][0], f"dwi[{e}] ({gs[e]} rows)")
+        assert_close(to_np(g["dwo"][e]), ref[e][1], f"dwo[{e}] ({gs[e]} rows)")

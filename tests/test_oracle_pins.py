@@ -422,6 +422,41 @@ def test_unrouted_expert_gets_zero_weight_gradient():
     assert (g[0] == 0).all() and (g[1] == 0).all()
 
 
+def _bf16_round(v):
+    """Nearest bf16 value (ties to even) of float64 data, through torch's own conversion from float32."""
+    return torch.from_numpy(np.asarray(v, np.float32)).to(torch.bfloat16).double().numpy()
+
+
+def test_weight_gradient_with_stored_bf16_factors():
+    """stored_bf16 rounds a, do = w * dy and dh to bf16 before the dW products (reading R9). Reference:
+    float64 numpy per expert on the picked rows, the three factors rounded by torch, dh from the
+    unrounded do. Rounding a different factor (h instead of dh, or none) moves dW by ~2^-9 relative,
+    far outside the 1e-4 the two fp32/f64 paths keep."""
+    T, emb, mlp, E, k = 40, 32, 24, 4, 2
+    x, wr, wi, wo = _case(T, emb, mlp, E, k, seed=33, sigma=0.4)
+    dy = _bf16(np.random.default_rng(4).standard_normal((T, emb)))
+    idx, w, _ = oracle.route(x, wr, None, k)
+    got = oracle.ffn_wgrad_experts(x, idx, w, wi, wo, dy, range(E), stored_bf16=True)
+    plain = oracle.ffn_wgrad_experts(x, idx, w, wi, wo, dy, range(E))
+    xv, wiv, wov, dyv = _val(x), _val(wi), _val(wo), _val(dy)
+    for e in range(E):
+        t_, j_ = np.nonzero(idx == e)                        # ascending token: expert-sorted order
+        h = xv[t_] @ wiv[e]
+        g, u = h[:, :mlp], h[:, mlp:]
+        a = _silu(g) * u
+        do = (w[t_, j_].astype(np.float32)[:, None] * dyv[t_].astype(np.float32)).astype(np.float64)
+        da = do @ wov[e].T
+        sg = scipy.special.expit(g)
+        dh = np.concatenate([da * u * sg * (1 + g * (1 - sg)), da * g * sg], axis=1)
+        dwo = _bf16_round(a).T @ _bf16_round(do)
+        dwi = xv[t_].T @ _bf16_round(dh)
+        for name, gv, pv, rv in (("dwi", got[e][0], plain[e][0], dwi), ("dwo", got[e][1], plain[e][1], dwo)):
+            rel = np.linalg.norm(gv - rv) / np.linalg.norm(rv)
+            assert rel <= 1e-4, (e, name, rel)
+            # the unrounded reference is measurably elsewhere: the check sees the rounding
+            assert np.linalg.norm(pv - rv) / np.linalg.norm(rv) > 1e-3, (e, name)
+
+
 def test_backward_stage_composition_equals_per_token_backward():
     """combine-bwd -> NT GEMM + SwiGLU-bwd -> NT GEMM -> permute-bwd == the per-token backward;
     wgrad stage on the sorted activations == the per-expert weight gradients."""
