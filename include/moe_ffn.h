@@ -183,6 +183,47 @@ int moe_grouped_gemm_wgrad(const moe_bf16_t* A, const moe_bf16_t* D, const int32
                            int64_t M, int32_t P, int32_t Q, moe_bf16_t* C, moe_stream_t stream);
 
 /*
+ * moe_grouped_gemm_grid / moe_grouped_gemm_wgrad_grid -- the same calls with
+ * the size of the persistent grid given: `grid` workgroups (0, or a positive
+ * multiple of 8 up to 65536; 0 = one per compute unit, which is what
+ * moe_grouped_gemm and moe_grouped_gemm_wgrad launch). The result does not
+ * depend on the grid: every output tile is computed whole by one workgroup,
+ * in the same order of k. A small grid makes each workgroup run many tiles
+ * in turn; tests use it to cover the persistent loop's tile-to-tile hand-over
+ * (loads of the next tile issued during the current tile's epilogue) on
+ * shapes small enough for an element-by-element comparison.
+ */
+int moe_grouped_gemm_grid(int op, int epilogue, const moe_bf16_t* A, const moe_bf16_t* B, const float* aux_in,
+                          float* aux_out, const int32_t* group_offsets, int32_t E, int64_t M, int32_t K, int32_t N,
+                          const moe_gemm_rows_t* rows, moe_bf16_t* C, int32_t grid, moe_stream_t stream);
+int moe_grouped_gemm_wgrad_grid(const moe_bf16_t* A, const moe_bf16_t* D, const int32_t* group_offsets, int32_t E,
+                                int64_t M, int32_t P, int32_t Q, moe_bf16_t* C, int32_t grid, moe_stream_t stream);
+
+/*
+ * moe_tile_schedule -- HOST call, no device access: the tile list that the
+ * persistent grouped GEMMs run on a grid of `grid` workgroups (a positive
+ * multiple of 8), computed by the same functions the kernels call. The pages'
+ * grouped GEMM runs only the tiles a group needs, masking the partial tile at
+ * a group edge ("MoE: fused TensorCore Pallas permute/combine kernels ...",
+ * Tests: boundary-tile masking; "[DRAFT][JAX] Optimize MoE block", Changes:
+ * group-aware kernels).
+ *  kind MOE_SCHED_GEMM: moe_grouped_gemm with the plain output, N output
+ *   columns. MOE_SCHED_GEMM_SWIGLU: the SwiGLU epilogue, N = 2*mlp (mlp
+ *   output columns). MOE_SCHED_WGRAD: moe_grouped_gemm_wgrad with C[e]
+ *   [N, Q] (N is P there); Q is ignored by the other kinds.
+ *  group_offsets: HOST array [E + 1], read as the kernels read theirs.
+ *  tiles: HOST array [capacity][7] int32 or NULL when capacity is 0; tile i
+ *   is {workgroup, turn, expert, row0, row1, col0, col1}: rows [row0, row1)
+ *   of the output (of dW[e] for WGRAD) and columns [col0, col1) that the
+ *   workgroup computes on that turn, past group ends and widths excluded.
+ *  *count receives the number of tiles (tiles beyond capacity are counted,
+ *   not written).
+ */
+enum { MOE_SCHED_GEMM = 0, MOE_SCHED_GEMM_SWIGLU = 1, MOE_SCHED_WGRAD = 2 };
+int moe_tile_schedule(int32_t kind, const int32_t* group_offsets, int32_t E, int64_t M, int32_t N, int32_t Q,
+                      int32_t grid, int32_t* tiles, int64_t capacity, int64_t* count);
+
+/*
  * moe_combine -- unpermute plus top-k weighted sum ("MoE: fused TensorCore
  * Pallas permute/combine kernels ...", Commits table, commit 1):
  *  y[t] = sum_{j<k} topk_w[t, j] * ys[slot_row[t*k + j]], accumulated in fp32

@@ -113,11 +113,12 @@ def permute(x: torch.Tensor, topk_idx: torch.Tensor, E: int, rows: bool = True) 
 def grouped_gemm(A: torch.Tensor, B: torch.Tensor, group_offsets: torch.Tensor, op: str = "nn",
                  epilogue: str = "none", aux_in: torch.Tensor | None = None, save_h: bool = False,
                  out: torch.Tensor | None = None, row_slot: torch.Tensor | None = None, slot_div: int = 1,
-                 slot_scale: torch.Tensor | None = None, M: int | None = None):
+                 slot_scale: torch.Tensor | None = None, M: int | None = None, grid: int = 0):
     """Ragged grouped GEMM (see moe_grouped_gemm). Returns C, or (C, h) with save_h (SwiGLU, h in fp32).
 
     row_slot [M] int32 (optional): output row r reads A row row_slot[r] // slot_div (A is not permuted).
-    slot_scale (optional, fp32): per-row scale, indexed by row_slot[r] (or r)."""
+    slot_scale (optional, fp32): per-row scale, indexed by row_slot[r] (or r).
+    grid: workgroups of the persistent grid (0 = one per compute unit; see moe_grouped_gemm_grid)."""
     _need(A, "A", torch.bfloat16)
     dev = A.device
     _need(B, "B", torch.bfloat16, dev)
@@ -140,13 +141,15 @@ def grouped_gemm(A: torch.Tensor, B: torch.Tensor, group_offsets: torch.Tensor, 
         n_slots = A.shape[0] * slot_div if row_slot is not None else 0
         rows = C.byref(MoeGemmRows(None if row_slot is None else row_slot.data_ptr(), n_slots, slot_div,
                                    None if slot_scale is None else slot_scale.data_ptr()))
-    _lib.check(_lib.lib().moe_grouped_gemm(_OP[op], epi, _ptr(A), _ptr(B), _ptr(aux_in), _ptr(h), _ptr(group_offsets),
-                                           E, M, K, N, rows, _ptr(C_), _stream(dev)), "moe_grouped_gemm")
+    _lib.check(_lib.lib().moe_grouped_gemm_grid(_OP[op], epi, _ptr(A), _ptr(B), _ptr(aux_in), _ptr(h),
+                                                _ptr(group_offsets), E, M, K, N, rows, _ptr(C_), grid, _stream(dev)),
+               "moe_grouped_gemm")
     return (C_, h) if save_h else C_
 
 
-def grouped_gemm_wgrad(A: torch.Tensor, D: torch.Tensor, group_offsets: torch.Tensor, E: int) -> torch.Tensor:
-    """C [E, P, Q] = per-group A^T D."""
+def grouped_gemm_wgrad(A: torch.Tensor, D: torch.Tensor, group_offsets: torch.Tensor, E: int,
+                       grid: int = 0) -> torch.Tensor:
+    """C [E, P, Q] = per-group A^T D (grid as in grouped_gemm)."""
     _need(A, "A", torch.bfloat16)
     dev = A.device
     _need(D, "D", torch.bfloat16, dev)
@@ -154,9 +157,28 @@ def grouped_gemm_wgrad(A: torch.Tensor, D: torch.Tensor, group_offsets: torch.Te
     M, P = A.shape
     Q = D.shape[1]
     C_ = torch.empty((E, P, Q), dtype=torch.bfloat16, device=dev)
-    _lib.check(_lib.lib().moe_grouped_gemm_wgrad(_ptr(A), _ptr(D), _ptr(group_offsets), E, M, P, Q, _ptr(C_),
-                                                 _stream(dev)), "moe_grouped_gemm_wgrad")
+    _lib.check(_lib.lib().moe_grouped_gemm_wgrad_grid(_ptr(A), _ptr(D), _ptr(group_offsets), E, M, P, Q, _ptr(C_),
+                                                      grid, _stream(dev)), "moe_grouped_gemm_wgrad")
     return C_
+
+
+_SCHED = {"gemm": _lib.MOE_SCHED_GEMM, "swiglu": _lib.MOE_SCHED_GEMM_SWIGLU, "wgrad": _lib.MOE_SCHED_WGRAD}
+
+
+def tile_schedule(kind: str, group_offsets, M: int, N: int, grid: int, Q: int = 0):
+    """Host-side tile list of a persistent grouped GEMM (moe_tile_schedule): int32 array [n, 7] of
+    (workgroup, turn, expert, row0, row1, col0, col1). group_offsets: host integer array [E + 1]."""
+    import numpy as np
+
+    off = np.ascontiguousarray(group_offsets, dtype=np.int32)
+    E = len(off) - 1
+    count = C.c_int64(0)
+    f = _lib.lib().moe_tile_schedule
+    _lib.check(f(_SCHED[kind], off.ctypes.data, E, M, N, Q, grid, None, 0, C.byref(count)), "moe_tile_schedule")
+    out = np.empty((count.value, 7), np.int32)
+    _lib.check(f(_SCHED[kind], off.ctypes.data, E, M, N, Q, grid, out.ctypes.data if count.value else None,
+                 count.value, C.byref(count)), "moe_tile_schedule")
+    return out
 
 
 def combine(ys: torch.Tensor, slot_row: torch.Tensor, topk_w: torch.Tensor | None, T: int, k: int) -> torch.Tensor:

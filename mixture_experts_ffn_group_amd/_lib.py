@@ -18,6 +18,7 @@ MOE_OK = 0
 MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_ALIGN = 1, 2, 3, 4, 5, 6
 MOE_NN, MOE_NT = 0, 1
 MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_SWIGLU_BWD = 0, 1, 2
+MOE_SCHED_GEMM, MOE_SCHED_GEMM_SWIGLU, MOE_SCHED_WGRAD = 0, 1, 2
 
 # Every function the header declares, with its ctypes signature.
 _p = C.c_void_p
@@ -52,6 +53,10 @@ SIGNATURES = {
     "moe_grouped_gemm": ([C.c_int, C.c_int, _p, _p, _p, _p, _p, _i32, _i64, _i32, _i32, C.POINTER(MoeGemmRows), _p,
                           _p], C.c_int),
     "moe_grouped_gemm_wgrad": ([_p, _p, _p, _i32, _i64, _i32, _i32, _p, _p], C.c_int),
+    "moe_grouped_gemm_grid": ([C.c_int, C.c_int, _p, _p, _p, _p, _p, _i32, _i64, _i32, _i32, C.POINTER(MoeGemmRows),
+                               _p, _i32, _p], C.c_int),
+    "moe_grouped_gemm_wgrad_grid": ([_p, _p, _p, _i32, _i64, _i32, _i32, _p, _i32, _p], C.c_int),
+    "moe_tile_schedule": ([_i32, _p, _i32, _i64, _i32, _i32, _i32, _p, _i64, C.POINTER(_i64)], C.c_int),
     "moe_combine": ([_SHP, _p, _p, _p, _p, _p], C.c_int),
     "moe_combine_bwd": ([_SHP, _p, _p, _p, _p, _p, _p, _p], C.c_int),
     "moe_ffn_fwd": ([_SHP, _p, _p, _p, _p, _p, _p, _p, C.POINTER(MoeSaved), _p, _sz, _p], C.c_int),

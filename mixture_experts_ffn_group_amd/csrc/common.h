@@ -5,6 +5,8 @@
 #include <hip/hip_bf16.h>
 #include <stdint.h>
 
+#include "tiles.h"
+
 namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -17,7 +19,6 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
-constexpr int kNumXcd = 8;   // MI355X: 8 XCDs, workgroups dealt round-robin across them
 constexpr int kMaxExperts = 256;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -39,14 +40,6 @@ __device__ __forceinline__ void st16(void* p, u32x4_t v) { *reinterpret_cast<u32
 __device__ __forceinline__ void st8(void* p, u32x2_t v) { *reinterpret_cast<u32x2_t*>(p) = v; }
 
 __device__ __forceinline__ int popc64(uint64_t v) { return __popcll(v); }
-
-// Persistent-grid tile index: workgroup w sits on XCD w % 8. Tile sequence
-// number `it` of workgroup w is it * G + (w % 8) * (G / 8) + w / 8, so at any
-// moment each XCD works on a contiguous run of G / 8 tiles and those tiles
-// share operands in that XCD's L2. G must be a multiple of 8.
-__device__ __forceinline__ int64_t xcd_tile(int64_t it, int w, int G) {
-  return it * G + (int64_t)(w % kNumXcd) * (G / kNumXcd) + w / kNumXcd;
-}
 
 // MXFP8 element and scale encodings (OCP microscaling, E4M3 elements with an
 // E8M0 scale per 32-element block; see mxfp8.hip).

@@ -195,14 +195,8 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
   {  // ragged tile list: tiles of expert e = ceil(rows_e / BM) * ntn, prefix over experts
     const int tid = threadIdx.x;
     int tiles = 0;
-    if (tid <= p.E) s_lo[tid] = min(max(p.off[tid], 0), p.M);
-    if (tid < p.E) {
-      int lo = p.off[tid], hi = p.off[tid + 1];
-      lo = min(max(lo, 0), p.M);
-      hi = min(max(hi, 0), p.M);
-      const int n = hi > lo ? hi - lo : 0;
-      tiles = ((n + BM - 1) / BM) * ntn;
-    }
+    if (tid <= p.E) s_lo[tid] = clamp_rows(p.off[tid], p.M);
+    if (tid < p.E) tiles = group_tiles(clamp_rows(p.off[tid + 1], p.M) - clamp_rows(p.off[tid], p.M), ntn);
     const int incl = block_incl_scan_n<GTHR / 64>(tiles, s_wsum);
     if (tid < p.E) s_pref[tid + 1] = incl;
     if (tid == 0) s_pref[0] = 0;
@@ -270,25 +264,13 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
   auto decode = [&](int64_t it) -> bool {
     const int64_t tl = xcd_tile(it, blockIdx.x, gridDim.x);
     if (tl >= total) return false;
-    const int tile = (int)tl;
-    int lo = 0, hi = p.E;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_pref[mid] <= tile) lo = mid;
-      else hi = mid;
-    }
-    const int e = lo;
-    // Tile order inside an expert: with 4 or more row blocks the row block
-    // varies fastest, so the workgroups of an XCD share one weight panel while
-    // they sweep the expert's rows (measured: wo GEMM 1.01 -> 0.97 ms at 128
-    // experts of ~2048 rows, K = 768). With 1-3 row blocks the column tile
-    // varies fastest, so all column tiles read the same row block at once (the
-    // other order cost 12 % at 256 experts of ~256 rows, K = 7168).
-    const int local = tile - s_pref[e];
-    const int nmt = (s_pref[e + 1] - s_pref[e]) / ntn;
-    const bool rows_fast = nmt >= 4;
-    const int mt = rows_fast ? local % nmt : local / ntn;
-    const int nt = rows_fast ? local / nmt : local % ntn;
+    // Tile order inside an expert (ragged_tile): with 4 or more row blocks the
+    // row block varies fastest (measured: wo GEMM 1.01 -> 0.97 ms at 128
+    // experts of ~2048 rows, K = 768); with 1-3 row blocks the column tile
+    // varies fastest (the other order cost 12 % at 256 experts of ~256 rows,
+    // K = 7168).
+    const RaggedTile rt = ragged_tile((int)tl, s_pref, p.E, ntn);
+    const int e = rt.e, mt = rt.mt, nt = rt.nt;
     m0 = __builtin_amdgcn_readfirstlane(s_lo[e] + mt * BM);
     m_end = __builtin_amdgcn_readfirstlane(max(s_lo[e + 1], s_lo[e]));
     n0 = __builtin_amdgcn_readfirstlane(nt * tile_n);
@@ -738,7 +720,7 @@ __global__ __launch_bounds__(GTHR, 1) void wgrad_kernel(WgradP p) {
   // group offsets, clamped to [0, M], read once: a tile's rows are then known
   // without a global load between two tiles
   __shared__ int s_off[kMaxExperts + 1];
-  for (int i = threadIdx.x; i <= p.E; i += GTHR) s_off[i] = min(max(p.off[i], 0), p.M);
+  for (int i = threadIdx.x; i <= p.E; i += GTHR) s_off[i] = clamp_rows(p.off[i], p.M);
   __syncthreads();
   const int tp = (p.P + 255) / 256, tq = (p.Q + 255) / 256;
   uint8_t* const As0 = smem;
@@ -769,24 +751,17 @@ __global__ __launch_bounds__(GTHR, 1) void wgrad_kernel(WgradP p) {
   // share the chunk swizzle ((2j + lane/32) & 3 repeats with period 2) and lie
   // 4 k-rows apart, so only j = 0, 1 are kept
   uint32_t a_off[2], d_off[2];
-  // Tiles are dealt by expert: XCD x (workgroups w with w % 8 == x) takes
-  // experts x, x + 8, ..., each expert's tiles in turn over its G / 8
-  // workgroups. Every expert has the same number of tiles whatever its row
-  // count, so the XCDs stay balanced when E is a multiple of 8, and an
-  // expert's operand rows are read into one XCD's L2 rather than into all
-  // eight. Inside an expert the dimension with fewer 256-blocks varies
-  // fastest: its panels stay in L2 while the other dimension's stream past
+  // Tiles are dealt by expert (wgrad_tile): XCD x takes experts x, x + 8, ...,
+  // so an expert's operand rows are read into one XCD's L2 rather than into
+  // all eight; inside an expert the dimension with fewer 256-blocks varies
+  // fastest, so its panels stay in L2 while the other dimension's stream past
   // once each.
-  const int per_xcd = gridDim.x / kNumXcd;
-  const int my_xcd = blockIdx.x % kNumXcd, my_slot = blockIdx.x / kNumXcd;
   auto decode = [&](int64_t it) -> bool {
-    const int64_t j = it * per_xcd + my_slot;
-    const int64_t ee = my_xcd + (int64_t)kNumXcd * (j / ((int64_t)tp * tq));
-    if (ee >= p.E) return false;
-    e = __builtin_amdgcn_readfirstlane((int)ee);
-    const int loc = (int)(j % ((int64_t)tp * tq));
-    p0 = __builtin_amdgcn_readfirstlane((tq <= tp ? loc / tq : loc % tp) * 256);
-    q0 = __builtin_amdgcn_readfirstlane((tq <= tp ? loc % tq : loc / tp) * 256);
+    WgradTile wt;
+    if (!wgrad_tile(it, blockIdx.x, gridDim.x, p.E, tp, tq, &wt)) return false;
+    e = __builtin_amdgcn_readfirstlane(wt.e);
+    p0 = __builtin_amdgcn_readfirstlane(wt.pt * 256);
+    q0 = __builtin_amdgcn_readfirstlane(wt.qt * 256);
     const int l0 = s_off[e], h0 = s_off[e + 1];
     lo = __builtin_amdgcn_readfirstlane(l0);
     n = __builtin_amdgcn_readfirstlane(h0 > l0 ? h0 - l0 : 0);
@@ -950,22 +925,22 @@ __global__ __launch_bounds__(GTHR, 1) void wgrad_kernel(WgradP p) {
   }
 }
 
+}  // namespace
+
 int persistent_grid() {
   int g = device_cu_count();
   g -= g % kNumXcd;
   return g < kNumXcd ? kNumXcd : g;
 }
 
-}  // namespace
-
 hipError_t launch_grouped_gemm(int op, int epi, const uint16_t* A, const uint16_t* B, const float* aux_in,
                                float* aux_out, const int32_t* group_offsets, int E, int64_t M, int K, int N,
                                const int32_t* row_slot, int n_slots, int slot_div, const float* slot_scale,
-                               uint16_t* C, hipStream_t stream) {
+                               uint16_t* C, hipStream_t stream, int grid_size) {
   if (M == 0) return hipSuccess;
   GemmP p{A, B, aux_in, aux_out, C, group_offsets, row_slot, slot_scale, E, (int)M, K, N,
           row_slot ? n_slots : (int)M, slot_div > 0 ? slot_div : 1};
-  const dim3 grid(persistent_grid()), block(GTHR);
+  const dim3 grid(grid_size > 0 ? grid_size : persistent_grid()), block(GTHR);
   const bool g = row_slot != nullptr || slot_scale != nullptr;
 #define MOE_GEMM_LAUNCH(O, P)                                                           \
   if (g) gemm_kernel<O, P, true><<<grid, block, 0, stream>>>(p);                        \
@@ -980,10 +955,10 @@ hipError_t launch_grouped_gemm(int op, int epi, const uint16_t* A, const uint16_
 }
 
 hipError_t launch_wgrad(const uint16_t* A, const uint16_t* D, const int32_t* group_offsets, int E, int64_t M, int P,
-                        int Q, uint16_t* C, hipStream_t stream) {
+                        int Q, uint16_t* C, hipStream_t stream, int grid_size) {
   if (E == 0) return hipSuccess;
   WgradP p{A, D, group_offsets, C, E, (int)M, P, Q};
-  wgrad_kernel<<<dim3(persistent_grid()), dim3(GTHR), 0, stream>>>(p);
+  wgrad_kernel<<<dim3(grid_size > 0 ? grid_size : persistent_grid()), dim3(GTHR), 0, stream>>>(p);
   return hipGetLastError();
 }
 

@@ -22,15 +22,19 @@ hipError_t launch_permute(int64_t T, int emb, int E, int k, const uint16_t* x, c
                           int32_t* group_sizes, int32_t* group_offsets, int32_t* sorted_slot, int32_t* slot_row,
                           uint16_t* xs, uint64_t* masks, int32_t* base, hipStream_t stream);
 
+// grid: workgroups of the persistent grid (a multiple of 8); 0 = persistent_grid().
 // row_slot (nullable): output row r reads A row row_slot[r] / slot_div, row_slot values in [0, n_slots).
 // slot_scale (nullable): output row r is scaled by slot_scale[row_slot[r]] (or slot_scale[r]).
 hipError_t launch_grouped_gemm(int op, int epi, const uint16_t* A, const uint16_t* B, const float* aux_in,
                                float* aux_out, const int32_t* group_offsets, int E, int64_t M, int K, int N,
                                const int32_t* row_slot, int n_slots, int slot_div, const float* slot_scale,
-                               uint16_t* C, hipStream_t stream);
+                               uint16_t* C, hipStream_t stream, int grid = 0);
 
 hipError_t launch_wgrad(const uint16_t* A, const uint16_t* D, const int32_t* group_offsets, int E, int64_t M, int P,
-                        int Q, uint16_t* C, hipStream_t stream);
+                        int Q, uint16_t* C, hipStream_t stream, int grid = 0);
+
+// Workgroups of the persistent GEMM grid: one per compute unit, rounded down to a multiple of 8 (at least 8).
+int persistent_grid();
 
 hipError_t launch_combine(int64_t T, int emb, int k, const uint16_t* ys, const int32_t* slot_row, const float* w,
                           uint16_t* y, hipStream_t stream);

@@ -6,9 +6,12 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <vector>
+#include <algorithm>
 
 #include "kernels.h"
 #include "moe_ffn.h"
+#include "tiles.h"
 
 namespace moe {
 
@@ -136,6 +139,23 @@ int check_gemm(int op, int epi, int64_t M, int K, int N, int E) {
   return MOE_OK;
 }
 
+int check_wgrad(int32_t E, int64_t M, int32_t P, int32_t Q) {
+  if (M < 0 || P <= 0 || Q <= 0 || E <= 0) return fail(MOE_ERR_SHAPE, "need M >= 0 and P, Q, E > 0");
+  if (E > 256) return fail(MOE_ERR_UNSUPPORTED, "E (%d) > 256", E);
+  if (M >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "M >= 2^31");
+  if (P % 8 || Q % 8) return fail(MOE_ERR_UNSUPPORTED, "P and Q must be multiples of 8");
+  if ((int64_t)E * ((P + 255) / 256) * ((Q + 255) / 256) >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "tile count too large");
+  return MOE_OK;
+}
+
+// grid: 0 (one workgroup per compute unit) or a multiple of 8 up to 65536
+int check_grid(int32_t grid) {
+  if (grid < 0 || grid % moe::kNumXcd || grid > 65536)
+    return fail(MOE_ERR_SHAPE, "grid (%d) must be 0 or a positive multiple of 8 up to 65536", grid);
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -240,11 +260,12 @@ int moe_permute(const moe_shape_t* s, const moe_bf16_t* x, const int32_t* topk_i
                     "moe_permute");
 }
 
-int moe_grouped_gemm(int op, int epilogue, const moe_bf16_t* A, const moe_bf16_t* B, const float* aux_in,
-                     float* aux_out, const int32_t* group_offsets, int32_t E, int64_t M, int32_t K, int32_t N,
-                     const moe_gemm_rows_t* rows, moe_bf16_t* C, moe_stream_t stream) {
+int moe_grouped_gemm_grid(int op, int epilogue, const moe_bf16_t* A, const moe_bf16_t* B, const float* aux_in,
+                          float* aux_out, const int32_t* group_offsets, int32_t E, int64_t M, int32_t K, int32_t N,
+                          const moe_gemm_rows_t* rows, moe_bf16_t* C, int32_t grid, moe_stream_t stream) {
   g_detail[0] = 0;
   if (int rc = check_gemm(op, epilogue, M, K, N, E)) return rc;
+  if (int rc = check_grid(grid)) return rc;
   NEED(B);
   NEED(group_offsets);
   if (M > 0) {
@@ -270,27 +291,85 @@ int moe_grouped_gemm(int op, int epilogue, const moe_bf16_t* A, const moe_bf16_t
   }
   return hip_status(moe::launch_grouped_gemm(op, epilogue, A, B, aux_in, epilogue == MOE_EPI_SWIGLU ? aux_out : nullptr,
                                              group_offsets, E, M, K, N, row_slot, n_slots, slot_div, slot_scale, C,
-                                             (hipStream_t)stream),
+                                             (hipStream_t)stream, grid),
                     "moe_grouped_gemm");
 }
 
-int moe_grouped_gemm_wgrad(const moe_bf16_t* A, const moe_bf16_t* D, const int32_t* group_offsets, int32_t E,
-                           int64_t M, int32_t P, int32_t Q, moe_bf16_t* C, moe_stream_t stream) {
+int moe_grouped_gemm(int op, int epilogue, const moe_bf16_t* A, const moe_bf16_t* B, const float* aux_in,
+                     float* aux_out, const int32_t* group_offsets, int32_t E, int64_t M, int32_t K, int32_t N,
+                     const moe_gemm_rows_t* rows, moe_bf16_t* C, moe_stream_t stream) {
+  return moe_grouped_gemm_grid(op, epilogue, A, B, aux_in, aux_out, group_offsets, E, M, K, N, rows, C, 0, stream);
+}
+
+int moe_grouped_gemm_wgrad_grid(const moe_bf16_t* A, const moe_bf16_t* D, const int32_t* group_offsets, int32_t E,
+                                int64_t M, int32_t P, int32_t Q, moe_bf16_t* C, int32_t grid, moe_stream_t stream) {
   g_detail[0] = 0;
-  if (M < 0 || P <= 0 || Q <= 0 || E <= 0) return fail(MOE_ERR_SHAPE, "need M >= 0 and P, Q, E > 0");
-  if (E > 256) return fail(MOE_ERR_UNSUPPORTED, "E (%d) > 256", E);
-  if (M >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "M >= 2^31");
-  if (P % 8 || Q % 8) return fail(MOE_ERR_UNSUPPORTED, "P and Q must be multiples of 8");
-  if ((int64_t)E * ((P + 255) / 256) * ((Q + 255) / 256) >= (int64_t(1) << 31))
-    return fail(MOE_ERR_UNSUPPORTED, "tile count too large");
+  if (int rc = check_wgrad(E, M, P, Q)) return rc;
+  if (int rc = check_grid(grid)) return rc;
   NEED(group_offsets);
   NEED(C);
   if (M > 0) {
     NEED(A);
     NEED(D);
   }
-  return hip_status(moe::launch_wgrad(A, D, group_offsets, E, M, P, Q, C, (hipStream_t)stream),
+  return hip_status(moe::launch_wgrad(A, D, group_offsets, E, M, P, Q, C, (hipStream_t)stream, grid),
                     "moe_grouped_gemm_wgrad");
+}
+
+int moe_grouped_gemm_wgrad(const moe_bf16_t* A, const moe_bf16_t* D, const int32_t* group_offsets, int32_t E,
+                           int64_t M, int32_t P, int32_t Q, moe_bf16_t* C, moe_stream_t stream) {
+  return moe_grouped_gemm_wgrad_grid(A, D, group_offsets, E, M, P, Q, C, 0, stream);
+}
+
+int moe_tile_schedule(int32_t kind, const int32_t* group_offsets, int32_t E, int64_t M, int32_t N, int32_t Q,
+                      int32_t grid, int32_t* tiles, int64_t capacity, int64_t* count) {
+  g_detail[0] = 0;
+  if (!group_offsets) return fail(MOE_ERR_NULL, "argument group_offsets is NULL");
+  if (!count) return fail(MOE_ERR_NULL, "argument count is NULL");
+  if (capacity < 0 || (capacity > 0 && !tiles)) return fail(MOE_ERR_NULL, "tiles is NULL with capacity > 0");
+  if (grid <= 0) return fail(MOE_ERR_SHAPE, "grid must be given (> 0) for the host schedule");
+  if (int rc = check_grid(grid)) return rc;
+  int64_t n = 0;
+  auto emit = [&](int w, int64_t it, int e, int r0, int r1, int c0, int c1) {
+    if (n < capacity) {
+      int32_t* t = tiles + 7 * n;
+      t[0] = w, t[1] = (int32_t)it, t[2] = e, t[3] = r0, t[4] = r1, t[5] = c0, t[6] = c1;
+    }
+    ++n;
+  };
+  if (kind == MOE_SCHED_WGRAD) {
+    if (int rc = check_wgrad(E, M, N, Q)) return rc;
+    const int tp = (N + moe::kWgradTile - 1) / moe::kWgradTile, tq = (Q + moe::kWgradTile - 1) / moe::kWgradTile;
+    for (int w = 0; w < grid; ++w) {
+      moe::WgradTile t;
+      for (int64_t it = 0; moe::wgrad_tile(it, w, grid, E, tp, tq, &t); ++it) {
+        const int p0 = t.pt * moe::kWgradTile, q0 = t.qt * moe::kWgradTile;
+        emit(w, it, t.e, p0, std::min(p0 + moe::kWgradTile, N), q0, std::min(q0 + moe::kWgradTile, Q));
+      }
+    }
+  } else if (kind == MOE_SCHED_GEMM || kind == MOE_SCHED_GEMM_SWIGLU) {
+    const bool swiglu = kind == MOE_SCHED_GEMM_SWIGLU;
+    if (int rc = check_gemm(swiglu ? MOE_NN : MOE_NT, swiglu ? MOE_EPI_SWIGLU : MOE_EPI_NONE, M, 64, N, E)) return rc;
+    const int width = swiglu ? N / 2 : N, tile_n = swiglu ? 128 : 256, ntn = (width + tile_n - 1) / tile_n;
+    std::vector<int> lo(E + 1), pref(E + 1);
+    for (int e = 0; e <= E; ++e) lo[e] = moe::clamp_rows(group_offsets[e], (int)M);
+    pref[0] = 0;
+    for (int e = 0; e < E; ++e) pref[e + 1] = pref[e] + moe::group_tiles(lo[e + 1] - lo[e], ntn);
+    for (int w = 0; w < grid; ++w) {
+      for (int64_t it = 0;; ++it) {
+        const int64_t tl = moe::xcd_tile(it, w, grid);
+        if (tl >= pref[E]) break;
+        const moe::RaggedTile t = moe::ragged_tile((int)tl, pref, E, ntn);
+        const int m0 = lo[t.e] + t.mt * moe::kTileRows, m_end = std::max(lo[t.e + 1], lo[t.e]);
+        const int n0 = t.nt * tile_n;
+        emit(w, it, t.e, m0, std::min(m0 + moe::kTileRows, m_end), n0, std::min(n0 + tile_n, width));
+      }
+    }
+  } else {
+    return fail(MOE_ERR_SHAPE, "unknown schedule kind %d", kind);
+  }
+  *count = n;
+  return MOE_OK;
 }
 
 int moe_combine(const moe_shape_t* s, const moe_bf16_t* ys, const int32_t* slot_row, const float* topk_w,

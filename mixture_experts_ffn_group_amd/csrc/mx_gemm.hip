@@ -132,12 +132,8 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
   {  // ragged tile list: tiles of expert e = ceil(rows_e / 256) * ntn, prefix over experts
     const int tid = threadIdx.x;
     int tiles = 0;
-    if (tid <= p.E) s_lo[tid] = min(max(p.off[tid], 0), p.M);
-    if (tid < p.E) {
-      const int lo = min(max(p.off[tid], 0), p.M), hi = min(max(p.off[tid + 1], 0), p.M);
-      const int n = hi > lo ? hi - lo : 0;
-      tiles = ((n + 255) / 256) * ntn;
-    }
+    if (tid <= p.E) s_lo[tid] = clamp_rows(p.off[tid], p.M);
+    if (tid < p.E) tiles = group_tiles(clamp_rows(p.off[tid + 1], p.M) - clamp_rows(p.off[tid], p.M), ntn);
     const int incl = mx_scan<MXT / 64>(tiles, s_wsum);
     if (tid < p.E) s_pref[tid + 1] = incl;
     if (tid == 0) s_pref[0] = 0;
@@ -174,19 +170,9 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
   auto decode = [&](int64_t it) -> bool {
     const int64_t tl = xcd_tile(it, blockIdx.x, gridDim.x);
     if (tl >= total) return false;
-    const int tile = (int)tl;
-    int lo = 0, hi = p.E;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_pref[mid] <= tile) lo = mid;
-      else hi = mid;
-    }
-    e = __builtin_amdgcn_readfirstlane(lo);
-    const int local = tile - s_pref[e];
-    const int nmt = (s_pref[e + 1] - s_pref[e]) / ntn;
-    const bool rows_fast = nmt >= 4;
-    const int mt = rows_fast ? local % nmt : local / ntn;
-    const int nt = rows_fast ? local / nmt : local % ntn;
+    const RaggedTile rt = ragged_tile((int)tl, s_pref, p.E, ntn);
+    e = __builtin_amdgcn_readfirstlane(rt.e);
+    const int mt = rt.mt, nt = rt.nt;
     m0 = __builtin_amdgcn_readfirstlane(s_lo[e] + mt * 256);
     m_end = __builtin_amdgcn_readfirstlane(max(s_lo[e + 1], s_lo[e]));
     n0 = __builtin_amdgcn_readfirstlane(nt * tile_n);

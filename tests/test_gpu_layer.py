@@ -3,9 +3,10 @@
 Small workloads are compared element by element on every token. Full-size
 workloads (the Gemma4-class layer, the Zipf token sweep, the DeepSeek-V3-shaped
 forward+backward) are generated on the device; routing, group sizes, sort
-order and the permuted rows are compared bit for bit on every token, and the
-FFN outputs and gradients on sampled tokens and experts that the oracle
-computes one by one.
+order and the permuted rows are compared bit for bit on every token. The
+forward output of the Gemma4-class layer and of the sweep is compared on
+every token; the DeepSeek-V3-shaped output and gradients on 64 sampled tokens
+and nine experts that the oracle computes one by one.
 """
 import numpy as np
 import pytest
@@ -191,9 +192,9 @@ def test_full_size_forward_sampled(name):
     torch.cuda.synchronize()
     h = _host(d)
     r_idx, r_w, gs, go, ss, sr = _check_routing_and_permute(saved, h)
-    toks = _sample_tokens(wl.T, 40, wl.seed)
-    ref = oracle.ffn_fwd_tokens(bits(h["x"]), r_idx, r_w, bits(h["wi"]), bits(h["wo"]), tokens=toks)
-    assert_close(to_np(y)[toks], ref, f"{name} y[sampled]")
+    # every token: the oracle streams each token's k experts, ~1.2 TMAC on the 32768-token layer
+    ref = oracle.ffn_fwd_tokens(bits(h["x"]), r_idx, r_w, bits(h["wi"]), bits(h["wo"]))
+    assert_close(to_np(y), ref, f"{name} y (every token)")
 
 
 @pytest.mark.slow
@@ -206,7 +207,7 @@ def test_full_size_deepseek_v3_shape_forward_backward_sampled():
     h = _host(d)
     r_idx, r_w, gs, go, ss, sr = _check_routing_and_permute(saved, h)
     x, wi, wo, dy = bits(h["x"]), bits(h["wi"]), bits(h["wo"]), bits(h["dy"])
-    toks = _sample_tokens(wl.T, 16, 5)
+    toks = _sample_tokens(wl.T, 64, 5)
     ref_y = oracle.ffn_fwd_tokens(x, r_idx, r_w, wi, wo, tokens=toks)
     assert_close(to_np(y)[toks], ref_y, "y[sampled]")
     dx, dtw = oracle.ffn_bwd_tokens(x, r_idx, r_w, wi, wo, dy, tokens=toks)
