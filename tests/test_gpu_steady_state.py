@@ -46,7 +46,7 @@ def _same_bits(a, b):
 
 
 @pytest.mark.parametrize("op,epi,K,N", [("nn", "none", 512, 1024), ("nn", "swiglu", 512, 1024),
-                                         ("nt", "none", 1024, 512), ("nt", "swiglu_bwd", 512, 512)])
+                                         ("nt", "none", 1024, 1024), ("nt", "swiglu_bwd", 512, 1024)])
 def test_grouped_gemm_small_grid_runs_many_tiles_per_workgroup(op, epi, K, N):
     M, E = 6000, 12
     rng = np.random.default_rng(K + N)
