@@ -44,7 +44,7 @@ def _lib(real: str) -> C.CDLL:
             "orc_ffn_fwd_tokens": ([_i32, _i32, _i32, _i32, _p, C.c_int, _p, _p, _p, C.c_int, _p, C.c_int,
                                     _i64, _p, _p, _p, _p, _p], C.c_int),
             "orc_ffn_bwd_tokens": ([_i32, _i32, _i32, _i32, _p, C.c_int, _p, _p, _p, C.c_int, _p, C.c_int,
-                                    _p, C.c_int, _i64, _p, _p, _p], C.c_int),
+                                    _p, C.c_int, _i64, _p, _p, _p, _i32], C.c_int),
             "orc_ffn_wgrad_expert": ([_i32, _i32, _i32, _i32, _p, C.c_int, _p, _p, _p, C.c_int, _p, C.c_int,
                                       _p, C.c_int, _i32, _i64, _p, _p, _p, _i32], C.c_int),
             "orc_grouped_gemm": ([_i32, _i32, _p, C.c_int, _p, C.c_int, _p, C.c_int, _p, _i32, _i64, _i32, _i32,
@@ -211,8 +211,10 @@ def ffn_fwd_tokens(x, topk_idx, topk_w, wi, wo, tokens=None, real: str = "f32", 
     return (y, h, a, o) if want_intermediates else y
 
 
-def ffn_bwd_tokens(x, topk_idx, topk_w, wi, wo, dy, tokens=None, real: str = "f32", threads: int | None = None):
-    """(dx [n, emb], dtopk_w [n, k]) for the listed tokens, routing held fixed."""
+def ffn_bwd_tokens(x, topk_idx, topk_w, wi, wo, dy, tokens=None, real: str = "f32", threads: int | None = None,
+                   stored_bf16: bool = False):
+    """(dx [n, emb], dtopk_w [n, k]) for the listed tokens, routing held fixed. With stored_bf16, o, dh and
+    dxs are rounded to bf16 where the layer stores them (moe_oracle.c, R9)."""
     x = np.ascontiguousarray(x)
     dy = np.ascontiguousarray(dy)
     wi = np.ascontiguousarray(wi)
@@ -238,7 +240,7 @@ def ffn_bwd_tokens(x, topk_idx, topk_w, wi, wo, dy, tokens=None, real: str = "f3
         lo, hi = lo_hi
         _check(lib.orc_ffn_bwd_tokens(emb, mlp, E, k, xp, xdt, _ptr(topk_idx), _ptr(topk_w), wip, widt, wop, wodt,
                                       dyp, dydt, hi - lo, tokens[lo:hi].ctypes.data, dx[lo:hi].ctypes.data,
-                                      dw[lo:hi].ctypes.data), "ffn_bwd_tokens")
+                                      dw[lo:hi].ctypes.data, int(bool(stored_bf16))), "ffn_bwd_tokens")
 
     chunks = _split(n, threads or default_threads())
     with ThreadPoolExecutor(len(chunks) or 1) as ex:

@@ -266,8 +266,10 @@ static void expert_forward(scratch_t* s, int32_t e, const void* wi, int wi_dt, c
   }
 }
 
-/* given dov = d(loss)/d(o): da = dov . wo[e]^T, dh = [dgate | dup], dxs = dh . wi[e]^T */
-static void expert_backward(scratch_t* s, int32_t e, const void* wi, int wi_dt, const void* wo, int wo_dt) {
+/* given dov = d(loss)/d(o): da = dov . wo[e]^T, dh = [dgate | dup], dxs = dh . wi[e]^T;
+   with round_dh, dh is rounded to bf16 (kept so in s->dh) before dxs */
+static void expert_backward_r(scratch_t* s, int32_t e, const void* wi, int wi_dt, const void* wo, int wo_dt,
+                              int round_dh) {
   const int32_t emb = s->emb, mlp = s->mlp, n2 = 2 * mlp;
   for (int32_t c = 0; c < mlp; ++c) {
     load_row(wo, wo_dt, ((int64_t)e * mlp + c) * emb, emb, s->wrow);
@@ -280,12 +282,18 @@ static void expert_backward(scratch_t* s, int32_t e, const void* wi, int wi_dt, 
     s->dh[c] = s->da[c] * u * sg * ((real)1 + g * ((real)1 - sg)); /* d silu(g)/dg = sg (1 + g (1 - sg)) */
     s->dh[mlp + c] = s->da[c] * silu(g);
   }
+  if (round_dh)
+    for (int32_t c = 0; c < n2; ++c) s->dh[c] = round_bf16(s->dh[c]);
   for (int32_t i = 0; i < emb; ++i) {
     load_row(wi, wi_dt, ((int64_t)e * emb + i) * n2, n2, s->wrow);
     real acc = 0;
     for (int32_t c = 0; c < n2; ++c) acc += s->dh[c] * s->wrow[c];
     s->dxs[i] = acc;
   }
+}
+
+static void expert_backward(scratch_t* s, int32_t e, const void* wi, int wi_dt, const void* wo, int wo_dt) {
+  expert_backward_r(s, e, wi, wi_dt, wo, wo_dt, 0);
 }
 
 static int check_common(int32_t emb, int32_t mlp, int32_t E, int32_t k, int x_dt, int wi_dt, int wo_dt) {
@@ -332,11 +340,13 @@ done:
 }
 
 /* Backward for the listed tokens, routing held fixed, loss L = sum(dy * y):
-   dx[i] = sum_j (FFN_e)'(x[t])^T (w_j dy[t]),  dtopk_w[i, j] = <FFN_e(x[t]), dy[t]>. */
+   dx[i] = sum_j (FFN_e)'(x[t])^T (w_j dy[t]),  dtopk_w[i, j] = <FFN_e(x[t]), dy[t]>.
+   stored_bf16 != 0 takes reading R9 into the backward: o is rounded to bf16 before the dtopk_w dot
+   product, dh before dxs = dh . wi[e]^T, and dxs before the sum over picks. */
 int orc_ffn_bwd_tokens(int32_t emb, int32_t mlp, int32_t E, int32_t k, const void* x, int x_dt,
                        const int32_t* topk_idx, const float* topk_w, const void* wi, int wi_dt, const void* wo,
                        int wo_dt, const void* dy, int dy_dt, int64_t ntok, const int64_t* tokens, real* dx,
-                       real* dtopk_w) {
+                       real* dtopk_w, int32_t stored_bf16) {
   int rc = check_common(emb, mlp, E, k, x_dt, wi_dt, wo_dt);
   if (rc) return rc;
   if (!valid_dt(dy_dt) || !x || !topk_idx || !topk_w || !wi || !wo || !dy) return ORC_EINVAL;
@@ -358,10 +368,14 @@ int orc_ffn_bwd_tokens(int32_t emb, int32_t mlp, int32_t E, int32_t k, const voi
       expert_forward(&s, e, wi, wi_dt, wo, wo_dt);
       real w = (real)topk_w[t * k + j];
       real dw = 0;
+      if (stored_bf16)
+        for (int32_t n = 0; n < emb; ++n) s.o[n] = round_bf16(s.o[n]);
       for (int32_t n = 0; n < emb; ++n) dw += s.o[n] * s.dyrow[n];
       if (dtopk_w) dtopk_w[q * k + j] = dw;
       for (int32_t n = 0; n < emb; ++n) s.dov[n] = w * s.dyrow[n];
-      expert_backward(&s, e, wi, wi_dt, wo, wo_dt);
+      expert_backward_r(&s, e, wi, wi_dt, wo, wo_dt, stored_bf16);
+      if (stored_bf16)
+        for (int32_t i = 0; i < emb; ++i) s.dxs[i] = round_bf16(s.dxs[i]);
       for (int32_t i = 0; i < emb; ++i) dxr[i] += s.dxs[i];
     }
   }

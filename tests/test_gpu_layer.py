@@ -139,7 +139,8 @@ def test_layer_backward_every_token_and_expert():
     g = moe.ffn_bwd(d["dy"], saved, d["wi"], d["wo"], wl.k)
     r_idx, r_w, *_ = _check_routing_and_permute(saved, h)
     x, wi, wo, dy = bits(h["x"]), bits(h["wi"]), bits(h["wo"]), bits(h["dy"])
-    dx, dtw = oracle.ffn_bwd_tokens(x, r_idx, r_w, wi, wo, dy)
+    # o, dh and dxs are stored in bf16 between stages (R9): the reference rounds them there too
+    dx, dtw = oracle.ffn_bwd_tokens(x, r_idx, r_w, wi, wo, dy, stored_bf16=True)
     assert_close(to_np(g["dx"]), dx, "dx")
     assert_close(g["dtopk_w"].cpu().numpy(), dtw, "dtopk_w")
     # dW = X^T dH multiplies factors the layer stores in bf16 (a, do, dh): the reference rounds them
@@ -229,7 +230,7 @@ def test_full_size_deepseek_v3_shape_forward_backward_sampled():
     toks = _sample_tokens(wl.T, 64, 5)
     ref_y = oracle.ffn_fwd_tokens(x, r_idx, r_w, wi, wo, tokens=toks)
     assert_close(to_np(y)[toks], ref_y, "y[sampled]")
-    dx, dtw = oracle.ffn_bwd_tokens(x, r_idx, r_w, wi, wo, dy, tokens=toks)
+    dx, dtw = oracle.ffn_bwd_tokens(x, r_idx, r_w, wi, wo, dy, tokens=toks, stored_bf16=True)
     assert_close(to_np(g["dx"])[toks], dx, "dx[sampled]")
     assert_close(g["dtopk_w"].cpu().numpy()[toks], dtw, "dtopk_w[sampled]")
     # dW on the most- and least-loaded experts (longest and shortest reductions), the median one and six

@@ -157,7 +157,7 @@ def test_layer_backward_many_tiles_per_workgroup(many_tiles):
     x, wi, wo, dy = bits(h["x"]), bits(h["wi"]), bits(h["wo"]), bits(h["dy"])
     idx, w, _ = oracle.route(x, h["wr"].numpy(), None, wl.k)
     assert np.array_equal(saved["topk_idx"].cpu().numpy(), idx)
-    dx, dtw = oracle.ffn_bwd_tokens(x, idx, w, wi, wo, dy)
+    dx, dtw = oracle.ffn_bwd_tokens(x, idx, w, wi, wo, dy, stored_bf16=True)
     assert_close(to_np(g["dx"]), dx, "dx (every token)")
     assert_close(g["dtopk_w"].cpu().numpy(), dtw, "dtopk_w (every token)")
     gs = np.bincount(idx.reshape(-1), minlength=wl.E)

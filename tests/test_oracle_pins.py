@@ -457,6 +457,41 @@ def test_weight_gradient_with_stored_bf16_factors():
             assert np.linalg.norm(pv - rv) / np.linalg.norm(rv) > 1e-3, (e, name)
 
 
+def test_backward_with_stored_bf16_activations():
+    """ffn_bwd_tokens with stored_bf16 (reading R9): dtopk_w from o rounded to bf16, dxs from dh rounded
+    to bf16, dx the sum of the rounded dxs. Reference: float64 numpy per token and pick, roundings by torch;
+    the unrounded oracle is measurably elsewhere."""
+    T, emb, mlp, E, k = 24, 64, 32, 4, 2
+    x, wr, wi, wo = _case(T, emb, mlp, E, k, seed=35, sigma=0.4)
+    dy = _bf16(np.random.default_rng(6).standard_normal((T, emb)))
+    idx, w, _ = oracle.route(x, wr, None, k)
+    dx, dtw = oracle.ffn_bwd_tokens(x, idx, w, wi, wo, dy, stored_bf16=True)
+    dx0, dtw0 = oracle.ffn_bwd_tokens(x, idx, w, wi, wo, dy)
+    xv, wiv, wov, dyv = _val(x), _val(wi), _val(wo), _val(dy)
+    rdx = np.zeros((T, emb))
+    rdw = np.zeros((T, k))
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            h = xv[t] @ wiv[e]
+            g, u = h[:mlp], h[mlp:]
+            o = (_silu(g) * u) @ wov[e]
+            rdw[t, j] = _bf16_round(o) @ dyv[t]
+            da = (float(w[t, j]) * dyv[t]) @ wov[e].T
+            sg = scipy.special.expit(g)
+            dh = _bf16_round(np.concatenate([da * u * sg * (1 + g * (1 - sg)), da * g * sg]))
+            rdx[t] += _bf16_round(dh @ wiv[e].T)
+    # dxs sums 2*mlp products with cancellation, so the fp32 oracle and the float64 reference round a
+    # few dxs elements to neighbouring bf16 values (one unit in the last place each); an element is
+    # counted as differing beyond 1e-5 of the largest |dx|
+    def off(a, ref):
+        return np.mean(np.abs(a - ref) > 1e-5 * np.abs(ref).max())
+    assert np.linalg.norm(dx - rdx) / np.linalg.norm(rdx) <= 1e-3 and off(dx, rdx) <= 0.05
+    assert off(dx0, rdx) >= 0.5                      # without the roundings nearly every element differs
+    assert np.linalg.norm(dtw - rdw) / np.linalg.norm(rdw) <= 1e-6
+    assert np.linalg.norm(dtw0 - rdw) / np.linalg.norm(rdw) > 1e-4
+
+
 def test_backward_stage_composition_equals_per_token_backward():
     """combine-bwd -> NT GEMM + SwiGLU-bwd -> NT GEMM -> permute-bwd == the per-token backward;
     wgrad stage on the sorted activations == the per-expert weight gradients."""
