@@ -213,8 +213,8 @@ def ffn_fwd_tokens(x, topk_idx, topk_w, wi, wo, tokens=None, real: str = "f32", 
 
 def ffn_bwd_tokens(x, topk_idx, topk_w, wi, wo, dy, tokens=None, real: str = "f32", threads: int | None = None,
                    stored_bf16: bool = False):
-    """(dx [n, emb], dtopk_w [n, k]) for the listed tokens, routing held fixed. With stored_bf16, o, dh and
-    dxs are rounded to bf16 where the layer stores them (moe_oracle.c, R9)."""
+    """(dx [n, emb], dtopk_w [n, k]) for the listed tokens, routing held fixed. With stored_bf16, a, o, dh
+    and dxs are rounded to bf16 where the layer stores them (moe_oracle.c, R9)."""
     x = np.ascontiguousarray(x)
     dy = np.ascontiguousarray(dy)
     wi = np.ascontiguousarray(wi)

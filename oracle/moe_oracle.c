@@ -67,11 +67,13 @@
  *     even mantissa, magnitudes above 448 saturating to 448, the sign kept
  *     (also on zero).
  *  R9 the pages fix only fp32 accumulation. Between stages the layer stores
- *     its activations (a, o, do = w * dy, dh) in bf16, rounded to nearest
- *     with ties to even. The reference keeps every intermediate in REAL; the
- *     weight-gradient function can instead round a, do and dh to bf16 where
- *     the layer stores them (stored_bf16), because each term of dW is a
- *     product of two such stored factors.
+ *     its activations (a, o, do = w * dy, dh, dxs) in bf16, rounded to
+ *     nearest with ties to even. The reference keeps every intermediate in
+ *     REAL. The backward functions can instead round them to bf16 where the
+ *     layer stores them (stored_bf16): each term of dW is a product of two
+ *     stored factors, and dtopk_w is a dot product over emb of the stored o,
+ *     so the storage alone moves those results by more than a bf16 output
+ *     rounding does.
  */
 #include <math.h>
 #include <stdint.h>
@@ -250,8 +252,10 @@ static int scratch_init(scratch_t* s, int32_t emb, int32_t mlp) {
 }
 static void scratch_free(scratch_t* s) { free(s->xrow); }
 
-/* h = x . wi[e] (2*mlp columns), a = silu(h[:mlp]) * h[mlp:], o = a . wo[e]. */
-static void expert_forward(scratch_t* s, int32_t e, const void* wi, int wi_dt, const void* wo, int wo_dt) {
+/* h = x . wi[e] (2*mlp columns), a = silu(h[:mlp]) * h[mlp:], o = a . wo[e]; with round_a, a is rounded
+   to bf16 (kept so in s->a) before o. */
+static void expert_forward_r(scratch_t* s, int32_t e, const void* wi, int wi_dt, const void* wo, int wo_dt,
+                             int round_a) {
   const int32_t emb = s->emb, mlp = s->mlp, n2 = 2 * mlp;
   for (int32_t c = 0; c < n2; ++c) s->h[c] = 0;
   for (int32_t i = 0; i < emb; ++i) {
@@ -259,6 +263,8 @@ static void expert_forward(scratch_t* s, int32_t e, const void* wi, int wi_dt, c
     for (int32_t c = 0; c < n2; ++c) s->h[c] += s->xrow[i] * s->wrow[c];
   }
   for (int32_t c = 0; c < mlp; ++c) s->a[c] = silu(s->h[c]) * s->h[mlp + c];
+  if (round_a)
+    for (int32_t c = 0; c < mlp; ++c) s->a[c] = round_bf16(s->a[c]);
   for (int32_t n = 0; n < emb; ++n) s->o[n] = 0;
   for (int32_t c = 0; c < mlp; ++c) {
     load_row(wo, wo_dt, ((int64_t)e * mlp + c) * emb, emb, s->wrow);
@@ -292,6 +298,9 @@ static void expert_backward_r(scratch_t* s, int32_t e, const void* wi, int wi_dt
   }
 }
 
+static void expert_forward(scratch_t* s, int32_t e, const void* wi, int wi_dt, const void* wo, int wo_dt) {
+  expert_forward_r(s, e, wi, wi_dt, wo, wo_dt, 0);
+}
 static void expert_backward(scratch_t* s, int32_t e, const void* wi, int wi_dt, const void* wo, int wo_dt) {
   expert_backward_r(s, e, wi, wi_dt, wo, wo_dt, 0);
 }
@@ -341,8 +350,8 @@ done:
 
 /* Backward for the listed tokens, routing held fixed, loss L = sum(dy * y):
    dx[i] = sum_j (FFN_e)'(x[t])^T (w_j dy[t]),  dtopk_w[i, j] = <FFN_e(x[t]), dy[t]>.
-   stored_bf16 != 0 takes reading R9 into the backward: o is rounded to bf16 before the dtopk_w dot
-   product, dh before dxs = dh . wi[e]^T, and dxs before the sum over picks. */
+   stored_bf16 != 0 takes reading R9 into the backward: a is rounded to bf16 before o = a . wo[e], o
+   before the dtopk_w dot product, dh before dxs = dh . wi[e]^T, and dxs before the sum over picks. */
 int orc_ffn_bwd_tokens(int32_t emb, int32_t mlp, int32_t E, int32_t k, const void* x, int x_dt,
                        const int32_t* topk_idx, const float* topk_w, const void* wi, int wi_dt, const void* wo,
                        int wo_dt, const void* dy, int dy_dt, int64_t ntok, const int64_t* tokens, real* dx,
@@ -365,7 +374,7 @@ int orc_ffn_bwd_tokens(int32_t emb, int32_t mlp, int32_t E, int32_t k, const voi
         rc = ORC_ERANGE;
         goto done;
       }
-      expert_forward(&s, e, wi, wi_dt, wo, wo_dt);
+      expert_forward_r(&s, e, wi, wi_dt, wo, wo_dt, stored_bf16);
       real w = (real)topk_w[t * k + j];
       real dw = 0;
       if (stored_bf16)
@@ -412,12 +421,11 @@ int orc_ffn_wgrad_expert(int32_t emb, int32_t mlp, int32_t E, int32_t k, const v
     }
     load_row(x, x_dt, t * emb, emb, s.xrow);
     load_row(dy, dy_dt, t * emb, emb, s.dyrow);
-    expert_forward(&s, e, wi, wi_dt, wo, wo_dt);
+    expert_forward_r(&s, e, wi, wi_dt, wo, wo_dt, stored_bf16);
     real w = (real)topk_w[slot];
     for (int32_t n = 0; n < emb; ++n) s.dov[n] = w * s.dyrow[n];
     expert_backward(&s, e, wi, wi_dt, wo, wo_dt);
-    if (stored_bf16) {
-      for (int32_t c = 0; c < mlp; ++c) s.a[c] = round_bf16(s.a[c]);
+    if (stored_bf16) { /* a was rounded by the forward */
       for (int32_t n = 0; n < emb; ++n) s.dov[n] = round_bf16(s.dov[n]);
       for (int32_t c = 0; c < n2; ++c) s.dh[c] = round_bf16(s.dh[c]);
     }

@@ -458,8 +458,8 @@ def test_weight_gradient_with_stored_bf16_factors():
 
 
 def test_backward_with_stored_bf16_activations():
-    """ffn_bwd_tokens with stored_bf16 (reading R9): dtopk_w from o rounded to bf16, dxs from dh rounded
-    to bf16, dx the sum of the rounded dxs. Reference: float64 numpy per token and pick, roundings by torch;
+    """ffn_bwd_tokens with stored_bf16 (reading R9): o from a rounded to bf16, dtopk_w from o rounded to
+    bf16, dxs from dh rounded to bf16, dx the sum of the rounded dxs. Reference: float64 numpy per token and pick, roundings by torch;
     the unrounded oracle is measurably elsewhere."""
     T, emb, mlp, E, k = 24, 64, 32, 4, 2
     x, wr, wi, wo = _case(T, emb, mlp, E, k, seed=35, sigma=0.4)
@@ -475,7 +475,7 @@ def test_backward_with_stored_bf16_activations():
             e = idx[t, j]
             h = xv[t] @ wiv[e]
             g, u = h[:mlp], h[mlp:]
-            o = (_silu(g) * u) @ wov[e]
+            o = _bf16_round(_silu(g) * u) @ wov[e]
             rdw[t, j] = _bf16_round(o) @ dyv[t]
             da = (float(w[t, j]) * dyv[t]) @ wov[e].T
             sg = scipy.special.expit(g)
