@@ -43,6 +43,29 @@ def assert_close(got, ref, name: str, rel: float = REL_FROB, abs_: float = MAX_A
     return r, a
 
 
+def bf16_ulp(v):
+    """Unit in the last place of bf16 at |v| (8 significand bits): 2^(floor(log2|v|) - 7); the smallest
+    normal's for |v| below it."""
+    a = np.maximum(np.abs(np.asarray(v, np.float64)), 2.0 ** -126)
+    return np.ldexp(1.0, np.floor(np.log2(a)).astype(np.int64) - 7)
+
+
+def assert_close_bf16_out(got, ref, name: str):
+    """A bf16 output against a reference with the same bf16-stored inputs: relF <= 1e-2, and per element
+    |G - O| <= max(2e-2, ulp_bf16(O)). Two fp32 accumulations of the same terms in different orders can
+    round to adjacent bf16 values, one ulp apart; from |O| >= 4 that ulp (2^-5 and up) is larger than
+    2e-2, so no bf16 result could meet the fixed bound there. Below 4 the bound is the fixed 2e-2."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    r, a, m = errors(got, ref)
+    assert np.isfinite(got).all(), f"{name}: non-finite values"
+    bound = np.maximum(MAX_ABS, bf16_ulp(ref))
+    worst = float(np.max(np.abs(got - ref) / bound)) if got.size else 0.0
+    assert r <= REL_FROB and worst <= 1.0, (f"{name}: rel_frob={r:.3e} (<= {REL_FROB}) max_abs={a:.3e} "
+                                            f"worst |G-O|/max(2e-2, ulp(O))={worst:.3f} max|ref|={m:.3g}")
+    return r, a
+
+
 def bf16_ulp_diff(a_bits: np.ndarray, b_bits: np.ndarray) -> int:
     """Largest distance in bf16 units in the last place between two bf16 arrays (same sign assumed near 0)."""
     def ordered(x):

@@ -21,7 +21,7 @@ import torch
 import mixture_experts_ffn_group_amd as moe
 import oracle
 import workloads
-from parity_util import assert_close, bf16_values, bits, to_np
+from parity_util import assert_close, assert_close_bf16_out, bf16_values, bits, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -122,7 +122,8 @@ def test_grid_argument_is_validated():
 
 # ---------------------------------------------------------------- the layer, many tiles per workgroup
 
-MANY = workloads.custom(65536, 512, 256, 16, 4, seed=4242, sigma_w=0.05, backward=True)
+# weights ~ N(0, 0.02), as in the pages' model settings
+MANY = workloads.custom(65536, 512, 256, 16, 4, seed=4242, sigma_w=0.02, backward=True)
 
 
 @pytest.fixture(scope="module")
@@ -164,8 +165,8 @@ def test_layer_backward_many_tiles_per_workgroup(many_tiles):
     experts = sorted({int(np.argmax(gs)), int(np.argmin(gs)), 3, 11})
     ref = oracle.ffn_wgrad_experts(x, idx, w, wi, wo, dy, experts, stored_bf16=True)
     for e in experts:
-        assert_close(to_np(g["dwi"][e]), ref[e][0], f"dwi[{e}]")
-        assert_close(to_np(g["dwo"][e]), ref[e][1], f"dwo[{e}]")
+        assert_close_bf16_out(to_np(g["dwi"][e]), ref[e][0], f"dwi[{e}]")
+        assert_close_bf16_out(to_np(g["dwo"][e]), ref[e][1], f"dwo[{e}]")
 
 
 def moe_grid():
