@@ -134,6 +134,24 @@ int moe_permute(const moe_shape_t* shape, const moe_bf16_t* x, const int32_t* to
                 int32_t* group_offsets, int32_t* sorted_slot, int32_t* slot_row, moe_bf16_t* xs, void* ws,
                 size_t ws_bytes, moe_stream_t stream);
 
+/*
+ * moe_permute_noalloc -- moe_permute without a workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation). Same arguments, outputs and
+ * errors as moe_permute, minus ws / ws_bytes. Its masks and row bases live in
+ * a fixed scratch array of the library, 4 MiB per GPU (allocated when the
+ * library's device code is loaded on that GPU and held until the process
+ * ends); it needs 12 * ceil(T / 64) * E bytes (each of its two regions
+ * rounded up to 256), so T <= 174,720 at E = 128 and T <= 87,360 at E = 256;
+ * a larger shape returns MOE_ERR_WORKSPACE and enqueues nothing. The call
+ * allocates nothing. All calls on one GPU share that GPU's scratch, which
+ * keeps the last call's contents: calls that may overlap on one GPU (several
+ * streams, several threads) race and must be serialised by the caller.
+ */
+int moe_permute_noalloc(const moe_shape_t* shape, const moe_bf16_t* x, const int32_t* topk_idx,
+                        int32_t* group_sizes, int32_t* group_offsets, int32_t* sorted_slot, int32_t* slot_row,
+                        moe_bf16_t* xs, moe_stream_t stream);
+
 /* Optional row mapping of a grouped GEMM (see moe_grouped_gemm). */
 typedef struct {
   const int32_t* row_slot;  /* [M] device, or NULL: output row r reads A row row_slot[r] / slot_div */

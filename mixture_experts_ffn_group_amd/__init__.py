@@ -87,9 +87,10 @@ def route(k: int, x: torch.Tensor | None = None, wr: torch.Tensor | None = None,
     return idx, w
 
 
-def permute(x: torch.Tensor, topk_idx: torch.Tensor, E: int, rows: bool = True) -> dict:
+def permute(x: torch.Tensor, topk_idx: torch.Tensor, E: int, rows: bool = True, noalloc: bool = False) -> dict:
     """Expert-sorted gather: dict of group_sizes [E], group_offsets [E+1], sorted_slot [S], slot_row [S]
-    (int32) and xs [S, emb] bf16. rows=False builds the index only (no xs)."""
+    (int32) and xs [S, emb] bf16. rows=False builds the index only (no xs). noalloc=True calls
+    moe_permute_noalloc, which takes no workspace (the library's fixed per-GPU scratch)."""
     _need(x, "x", torch.bfloat16)
     dev = x.device
     _need(topk_idx, "topk_idx", torch.int32, dev)
@@ -97,13 +98,19 @@ def permute(x: torch.Tensor, topk_idx: torch.Tensor, E: int, rows: bool = True) 
     k = topk_idx.shape[1]
     S = T * k
     s = _lib.shape(T, emb, 64, E, k)
-    ws_n = int(_lib.lib().moe_permute_workspace_bytes(C.byref(s)))
-    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
     out = dict(group_sizes=torch.empty(E, dtype=torch.int32, device=dev),
                group_offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
                sorted_slot=torch.empty(S, dtype=torch.int32, device=dev),
                slot_row=torch.empty(S, dtype=torch.int32, device=dev),
                xs=torch.empty((S, emb), dtype=torch.bfloat16, device=dev) if rows else None)
+    if noalloc:
+        _lib.check(_lib.lib().moe_permute_noalloc(C.byref(s), _ptr(x), _ptr(topk_idx), _ptr(out["group_sizes"]),
+                                                  _ptr(out["group_offsets"]), _ptr(out["sorted_slot"]),
+                                                  _ptr(out["slot_row"]), _ptr(out["xs"]), _stream(dev)),
+                   "moe_permute_noalloc")
+        return out
+    ws_n = int(_lib.lib().moe_permute_workspace_bytes(C.byref(s)))
+    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
     _lib.check(_lib.lib().moe_permute(C.byref(s), _ptr(x), _ptr(topk_idx), _ptr(out["group_sizes"]),
                                       _ptr(out["group_offsets"]), _ptr(out["sorted_slot"]), _ptr(out["slot_row"]),
                                       _ptr(out["xs"]), _ptr(ws), ws.numel(), _stream(dev)), "moe_permute")

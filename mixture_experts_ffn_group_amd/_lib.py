@@ -50,6 +50,7 @@ SIGNATURES = {
     "moe_route_bwd_workspace_bytes": ([_SHP], _sz),
     "moe_route": ([_SHP, _p, _p, _p, _p, _p, _p, _p], C.c_int),
     "moe_permute": ([_SHP, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p], C.c_int),
+    "moe_permute_noalloc": ([_SHP, _p, _p, _p, _p, _p, _p, _p, _p], C.c_int),
     "moe_grouped_gemm": ([C.c_int, C.c_int, _p, _p, _p, _p, _p, _i32, _i64, _i32, _i32, C.POINTER(MoeGemmRows), _p,
                           _p], C.c_int),
     "moe_grouped_gemm_wgrad": ([_p, _p, _p, _i32, _i64, _i32, _i32, _p, _p], C.c_int),

@@ -22,6 +22,14 @@ hipError_t launch_permute(int64_t T, int emb, int E, int k, const uint16_t* x, c
                           int32_t* group_sizes, int32_t* group_offsets, int32_t* sorted_slot, int32_t* slot_row,
                           uint16_t* xs, uint64_t* masks, int32_t* base, hipStream_t stream);
 
+// The same permute on the library's fixed per-GPU scratch (kPermuteScratchBytes): no workspace argument,
+// no allocation. The masks and bases ([nblk, E] uint64, [nblk, E] int32, each rounded up to 256 bytes) must
+// fit; concurrent calls on one GPU share the scratch and race.
+constexpr size_t kPermuteScratchBytes = size_t(4) << 20;
+hipError_t launch_permute_noalloc(int64_t T, int emb, int E, int k, const uint16_t* x, const int32_t* topk_idx,
+                                  int32_t* group_sizes, int32_t* group_offsets, int32_t* sorted_slot,
+                                  int32_t* slot_row, uint16_t* xs, hipStream_t stream);
+
 // grid: workgroups of the persistent grid (a multiple of 8); 0 = persistent_grid().
 // row_slot (nullable): output row r reads A row row_slot[r] / slot_div, row_slot values in [0, n_slots).
 // slot_scale (nullable): output row r is scaled by slot_scale[row_slot[r]] (or slot_scale[r]).

@@ -260,6 +260,28 @@ int moe_permute(const moe_shape_t* s, const moe_bf16_t* x, const int32_t* topk_i
                     "moe_permute");
 }
 
+int moe_permute_noalloc(const moe_shape_t* s, const moe_bf16_t* x, const int32_t* topk_idx, int32_t* group_sizes,
+                        int32_t* group_offsets, int32_t* sorted_slot, int32_t* slot_row, moe_bf16_t* xs,
+                        moe_stream_t stream) {
+  g_detail[0] = 0;
+  if (int rc = check_shape(s)) return rc;
+  NEED(group_sizes);
+  NEED(group_offsets);
+  if (s->T > 0) {
+    NEED(topk_idx);
+    NEED(sorted_slot);
+    NEED(slot_row);
+    MAYBE(xs);
+    if (xs) NEED(x);
+  }
+  if (permute_ws(s) > moe::kPermuteScratchBytes)
+    return fail(MOE_ERR_WORKSPACE, "needs %zu bytes of scratch; the fixed scratch holds %zu (12 * ceil(T/64) * E)",
+                permute_ws(s), moe::kPermuteScratchBytes);
+  return hip_status(moe::launch_permute_noalloc(s->T, s->emb, s->E, s->k, x, topk_idx, group_sizes, group_offsets,
+                                                sorted_slot, slot_row, xs, (hipStream_t)stream),
+                    "moe_permute_noalloc");
+}
+
 int moe_grouped_gemm_grid(int op, int epilogue, const moe_bf16_t* A, const moe_bf16_t* B, const float* aux_in,
                           float* aux_out, const int32_t* group_offsets, int32_t E, int64_t M, int32_t K, int32_t N,
                           const moe_gemm_rows_t* rows, moe_bf16_t* C, int32_t grid, moe_stream_t stream) {

@@ -13,6 +13,8 @@
 //   base[b][e]     = group_offsets[e] + sum_{b' < b} popcount(mask[b'][e]),
 //   row(t, j)      = base[b][e] + popcount(mask[b][e] & lanes below t),
 // which is the rank of token t among the tokens of expert e: the stable order.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -172,6 +174,47 @@ __global__ __launch_bounds__(256) void index_kernel(int64_t T, int E, int k, con
 }
 
 }  // namespace
+
+// Fixed scratch of the allocation-free permute: the per-block expert masks
+// and row bases, [nblk, E] uint64 then [nblk, E] int32, each region rounded up
+// to 256 bytes. One copy per GPU, held until the process ends. Host code
+// passes its device address (permute_scratch), never this name.
+static __device__ __align__(256) uint8_t scratch[kPermuteScratchBytes];
+
+// Device address of this GPU's copy of `scratch`, looked up once per device
+// (with that device current) and kept.
+hipError_t permute_scratch(uint8_t** out) {
+  static std::mutex mu;
+  static uint8_t* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_permute_noalloc(int64_t T, int emb, int E, int k, const uint16_t* x, const int32_t* topk_idx,
+                                  int32_t* group_sizes, int32_t* group_offsets, int32_t* sorted_slot,
+                                  int32_t* slot_row, uint16_t* xs, hipStream_t stream) {
+  const int64_t nblk = (T + kPermuteBlock - 1) / kPermuteBlock;
+  const size_t masks = ((size_t)nblk * E * sizeof(uint64_t) + 255) / 256 * 256;
+  const size_t base = ((size_t)nblk * E * sizeof(int32_t) + 255) / 256 * 256;
+  if (masks + base > kPermuteScratchBytes) return hipErrorInvalidValue;  // checked by the caller first
+  uint8_t* s = nullptr;
+  if (hipError_t e = permute_scratch(&s)) return e;
+  // every mask and base a call reads is written earlier in the same call, so the last call's contents
+  // need no clearing
+  return launch_permute(T, emb, E, k, x, topk_idx, group_sizes, group_offsets, sorted_slot, slot_row, xs,
+                        reinterpret_cast<uint64_t*>(s), reinterpret_cast<int32_t*>(s + masks), stream);
+}
 
 hipError_t launch_permute(int64_t T, int emb, int E, int k, const uint16_t* x, const int32_t* topk_idx,
                           int32_t* group_sizes, int32_t* group_offsets, int32_t* sorted_slot, int32_t* slot_row,
