@@ -109,7 +109,8 @@ __global__ __launch_bounds__(1024) void scan_kernel(int64_t nblk, int E, const u
   }
 }
 
-// One wave per token: read the row once (16 bytes per lane per chunk), write it to its k rows.
+// One wave per token: read the row once (16 bytes per lane per chunk), write it to its k rows
+// (non-temporal: the sorted copy is read back only by later kernels).
 __global__ __launch_bounds__(256) void scatter_kernel(int64_t T, int emb, int E, int k, const uint16_t* __restrict__ x,
                                                       const int32_t* __restrict__ topk_idx,
                                                       const uint64_t* __restrict__ masks,
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(int64_t T, int emb, int E,
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int c = c0 + lane + 64 * u;
-        if (c < nch) st16(dst + c * 8, v[u]);
+        if (c < nch) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4_t*>(dst + c * 8));
       }
     }
   }
