@@ -441,3 +441,37 @@ def test_route_bwd_full_size_gemma4_class():
     g = torch.from_numpy(np.random.default_rng(5).standard_normal((wl.T, wl.k)).astype(np.float32)).to(DEV)
     out = moe.route_bwd(x.to(DEV), wr.to(DEV), idx, w, g, perm["sorted_slot"], perm["group_offsets"])
     _check_route_bwd(x, wr, idx, w, g, perm, None, out, None, want_dx=False)
+
+
+@pytest.mark.parametrize("op,epi", [("nn", "swiglu"), ("nt", "swiglu_bwd")])
+def test_swiglu_epilogues_with_saturating_gates(op, epi):
+    """Gate values far into both tails (|g| up to ~200): the sigmoid's exponential overflows to inf or
+    underflows to 0 and its reciprocal must still give silu -> -0 / g and sigmoid -> 0 / 1, as in the
+    oracle's double-precision evaluation."""
+    M, K, N, E = 512, 64, 128, 2
+    rng = np.random.default_rng(99)
+    off = np.array([0, 200, M], np.int32)
+    A = rng.standard_normal((M, K))
+    A[:, 0] = np.linspace(-60.0, 60.0, M)              # one large input column drives the gates
+    A = _bf16_dev(A)
+    Nb = 2 * N if epi == "swiglu" else N
+    Bn = rng.standard_normal((E, K, Nb) if op == "nn" else (E, Nb, K)) * (0.5 / np.sqrt(K))
+    if op == "nn":
+        Bn[:, 0, :] = 3.0                               # gate and up both see 3 * A[:, 0]
+    else:
+        Bn[:, :, 0] = 3.0
+    B = _bf16_dev(Bn)
+    h = None
+    if epi == "swiglu_bwd":
+        hv = rng.standard_normal((M, 2 * N)) * 0.5
+        hv[:, :N] = np.linspace(-200.0, 200.0, M)[:, None]  # saved gate values in both tails
+        h = hv.astype(np.float32)
+    got = moe.grouped_gemm(A, B, torch.from_numpy(off).to(DEV), op=op, epilogue=epi,
+                           aux_in=None if h is None else torch.from_numpy(h).to(DEV))
+    g = to_np(got)
+    assert np.isfinite(g).all()
+    ref = oracle.grouped_gemm(0 if op == "nn" else 1, 1 if epi == "swiglu" else 2, bits(A), bits(B), off, aux=h)
+    rel = np.linalg.norm(g - ref) / np.linalg.norm(ref)
+    assert rel <= 1e-2, rel
+    # elementwise: one bf16 rounding of the result, plus the fp32 sums' own error
+    assert np.all(np.abs(g - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-3 * np.abs(ref).max()), np.abs(g - ref).max()
