@@ -107,52 +107,126 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
+// Row maximum with each lane move feeding the max directly (every lane of a
+// row has a source under these four patterns, so no lane keeps an old value).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_max_step(uint32_t v) {
+  return max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ uint32_t row_max_fused(uint32_t v) {
+  v = dpp_max_step<0xb1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max_step<0x4e>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max_step<0x141>(v);  // row_half_mirror
+  v = dpp_max_step<0x140>(v);  // row_mirror
+  return v;
+}
+
+// Batcher's odd-even merge sort network on N = 2^m elements (Knuth, TAOCP
+// vol. 3, 5.3.4), as a compile-time list of compare-exchange pairs.
+struct CxPair {
+  int a, b;
+};
+template <int N>
+struct OddEvenMergeNet {
+  CxPair p[N * N] = {};
+  int n = 0;
+  constexpr OddEvenMergeNet() {
+    for (int pp = 1; pp < N; pp <<= 1)
+      for (int kk = pp; kk >= 1; kk >>= 1)
+        for (int j = kk % pp; j + kk < N; j += 2 * kk)
+          for (int i = 0; i < kk && i + j + kk < N; ++i)
+            if ((i + j) / (2 * pp) == (i + j + kk) / (2 * pp)) p[n++] = CxPair{i + j, i + j + kk};
+  }
+};
+template <int N>
+__device__ __forceinline__ void sort_desc(uint64_t (&c)[N]) {
+  constexpr OddEvenMergeNet<N> net{};
+#pragma unroll
+  for (int q = 0; q < net.n; ++q) {
+    uint64_t& a = c[net.p[q].a];
+    uint64_t& b = c[net.p[q].b];
+    const bool sw = b > a;
+    const uint64_t hi = sw ? b : a, lo = sw ? a : b;
+    a = hi;
+    b = lo;
+  }
+}
+
 // Top-k for k <= 16, four tokens at a time per wave: token g of the group on
-// lanes 16g..16g+15, lane r holding experts r + 16q. Same picks as the
-// one-token-per-wave form below: the largest (key, -expert) each round.
+// lanes 16g..16g+15, lane r holding experts r + 16q as 64-bit candidates
+// (key(logit), ~expert), sorted once in descending order. Each round takes
+// the largest (key, -expert) of the row: one row maximum of the lanes' head
+// keys; when some row has more than one lane holding its maximum key (equal
+// logits, or only NaN and padding left at key 0), a second row maximum over
+// those lanes' low words picks the lowest expert. The winning lane parks the
+// expert in the token's logit row (already read into registers) and pops its
+// head. Same picks as taking the largest (key, -expert) of the remaining
+// candidates each round.
 template <int TB, int EP>
-__device__ __forceinline__ void route_topk16(const float* s_l, int64_t T, int64_t t0, int E, int k,
+__device__ __forceinline__ void route_topk16(float* s_l, int64_t T, int64_t t0, int E, int k,
                                              int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
   constexpr int EQ = EP / 16;       // experts per lane
-  constexpr int TPW = TB / kWaves;  // tokens per wave (a multiple of 4)
+  constexpr int TPW = TB / kWaves;  // tokens per wave (a multiple of 8)
+  constexpr int NG = 2;             // 4-token groups in flight per wave (independent chains)
+  static_assert(TPW % (4 * NG) == 0, "whole group pairs per wave");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r = lane & 15;
 #pragma unroll 1
-  for (int t4 = 0; t4 < TPW; t4 += 4) {
-    if (t0 + wave * TPW + t4 >= T) break;  // wave-uniform: no token of the group exists
-    const int tok = wave * TPW + t4 + g;
-    const int64_t t = t0 + tok;
-    uint64_t cand[EQ];
+  for (int t8 = 0; t8 < TPW; t8 += 4 * NG) {
+    if (t0 + wave * TPW + t8 >= T) break;  // wave-uniform: no token of the groups exists
+    float* row[NG];
+    int64_t t[NG];
+    uint64_t cand[NG][EQ];
 #pragma unroll
-    for (int q = 0; q < EQ; ++q) {
-      const int e = r + 16 * q;
-      const float l = s_l[tok * EP + e];
-      cand[q] = e < E ? (((uint64_t)order_key(l) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e)) : 0ull;
-    }
-    int my_e = 0;
-    float my_l = 0.0f, l0 = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      uint64_t best = 0ull;
+    for (int u = 0; u < NG; ++u) {
+      const int tok = wave * TPW + t8 + 4 * u + g;
+      t[u] = t0 + tok;
+      row[u] = s_l + tok * EP;
 #pragma unroll
-      for (int q = 0; q < EQ; ++q) best = cand[q] > best ? cand[q] : best;
-      const uint32_t key = row_max_u32((uint32_t)(best >> 32));
-      const uint32_t low = row_max_u32((uint32_t)(best >> 32) == key ? (uint32_t)best : 0u);
-      const int e = min(max((int)(0xffffffffu - low), 0), E - 1);
-      const float l = key_value(key);
-      if (j == 0) l0 = l;
-#pragma unroll
-      for (int q = 0; q < EQ; ++q)
-        if (e == r + 16 * q) cand[q] = 0ull;
-      if (r == j) {
-        my_e = e;
-        my_l = l;
+      for (int q = 0; q < EQ; ++q) {
+        const int e = r + 16 * q;
+        const float l = row[u][e];
+        cand[u][q] = e < E ? (((uint64_t)order_key(l) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e)) : 0ull;
       }
     }
-    const float ex = r < k ? expf(my_l - l0) : 0.0f;
-    const float sum = row_sum(ex);
-    if (r < k && t < T) {
-      topk_idx[t * k + r] = my_e;
-      topk_w[t * k + r] = ex / sum;
+#pragma unroll
+    for (int u = 0; u < NG; ++u) sort_desc(cand[u]);
+    float my_l[NG] = {}, l0[NG] = {};
+    for (int j = 0; j < k; ++j) {
+#pragma unroll
+      for (int u = 0; u < NG; ++u) {
+        const uint32_t hk = (uint32_t)(cand[u][0] >> 32), lo = (uint32_t)cand[u][0];
+        const uint32_t key = row_max_fused(hk);
+        bool win = hk == key;
+        if (__builtin_popcountll(__ballot(win)) > 4) {  // wave-uniform: each of the 4 rows has a holder
+          const uint32_t low = row_max_fused(win ? lo : 0u);
+          win = win && lo == low;
+        }
+        const float l = key_value(key);
+        if (j == 0) l0[u] = l;
+        if (r == j) my_l[u] = l;
+        if (win) row[u][j] = __int_as_float(min(max((int)(0xffffffffu - lo), 0), E - 1));
+        // pop: the winner takes each neighbour through a bitwise select (v_bfi_b32) on an opaque
+        // all-ones mask, so the shift is not rewritten as a candidate index chosen at run time
+        uint32_t m = 0u - (uint32_t)win;
+        asm volatile("" : "+v"(m));
+#pragma unroll
+        for (int q = 0; q < EQ; ++q) {
+          const uint64_t nx = q + 1 < EQ ? cand[u][q + 1] : 0ull;
+          const uint32_t h = ((uint32_t)(nx >> 32) & m) | ((uint32_t)(cand[u][q] >> 32) & ~m);
+          const uint32_t l32 = ((uint32_t)nx & m) | ((uint32_t)cand[u][q] & ~m);
+          cand[u][q] = ((uint64_t)h << 32) | l32;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NG; ++u) {
+      const float ex = r < k ? expf(my_l[u] - l0[u]) : 0.0f;
+      const float sum = row_sum(ex);
+      if (r < k && t[u] < T) {
+        topk_idx[t[u] * k + r] = __float_as_int(row[u][r]);
+        topk_w[t[u] * k + r] = ex / sum;
+      }
     }
   }
 }
