@@ -70,9 +70,12 @@ def test_route_bit_exact_with_subnormal_products_and_logits(E):
     assert np.abs(w.cpu().numpy() - r_w).max(initial=0) <= W_ABS
 
 
-def test_route_logits_in_with_ties_zero_signs_and_minus_inf():
-    rng = np.random.default_rng(11)
-    T, E, k = 300, 40, 6
+@pytest.mark.parametrize("E,k", [(40, 6), (256, 16), (130, 16), (128, 8)])
+def test_route_logits_in_with_ties_zero_signs_and_minus_inf(E, k):
+    """Both lane layouts of the k <= 16 top-k (8 candidates per lane for E <= 128, 16 above), with ties
+    inside a lane, across lanes of a row and in whole rows."""
+    rng = np.random.default_rng(11 + E)
+    T = 300
     l = rng.standard_normal((T, E)).astype(np.float32)
     l[:, 5] = l[:, 9]                      # exact ties -> lower id first
     l[::3, 1] = 0.0
@@ -80,11 +83,14 @@ def test_route_logits_in_with_ties_zero_signs_and_minus_inf():
     l[::3, 3:8] = 0.0
     l[::7, 0] = -np.inf                    # never picked while finite logits remain
     l[5] = 0.25                            # all equal -> experts 0..k-1
+    l[6, ::16] = 3.0                       # equal maxima in one lane (experts r + 16q share lane r)
+    l[7, :16] = 2.0                        # equal maxima across the 16 lanes of a row
+    l[8, 1::2] = -np.inf                   # half the experts at -inf
     idx, w = moe.route(k, logits=torch.from_numpy(l).to(DEV))
     r_idx, r_w = oracle.topk(l, k)
     assert np.array_equal(idx.cpu().numpy(), r_idx)
     assert np.abs(w.cpu().numpy() - r_w).max() <= W_ABS
-    assert (w[5].cpu().numpy() == np.float32(1.0 / 6)).all() or np.abs(w[5].cpu().numpy() - 1 / 6).max() < 1e-7
+    assert np.abs(w[5].cpu().numpy() - 1 / k).max() < 1e-7
 
 
 def test_route_zipf_logits_workload():
