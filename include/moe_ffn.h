@@ -234,6 +234,9 @@ int moe_grouped_gemm_wgrad_grid(const moe_bf16_t* A, const moe_bf16_t* D, const 
  *   is {workgroup, turn, expert, row0, row1, col0, col1}: rows [row0, row1)
  *   of the output (of dW[e] for WGRAD) and columns [col0, col1) that the
  *   workgroup computes on that turn, past group ends and widths excluded.
+ *   GEMM row blocks are 256 rows, except that a group of 257-512 rows runs
+ *   as two halves (its first ceil(n/2) rows, then the rest) whose tiles of
+ *   each column are adjacent in the list.
  *  *count receives the number of tiles (tiles beyond capacity are counted,
  *   not written).
  */

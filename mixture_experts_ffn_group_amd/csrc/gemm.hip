@@ -239,7 +239,7 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
   const bool loader = !SPLIT || wave_u < 4;
   const uint32_t lds_a = lds_addr(As0) + wave_u * LPW * 1024, lds_b = lds_addr(Bs0) + wave_u * LPW * 1024;
   const int nk = p.K / GBK;
-  int m0, m_end, n0;
+  int m0, m_end, m_cls, n0;  // tile rows [m0, m_end); m_cls sets the waves' multiply class
   const uint16_t *Ab, *Bexp;
   uint32_t a_off[LPW], b_off[LPW];
   // the copies of a k-slice have landed once at most those of the n k-slices
@@ -266,13 +266,18 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
     if (tl >= total) return false;
     // Tile order inside an expert (ragged_tile): with 4 or more row blocks the
     // row block varies fastest (measured: wo GEMM 1.01 -> 0.97 ms at 128
-    // experts of ~2048 rows, K = 768); with 1-3 row blocks the column tile
+    // experts of ~2048 rows, K = 768); with 1 or 3 row blocks the column tile
     // varies fastest (the other order cost 12 % at 256 experts of ~256 rows,
-    // K = 7168).
+    // K = 7168); with 2 row blocks the two equal halves of a column are adjacent.
     const RaggedTile rt = ragged_tile((int)tl, s_pref, p.E, ntn);
     const int e = rt.e, mt = rt.mt, nt = rt.nt;
-    m0 = __builtin_amdgcn_readfirstlane(s_lo[e] + mt * BM);
-    m_end = __builtin_amdgcn_readfirstlane(max(s_lo[e + 1], s_lo[e]));
+    {  // a group of 257-512 rows runs as two equal halves (tile_rows)
+      int r0, r1, rc;
+      tile_rows(s_lo[e], max(s_lo[e + 1], s_lo[e]), mt, &r0, &r1, &rc);
+      m0 = __builtin_amdgcn_readfirstlane(r0);
+      m_end = __builtin_amdgcn_readfirstlane(r1);
+      m_cls = __builtin_amdgcn_readfirstlane(rc);
+    }
     n0 = __builtin_amdgcn_readfirstlane(nt * tile_n);
     Bexp = uniform_ptr(p.B + (int64_t)__builtin_amdgcn_readfirstlane(e) * p.K * p.N);
     Ab = GATHER ? p.A : uniform_ptr(p.A + (int64_t)m0 * p.K);
@@ -378,8 +383,8 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
       wait_vm_all();  // this wave's loads of the first k-slices (and the last tile's stores) are done
       __syncthreads();
     }
-    // rows of this tile that hold outputs, from this wave's first row (wave-uniform)
-    const int wrows = m_end - (m0 + (wave_u >> 2) * 128);
+    // rows of this tile that count for the multiply, from this wave's first row (wave-uniform)
+    const int wrows = m_cls - (m0 + (wave_u >> 2) * 128);
     using NI4 = std::integral_constant<int, 4>;
     using NI2 = std::integral_constant<int, 2>;
     // k-slice kt on stage kt % NST. On entry its first 16-wide sub-slice is in

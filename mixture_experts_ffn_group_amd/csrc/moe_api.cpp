@@ -382,9 +382,10 @@ int moe_tile_schedule(int32_t kind, const int32_t* group_offsets, int32_t E, int
         const int64_t tl = moe::xcd_tile(it, w, grid);
         if (tl >= pref[E]) break;
         const moe::RaggedTile t = moe::ragged_tile((int)tl, pref, E, ntn);
-        const int m0 = lo[t.e] + t.mt * moe::kTileRows, m_end = std::max(lo[t.e + 1], lo[t.e]);
+        int r0, r1, rc;
+        moe::tile_rows(lo[t.e], std::max(lo[t.e + 1], lo[t.e]), t.mt, &r0, &r1, &rc);
         const int n0 = t.nt * tile_n;
-        emit(w, it, t.e, m0, std::min(m0 + moe::kTileRows, m_end), n0, std::min(n0 + tile_n, width));
+        emit(w, it, t.e, r0, r1, n0, std::min(n0 + tile_n, width));
       }
     }
   } else {

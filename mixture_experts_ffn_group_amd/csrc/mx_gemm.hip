@@ -163,7 +163,7 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
     const int t = p.row_slot[r] / p.slot_div;
     return t < 0 ? 0 : (t >= p.a_rows ? p.a_rows - 1 : t);
   };
-  int m0 = 0, m_end = 0, n0 = 0, e = 0;
+  int m0 = 0, m_end = 0, m_cls = 0, n0 = 0, e = 0;  // tile rows [m0, m_end); m_cls sets the multiply class
   const uint8_t* Bexp = p.B;
   const uint8_t* Bsexp = p.Bs;
   uint32_t a_off[LPW], b_off[LPW], s_off, s_off2 = 0;
@@ -173,8 +173,13 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
     const RaggedTile rt = ragged_tile((int)tl, s_pref, p.E, ntn);
     e = __builtin_amdgcn_readfirstlane(rt.e);
     const int mt = rt.mt, nt = rt.nt;
-    m0 = __builtin_amdgcn_readfirstlane(s_lo[e] + mt * 256);
-    m_end = __builtin_amdgcn_readfirstlane(max(s_lo[e + 1], s_lo[e]));
+    {  // a group of 257-512 rows runs as two equal halves (tile_rows)
+      int r0, r1, rc;
+      tile_rows(s_lo[e], max(s_lo[e + 1], s_lo[e]), mt, &r0, &r1, &rc);
+      m0 = __builtin_amdgcn_readfirstlane(r0);
+      m_end = __builtin_amdgcn_readfirstlane(r1);
+      m_cls = __builtin_amdgcn_readfirstlane(rc);
+    }
     n0 = __builtin_amdgcn_readfirstlane(nt * tile_n);
     Bexp = mx_uniform(p.B + (int64_t)e * p.N * p.K);
     Bsexp = mx_uniform(p.Bs + (int64_t)e * nk * p.N * 4);
@@ -315,7 +320,7 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
       }
     };
     // rows of this tile that hold outputs, from this wave's first row (wave-uniform)
-    const int wrows = m_end - (m0 + (wave_u >> 2) * 128);
+    const int wrows = m_cls - (m0 + (wave_u >> 2) * 128);
     if (wrows > 64) {
       kloop(std::integral_constant<int, 4>{});
     } else if (wrows > 0) {

@@ -47,7 +47,12 @@ def _check_gemm(kind, off, M, N, grid):
     for (_, _, e, r0, r1, c0, c1) in tiles:
         assert sizes[e] > 0, "a tile for an empty group"
         assert lo[e] <= r0 < r1 <= lo[e + 1], (e, r0, r1, lo[e], lo[e + 1])
-        assert r1 - r0 <= 256 and (r0 - lo[e]) % 256 == 0
+        n = sizes[e]
+        if 256 < n <= 512:  # two equal halves: the first ceil(n/2) rows, then the rest
+            h = (n + 1) // 2
+            assert (r0, r1) in ((lo[e], lo[e] + h), (lo[e] + h, lo[e] + n)), (e, r0, r1, lo[e], n)
+        else:
+            assert r1 - r0 <= 256 and (r0 - lo[e]) % 256 == 0
         assert c0 % tile_n == 0 and c1 == min(c0 + tile_n, width)
         cover[r0:r1, c0 // tile_n] += 1
     in_group = np.zeros(M, bool)
@@ -88,12 +93,40 @@ def test_gemm_tiles_zipf_like_128_experts_many_turns():
     _check_gemm("gemm", off, int(off[-1]), 2048, 256)
 
 
-def test_gemm_partial_last_row_block():
-    # a group of 257 rows: one full 256-row block and one of a single row, for every column tile
+def test_gemm_two_block_group_runs_as_equal_halves():
+    # a group of 257 rows runs as halves of 129 and 128 rows for every column tile, and a group of
+    # 513 rows as three 256-row blocks (the last of one row)
     off = _offsets([257])
     t = _check_gemm("gemm", off, 257, 512, 8)
-    heights = sorted((t[:, 4] - t[:, 3]).tolist())
-    assert heights == [1, 1, 256, 256]
+    assert sorted((t[:, 4] - t[:, 3]).tolist()) == [128, 128, 129, 129]
+    off = _offsets([513])
+    t = _check_gemm("gemm", off, 513, 512, 8)
+    assert sorted((t[:, 4] - t[:, 3]).tolist()) == [1, 1, 256, 256, 256, 256]
+
+
+@pytest.mark.parametrize("kind,N", [("swiglu", 2 * 2048), ("gemm", 7168)])
+def test_gemm_two_block_halves_run_side_by_side(kind, N):
+    """256 groups of 256 +- 16 rows (the DeepSeek-V3 shape): both halves of a column of a 257-272-row
+    group run on the same turn, on workgroups w and w + 8 (the same XCD, neighbouring slots). Every
+    expert then has an even tile count, so workgroups 16i + x and 16i + 8 + x get tiles of equal
+    height (+-1 row) on every turn, and stay in step."""
+    rng = np.random.default_rng(3)
+    sizes = 256 + rng.integers(-16, 17, 256)
+    off = _offsets(sizes)
+    t = _check_gemm(kind, off, int(off[-1]), N, 256)
+    by = {}
+    for (w, it, e, r0, r1, c0, c1) in t:
+        by[(int(w), int(it))] = (int(e), int(r0), int(r1), int(c0))
+        if 256 < sizes[e]:
+            by.setdefault(("pair", int(e), int(c0)), []).append((int(w), int(it)))
+    pairs = [v for k, v in by.items() if k[0] == "pair"]
+    assert len(pairs) == int((sizes > 256).sum()) * (-(-(N // 2 if kind == "swiglu" else N) // (128 if kind == "swiglu" else 256)))
+    for (wa, ia), (wb, ib) in (sorted(v) for v in pairs):
+        assert ia == ib and wb == wa + 8 and (wa // 8) % 2 == 0, (wa, ia, wb, ib)
+    for (w, it), (e, r0, r1, c0) in [(k, v) for k, v in by.items() if k[0] != "pair"]:
+        if (w // 8) % 2 == 0 and (w + 8, it) in by:
+            _, q0, q1, _ = by[(w + 8, it)]
+            assert abs((r1 - r0) - (q1 - q0)) <= 1, (w, it, r1 - r0, q1 - q0)
 
 
 @pytest.mark.parametrize("E,P,Q,grid", [(8, 512, 1536, 8), (5, 296, 64, 16), (256, 7168, 4096, 256),
