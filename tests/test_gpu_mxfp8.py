@@ -118,7 +118,7 @@ def test_grouped_gemm_mx_matches_oracle(M, K, N, E, empty, epi):
 
 # Groups whose last 256-row tile ends at every 32-row block boundary of either half of the tile, and just past
 # them, plus an empty group: every k-loop form of the tile (four blocks, two blocks, none).
-MX_PARTIAL_SIZES = [1, 32, 33, 64, 65, 128, 129, 160, 224, 255, 256, 257, 300, 543, 0]
+MX_PARTIAL_SIZES = [1, 32, 33, 64, 65, 128, 129, 160, 224, 255, 256, 257, 300, 384, 385, 448, 449, 512, 543, 0]
 
 
 @pytest.mark.parametrize("epi", ["none", "swiglu"])
