@@ -25,10 +25,13 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// Two floats -> two bf16 (round to nearest even, hardware convert), lo in bits 0..15.
+// Two floats -> two bf16 (round to nearest even), lo in bits 0..15: one v_cvt_pk_bf16_f32 with
+// both sources. Converting the two values separately gives one convert each plus a shift and an
+// OR to merge them: four instructions per pair in every GEMM epilogue.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __hip_bfloat162 v = __float22bfloat162_rn(make_float2(lo, hi));
-  return *reinterpret_cast<uint32_t*>(&v);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // silu(g) = g * sigmoid(g), sigmoid(g) = 1 / (1 + e^-g), with the hardware reciprocal (about 1 ulp of

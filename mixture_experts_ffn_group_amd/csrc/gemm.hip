@@ -282,15 +282,28 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
     Bexp = uniform_ptr(p.B + (int64_t)__builtin_amdgcn_readfirstlane(e) * p.K * p.N);
     Ab = GATHER ? p.A : uniform_ptr(p.A + (int64_t)m0 * p.K);
     if (!loader) return true;
+    if (GATHER) {
+      // all LPW slot loads first, into a_off itself (the current tile's offsets are dead by now and
+      // few other registers are free with the accumulators live), then their conversion: loaded and
+      // used one at a time they cost LPW round trips
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-      const int row = (wave_u * LPW + j) * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ ((row >> 2) & 3);
-      const int r = min(m0 + row, m_end - 1);
-      if (GATHER) {
-        const int s = min(max(p.row_slot[r], 0), p.n_slots - 1);
+      for (int j = 0; j < LPW; ++j) {
+        const int row = (wave_u * LPW + j) * 16 + (lane >> 2);
+        a_off[j] = (uint32_t)p.row_slot[min(m0 + row, m_end - 1)];
+      }
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) {
+        const int row = (wave_u * LPW + j) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ ((row >> 2) & 3);
+        const int s = min(max((int)a_off[j], 0), p.n_slots - 1);
         a_off[j] = (uint32_t)((s / p.slot_div) * p.K + c * 8) * 2u;
-      } else {
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) {
+        const int row = (wave_u * LPW + j) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ ((row >> 2) & 3);
+        const int r = min(m0 + row, m_end - 1);
         a_off[j] = (uint32_t)((r - m0) * p.K + c * 8) * 2u;
       }
     }
@@ -437,12 +450,26 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
     // optional per-row fp32 scale (the top-k weight of the row's slot), applied as values are read;
     // fetched before the prefetch so that its wait does not cover the next tile's loads
     float sc4[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-    if (GATHER && p.slot_scale) {
+    if (GATHER && p.slot_scale) {  // the four indices, then the four scales: two round trips
+      int si[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = min(cm0 + wm * 128 + i * 32 + (lane & 31), cm_end - 1);
-        sc4[i] = p.slot_scale[p.row_slot ? min(max(p.row_slot[m], 0), p.n_slots - 1) : m];
+      for (int i = 0; i < 4; ++i) si[i] = min(cm0 + wm * 128 + i * 32 + (lane & 31), cm_end - 1);
+      if (p.row_slot) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) si[i] = p.row_slot[si[i]];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) si[i] = min(max(si[i], 0), p.n_slots - 1);
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc4[i] = p.slot_scale[si[i]];
+    }
+    // The scales are consumed here, before the copies go out. The copies are inline asm, which the
+    // compiler does not count, so a first use in the epilogue would carry a vmcnt wait sized for the
+    // compiler's own loads, covering the copies too; and since the loads are conditional, that wait
+    // (and any reuse of their registers, even in the next k-loop) was kept on both paths.
+    if (GATHER) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(sc4[i]));
     }
     const bool more = decode(it + 1);
     // The last stage carries the copying waves' output to the storing waves
