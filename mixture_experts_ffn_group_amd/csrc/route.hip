@@ -282,6 +282,20 @@ __device__ __forceinline__ void route_topk(const float* s_l, int64_t T, int64_t 
   }
 }
 
+// Bias of the experts a lane's accumulators hold: MODE 0, expert 32*wave + lane%32 for both
+// blocks; MODE 1, experts 64*wave + 32*blk + lane%32. Loaded together (one round trip); a load per
+// accumulator at the logit store was waited one at a time.
+template <int MODE>
+__device__ __forceinline__ void lane_bias(const float* bias, int E, int wave, int lane, float (&bv)[2]) {
+  bv[0] = bv[1] = 0.0f;
+  if (!bias) return;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int e = MODE == 0 ? 32 * wave + (lane & 31) : 64 * wave + 32 * b + (lane & 31);
+    if (e < E) bv[b] = bias[e];
+  }
+}
+
 // Output layout of v_mfma_f32_32x32x1_2b_f32 (measured): lane l, register r ->
 // block r/16, row ((r%16)/4)*8 + (l/32)*4 + r%4 of that block, column l%32;
 // lane l feeds row l%32 (A) and column l%32 (B) of block l/32.
@@ -382,13 +396,15 @@ __global__ __launch_bounds__(256) void route_kernel(int64_t T, int emb, int E, i
       b ^= 1;
     }
     if (busy) {
+      float bv[2];
+      lane_bias<MODE>(bias, E, wave, lane, bv);
 #pragma unroll
       for (int r = 0; r < 32; ++r) {
         const int blk = r >> 4, rr = r & 15;
         const int row = (rr >> 2) * 8 + (lane >> 5) * 4 + (rr & 3), col = lane & 31;
         const int tok = MODE == 0 ? 32 * blk + row : row;
         const int e = MODE == 0 ? 32 * wave + col : 64 * wave + 32 * blk + col;
-        if (e < E) s_l[tok * EP + e] = bias ? acc[r] + bias[e] : acc[r];
+        if (e < E) s_l[tok * EP + e] = bias ? acc[r] + bv[blk] : acc[r];
       }
     }
   }
@@ -459,6 +475,10 @@ __global__ __launch_bounds__(256) void route_ring_kernel(int64_t T, int emb, int
   const int tok_a = MODE == 0 ? lane : (lane & 31);  // A operand: this lane's token
   const int exp_b = MODE == 0 ? 32 * wave + (lane & 31) : 64 * wave + lane;  // B operand: its expert
   const bool busy = (MODE == 0 ? 32 : 64) * wave < E;  // wave-uniform
+  // bias of this lane's experts, loaded before the copies: the latency hides under the MFMA loop,
+  // and the loads being older than every copy, the copy waits below still count correctly
+  float bv[2] = {0.0f, 0.0f};
+  if (busy) lane_bias<MODE>(bias, E, wave, lane, bv);
   f32x32_t acc;
 #pragma unroll
   for (int r = 0; r < 32; ++r) acc[r] = 0.0f;
@@ -526,7 +546,7 @@ __global__ __launch_bounds__(256) void route_ring_kernel(int64_t T, int emb, int
       const int row = (rr >> 2) * 8 + (lane >> 5) * 4 + (rr & 3), col = lane & 31;
       const int tok = MODE == 0 ? 32 * blk + row : row;
       const int e = MODE == 0 ? 32 * wave + col : 64 * wave + 32 * blk + col;
-      if (e < E) s_l[tok * EP + e] = bias ? acc[r] + bias[e] : acc[r];
+      if (e < E) s_l[tok * EP + e] = bias ? acc[r] + bv[blk] : acc[r];
     }
   }
   __syncthreads();
