@@ -157,10 +157,10 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
   const uint32_t lds0 = mx_lds_addr(smem);
   const int nk = p.K / 64;
   const int nslice_rows = p.a_rows;  // rows of A's scale slices
-  // A row of output row r: the token row through the slot index, or r itself
-  auto a_row = [&](int r) -> int {
-    if (!GATHER) return r;
-    const int t = p.row_slot[r] / p.slot_div;
+  // With the gather, output row r reads token row row_slot[r] / slot_div (clamped); this is that
+  // row from an already loaded slot.
+  auto slot_row = [&](int slot) -> int {
+    const int t = slot / p.slot_div;
     return t < 0 ? 0 : (t >= p.a_rows ? p.a_rows - 1 : t);
   };
   int m0 = 0, m_end = 0, m_cls = 0, n0 = 0, e = 0;  // tile rows [m0, m_end); m_cls sets the multiply class
@@ -184,12 +184,23 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
     Bexp = mx_uniform(p.B + (int64_t)e * p.N * p.K);
     Bsexp = mx_uniform(p.Bs + (int64_t)e * nk * p.N * 4);
     if (!loader) return true;
+    // With the gather, every slot this lane needs is loaded first, into the offset registers
+    // themselves (few others are free while the accumulators are live), and converted after:
+    // loaded and used one at a time, each cost a round trip.
+    const bool a_scale_row = SPLIT || wave_u < 4;  // s_off is an A scale row
+    if (GATHER) {
+#pragma unroll
+      for (int j = 0; j < LPW; ++j)
+        a_off[j] = (uint32_t)p.row_slot[min(m0 + (wave_u * LPW + j) * 16 + (lane >> 2), m_end - 1)];
+      if (a_scale_row)
+        s_off = (uint32_t)p.row_slot[min(m0 + (SPLIT ? wave_u : (wave_u & 3)) * 64 + lane, m_end - 1)];
+    }
     // tile rows: block b = LPW*wave + j holds rows 16b .. 16b+15; lane L -> row 16b + L/4, physical chunk L%4
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const int row = (wave_u * LPW + j) * 16 + (lane >> 2);
       const int c = (lane & 3) ^ ((row >> 2) & 3);
-      const int r = a_row(min(m0 + row, m_end - 1));
+      const int r = GATHER ? slot_row((int)a_off[j]) : min(m0 + row, m_end - 1);
       a_off[j] = (uint32_t)r * (uint32_t)p.K + (uint32_t)c * 16u;
       int n;
       if (EPI == MXE_SWIGLU) {
@@ -204,12 +215,12 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
     // roles split, waves 0-3 copy both: s_off for A, s_off2 for B)
     if (SPLIT) {
       const int row = wave_u * 64 + lane;
-      s_off = (uint32_t)a_row(min(m0 + row, m_end - 1)) * 4u;
+      s_off = (uint32_t)(GATHER ? slot_row((int)s_off) : min(m0 + row, m_end - 1)) * 4u;
       s_off2 = (uint32_t)(n0 + row < p.N ? n0 + row : p.N - 1) * 4u;
     } else {
       const int row = (wave_u & 3) * 64 + lane;
       if (wave_u < 4) {
-        s_off = (uint32_t)a_row(min(m0 + row, m_end - 1)) * 4u;
+        s_off = (uint32_t)(GATHER ? slot_row((int)s_off) : min(m0 + row, m_end - 1)) * 4u;
       } else {
         int n;
         if (EPI == MXE_SWIGLU) {
