@@ -248,13 +248,19 @@ def measure(wl, dev, steps, warmup, bwd=False, remat=False, mx=False, flush_comb
     for _ in range(warmup):
         run_step()
     torch.cuda.synchronize()
+    # The step time: K steps of the launches alone, bracketed by synchronizations.
+    t0 = time.perf_counter()
+    for s in range(steps):
+        run_step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # The stage breakdown: K more steps with an event on the stream between the launches (the event
+    # writes sit between the kernels, so this pass is not the one the step time is taken from).
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for s in range(steps):
         run_step(evs[s])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     stage_ms = {name: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(steps)]))
                 for i, (name, _) in enumerate(calls)}
 
