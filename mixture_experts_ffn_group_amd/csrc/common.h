@@ -41,6 +41,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float silu_f(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 __device__ __forceinline__ float sigmoid_f(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
+// The lanes of one wave hand values to each other through LDS with no barrier between the
+// write and the read. The hardware runs a wave's LDS instructions in order, so the read sees the
+// other lanes' writes; the compiler, reasoning lane by lane, does not know that. Where a lane
+// wrote nothing to an address since it last read it (a staging block written by half the lanes,
+// then read back by all), it may reuse the value it read before: it did so once the reads of such
+// a block were issued together, and half the stored rows were stale. This empty asm with a memory
+// clobber stands between each write phase and the read phase that follows, and between that read
+// phase and the next write phase; it emits no instruction.
+__device__ __forceinline__ void wave_lds_fence() { asm volatile("" ::: "memory"); }
+
 // 16-byte global load / store.
 __device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }

@@ -507,12 +507,15 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
     // Read the staged block back, four lanes per row, and store rows m0r + 0..31,
     // 16 bytes at column byte offset 16 * (lane % 4) from row_ptr(m).
     auto drain = [&](int m0r, auto row_ptr, int valid_chunks) {
+      wave_lds_fence();
+      u32x4_t v[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) v[k] = *reinterpret_cast<const u32x4_t*>(stg + stg64(16 * k + (lane >> 2), lane & 3));
+      wave_lds_fence();
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        const int rr = 16 * k + (lane >> 2), c = lane & 3;
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + stg64(rr, c));
-        const int m = m0r + rr;
-        if (m < cm_end && c < valid_chunks) sto(reinterpret_cast<uint16_t*>(row_ptr(m)) + c * 8, v);
+        const int m = m0r + 16 * k + (lane >> 2), c = lane & 3;
+        if (m < cm_end && c < valid_chunks) sto(reinterpret_cast<uint16_t*>(row_ptr(m)) + c * 8, v[k]);
       }
     };
     // A copying wave's output crosses as [rows][bytes] in its region xr, 16-byte
@@ -560,12 +563,15 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
                         pack4(sc * acc[i][f][4 * q], sc * acc[i][f][4 * q + 1], sc * acc[i][f][4 * q + 2],
                               sc * acc[i][f][4 * q + 3]);
               }
+              wave_lds_fence();
+              u32x4_t v[2];
+#pragma unroll
+              for (int kk = 0; kk < 2; ++kk) v[kk] = *reinterpret_cast<const u32x4_t*>(stg + stg128(8 * kk + (lane >> 3), lane & 7));
+              wave_lds_fence();
 #pragma unroll
               for (int kk = 0; kk < 2; ++kk) {
-                const int rr = 8 * kk + (lane >> 3), c = lane & 7;
-                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + stg128(rr, c));
-                const int m = m0r + 16 * h + rr;
-                if (m < cm_end && c < valid) sto(p.C + (int64_t)m * p.N + n0w + c * 8, v);
+                const int m = m0r + 16 * h + 8 * kk + (lane >> 3), c = lane & 7;
+                if (m < cm_end && c < valid) sto(p.C + (int64_t)m * p.N + n0w + c * 8, v[kk]);
               }
             }
           }
@@ -575,12 +581,15 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
           const int m0r = cm0 + wm_s * 128 + ph * 64;
           const int n0w = cn0 + wn_s * 64;
           const int valid = min(8, (p.N - n0w) >> 3);
+          // all eight reads go out before the first store: a read waited just
+          // before its own masked store would serialize the LDS latencies
+          u32x4_t v[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const u32x4_t*>(xr + xoff128(8 * j + (lane >> 3), lane & 7));
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            const int rr = 8 * j + (lane >> 3), c = lane & 7;
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xr + xoff128(rr, c));
-            const int m = m0r + rr;
-            if (m < cm_end && c < valid) sto(p.C + (int64_t)m * p.N + n0w + c * 8, v);
+            const int m = m0r + 8 * j + (lane >> 3), c = lane & 7;
+            if (m < cm_end && c < valid) sto(p.C + (int64_t)m * p.N + n0w + c * 8, v[j]);
           }
         }
         kbarrier();  // read back: the region may be written again
@@ -625,12 +634,13 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
         const int m0r = cm0 + wm_s * 128;
         const int c0 = cn0 + wn_s * 32;
         const int valid = min(4, (mlp - c0) >> 3);
+        u32x4_t v[8];  // reads first, then the masked stores
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const u32x4_t*>(xr + xoff64(16 * j + (lane >> 2), lane & 3));
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int rr = 16 * j + (lane >> 2), c = lane & 3;
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xr + xoff64(rr, c));
-          const int m = m0r + rr;
-          if (m < cm_end && c < valid) sto(p.C + (int64_t)m * mlp + c0 + c * 8, v);
+          const int m = m0r + 16 * j + (lane >> 2), c = lane & 3;
+          if (m < cm_end && c < valid) sto(p.C + (int64_t)m * mlp + c0 + c * 8, v[j]);
         }
       }
       kbarrier();  // read back: the stage may be loaded
@@ -925,13 +935,16 @@ __global__ __launch_bounds__(GTHR, 1) void wgrad_kernel(WgradP p) {
                   *reinterpret_cast<u32x2_t*>(stg + stg128(r - 16 * h, f * 4 + q) + hh * 8) =
                       pack4(acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]);
             }
+            wave_lds_fence();
+            u32x4_t v[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) v[kk] = *reinterpret_cast<const u32x4_t*>(stg + stg128(8 * kk + (lane >> 3), lane & 7));
+            wave_lds_fence();
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-              const int rr = 8 * kk + (lane >> 3), c = lane & 7;
-              const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + stg128(rr, c));
-              const int pr = pr0 + 16 * h + rr;
+              const int pr = pr0 + 16 * h + 8 * kk + (lane >> 3), c = lane & 7;
               if (pr < p.P && c < valid)
-                __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(Ce + (int64_t)pr * p.Q + qw + c * 8));
+                __builtin_nontemporal_store(v[kk], reinterpret_cast<u32x4_t*>(Ce + (int64_t)pr * p.Q + qw + c * 8));
             }
           }
         }
@@ -941,13 +954,14 @@ __global__ __launch_bounds__(GTHR, 1) void wgrad_kernel(WgradP p) {
         const int pr0 = cp0 + wm_s * 128 + ph * 64;
         const int qw = cq0 + wn_s * 64;
         const int valid = min(8, (p.Q - qw) >> 3);
+        u32x4_t v[8];  // reads first, then the masked stores
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const u32x4_t*>(xr + stg128(8 * j + (lane >> 3), lane & 7));
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int rr = 8 * j + (lane >> 3), c = lane & 7;
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xr + stg128(rr, c));
-          const int pr = pr0 + rr;
+          const int pr = pr0 + 8 * j + (lane >> 3), c = lane & 7;
           if (pr < p.P && c < valid)
-            __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(Ce + (int64_t)pr * p.Q + qw + c * 8));
+            __builtin_nontemporal_store(v[j], reinterpret_cast<u32x4_t*>(Ce + (int64_t)pr * p.Q + qw + c * 8));
         }
       }
       kbarrier();  // read back: the region may be written again

@@ -390,12 +390,15 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
                     *reinterpret_cast<u32x2_t*>(stg + stg128(r - 16 * hf, f * 4 + q) + hh * 8) =
                         mx_pack4(acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]);
               }
+              wave_lds_fence();
+              u32x4_t v[2];
+#pragma unroll
+              for (int kk = 0; kk < 2; ++kk) v[kk] = *reinterpret_cast<const u32x4_t*>(stg + stg128(8 * kk + (lane >> 3), lane & 7));
+              wave_lds_fence();
 #pragma unroll
               for (int kk = 0; kk < 2; ++kk) {
-                const int rr = 8 * kk + (lane >> 3), c = lane & 7;
-                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + stg128(rr, c));
-                const int m = m0r + 16 * hf + rr;
-                if (m < cm_end && c < valid) sto(p.C + (int64_t)m * p.N + n0w + c * 8, v);
+                const int m = m0r + 16 * hf + 8 * kk + (lane >> 3), c = lane & 7;
+                if (m < cm_end && c < valid) sto(p.C + (int64_t)m * p.N + n0w + c * 8, v[kk]);
               }
             }
           }
@@ -405,12 +408,13 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
           const int m0r = cm0 + wm_s * 128 + ph * 64;
           const int n0w = cn0 + wn_s * 64;
           const int valid = min(8, (p.N - n0w) >> 3);
+          u32x4_t v[8];  // reads first, then the masked stores
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const u32x4_t*>(xr + stg128(8 * j + (lane >> 3), lane & 7));
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            const int rr = 8 * j + (lane >> 3), c = lane & 7;
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xr + stg128(rr, c));
-            const int m = m0r + rr;
-            if (m < cm_end && c < valid) sto(p.C + (int64_t)m * p.N + n0w + c * 8, v);
+            const int m = m0r + 8 * j + (lane >> 3), c = lane & 7;
+            if (m < cm_end && c < valid) sto(p.C + (int64_t)m * p.N + n0w + c * 8, v[j]);
           }
         }
         kbarrier();  // read back: the region may be written again
@@ -433,12 +437,15 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x2_t*>(stg + stg64(r, q) + hh * 8) = pk[q];
           const int valid = min(4, (mlp - c0) >> 3);
+          wave_lds_fence();
+          u32x4_t v[2];
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) v[k2] = *reinterpret_cast<const u32x4_t*>(stg + stg64(16 * k2 + (lane >> 2), lane & 3));
+          wave_lds_fence();
 #pragma unroll
           for (int k2 = 0; k2 < 2; ++k2) {
-            const int rr = 16 * k2 + (lane >> 2), c = lane & 3;
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + stg64(rr, c));
-            const int m = m0r + rr;
-            if (m < cm_end && c < valid) st16(p.C + (int64_t)m * mlp + c0 + c * 8, v);
+            const int m = m0r + 16 * k2 + (lane >> 2), c = lane & 3;
+            if (m < cm_end && c < valid) st16(p.C + (int64_t)m * mlp + c0 + c * 8, v[k2]);
           }
         }
         if (p.Cq && c0 < mlp) {
@@ -464,9 +471,11 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
             for (int u = 0; u < 4; ++u) word |= mx_e4m3_code(ldexpf(v[4 * q + u], 127 - sc)) << (8 * u);
             *reinterpret_cast<uint32_t*>(stg + 1024 + r * 32 + 8 * q + 4 * hh) = word;  // [32 rows][32 codes]
           }
+          wave_lds_fence();
           {
             const int rr = lane >> 1, c = lane & 1;
             const u32x4_t w = *reinterpret_cast<const u32x4_t*>(stg + 1024 + rr * 32 + c * 16);
+            wave_lds_fence();
             const int m = m0r + rr;
             if (m < cm_end) st16(p.Cq + (int64_t)m * mlp + c0 + c * 16, w);
           }
