@@ -403,8 +403,8 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
     // k-slice kt on stage kt % NST. On entry its first 16-wide sub-slice is in
     // fragment set 0. The barrier sits before the second sub-slice: every wave
     // then holds all of stage kt % NST in registers, so the loads of k-slice
-    // kt + NST go into it at once, and k-slice kt+1 (issued NST-1 k-slices
-    // ago) must have landed. The next stage's first fragments are read under
+    // kt + NST can go into it during the second sub-slice, and k-slice kt+1
+    // (issued NST-1 k-slices ago) must have landed. The next stage's first fragments are read under
     // the second sub-slice's MFMAs (also on the last k-slice, where they go
     // unused: it keeps the body one basic block).
     // wait for k-slice kt+1 (the loads issued after it: k-slices kt+2 and kt+3, where they exist), then barrier
@@ -419,6 +419,48 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
         __syncthreads();
       }
     };
+    // Second sub-slice of k-slice kt: per row block i, its two MFMAs, then the read of
+    // block i of the next stage's first fragments (and of one B fragment every other
+    // block), then one A copy of k-slice kt + NST; the B copies follow the last MFMA.
+    // Issued as one burst after the barrier (the first form), a copying wave's eight
+    // copies held back its MFMAs until the last of them was accepted. Measured,
+    // alternating on one box (32768-token workload, DeepSeek-V3 shape in brackets):
+    // GEMM1 1.463 -> 1.437 ms (4.66 -> 4.57), GEMM2 0.964 -> 0.954 (2.465 -> 2.43).
+    // Spreading the B copies over the MFMAs as well, one per MFMA or across both
+    // sub-slices, was slower than the burst form.
+    auto second_half = [&](auto NIc, int kt) {
+      constexpr int NI = decltype(NIc)::value;
+      const int nst = (kt + 1) & (NST - 1);
+      const uint8_t* As = As0 + nst * kOpStage;
+      const uint8_t* Bs = Bs0 + nst * kOpStage;
+      const int kn = kt + NST;
+      const bool cp = loader && kn < nk;
+      const uint16_t* Ak = Ab + kn * GBK;
+      const uint16_t* Bk = OP == OP_NT ? Bexp + kn * GBK : Bexp + (int64_t)(kn * GBK) * p.N;
+      const uint32_t cst = (uint32_t)(kn & (NST - 1)) * kOpStage;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) acc[i][f] = mfma(bf[1][f], af[1][i], acc[i][f]);
+        af[0][i] = frag_k4(As, lane, 0, wm * 128 + i * 32);
+        if (i & 1) {
+          const int f = i >> 1;
+          if (OP == OP_NT) bf[0][f] = frag_k4(Bs, lane, 0, frag_col8<EPI>(wn, f));
+          else bf[0][f] = frag_tr(Bs, lane, 0, frag_col8<EPI>(wn, f));
+        }
+        if (cp && i < LPW) g2lds16(Ak, a_off[i], lds_a + cst + i * 1024);
+      }
+      if (NI == 2) {
+        if (OP == OP_NT) bf[0][1] = frag_k4(Bs, lane, 0, frag_col8<EPI>(wn, 1));
+        else bf[0][1] = frag_tr(Bs, lane, 0, frag_col8<EPI>(wn, 1));
+      }
+      if (cp) {
+#pragma unroll
+        for (int j = NI; j < LPW; ++j) g2lds16(Ak, a_off[j], lds_a + cst + j * 1024);
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) g2lds16(Bk, b_off[j], lds_b + cst + j * 1024);
+      }
+    };
     auto kloop = [&](auto NIc) {
       read_frags(NIc, 0, 0, 0);
       for (int kt = 0; kt < nk; ++kt) {
@@ -427,10 +469,7 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
         mfmas(NIc, 0);
         interleave(NIc);
         kwait(kt);
-        if (kt + NST < nk) issue_loads(kt + NST);
-        read_frags(NIc, (kt + 1) & (NST - 1), 0, 0);
-        mfmas(NIc, 1);
-        interleave(NIc);
+        second_half(NIc, kt);
       }
     };
     if (wrows > 64) {
@@ -882,10 +921,31 @@ __global__ __launch_bounds__(GTHR, 1) void wgrad_kernel(WgradP p) {
       interleave();
       if (loader) wait_loads_after(kt + 3 < nk ? 2 : (kt + 2 < nk ? 1 : 0));
       kbarrier();
-      if (kt + NST < nk) issue_loads(kt + NST);
-      read_frags((kt + 1) & (NST - 1), 0, 0);
-      mfmas(1);
-      interleave();
+      {
+        // second sub-slice, as in gemm_kernel: per row block i its two MFMAs, the next
+        // stage's fragment reads, then one A copy of k-slice kt + NST; the D copies last
+        const int nst = (kt + 1) & (NST - 1);
+        const uint8_t* As = As0 + nst * kOpStage;
+        const uint8_t* Ds = Ds0 + nst * kOpStage;
+        const int kn = kt + NST;
+        const bool cp = loader && kn < nk;
+        const int r0 = lo + kn * GBK, rows = min(GBK, n - kn * GBK);
+        const uint32_t cst = (uint32_t)(kn & (NST - 1)) * kOpStage;
+        const i32x4_t ra = buffer_rsrc(p.A + (int64_t)r0 * p.P, (uint32_t)(rows * p.P * 2));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int f = 0; f < 2; ++f) acc[i][f] = mfma(df[1][f], af[1][i], acc[i][f]);
+          af[0][i] = frag_tr(As, lane, 0, wm * 128 + i * 32);
+          if (i & 1) df[0][i >> 1] = frag_tr(Ds, lane, 0, wn * 64 + (i >> 1) * 32);
+          if (cp) b2lds16(ra, a_off[i & 1] + (uint32_t)((i >> 1) * 8 * p.P), lds_a + cst + i * 1024);
+        }
+        if (cp) {
+          const i32x4_t rd = buffer_rsrc(p.D + (int64_t)r0 * p.Q, (uint32_t)(rows * p.Q * 2));
+#pragma unroll
+          for (int j = 0; j < 4; ++j) b2lds16(rd, d_off[j & 1] + (uint32_t)((j >> 1) * 8 * p.Q), lds_d + cst + j * 1024);
+        }
+      }
     }
 
     const int ce = e, cp0 = p0, cq0 = q0;
