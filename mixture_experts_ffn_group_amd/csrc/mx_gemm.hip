@@ -374,32 +374,31 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
                     mx_pack4(acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]);
           }
         } else if (ph == 0) {
-          // the storing wave's own block, 16 rows x 128 B at a time through its staging area
+          // the storing wave's own block, 32 rows x 128 B at a time: rows 0-15 in its
+          // staging area, rows 16-31 in that of its copying wave (unused here)
+          uint8_t* const wb = r < 16 ? stg : s_stage[wave - 4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int m0r = cm0 + wm * 128 + i * 32;
             const int n0w = cn0 + wn * 64;
             const int valid = min(8, (p.N - n0w) >> 3);
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-              if ((r >> 4) == hf) {
+            for (int f = 0; f < 2; ++f)
 #pragma unroll
-                for (int f = 0; f < 2; ++f)
+              for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<u32x2_t*>(wb + stg128(r & 15, f * 4 + q) + hh * 8) =
+                    mx_pack4(acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]);
+            wave_lds_fence();
+            u32x4_t v[4];
 #pragma unroll
-                  for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<u32x2_t*>(stg + stg128(r - 16 * hf, f * 4 + q) + hh * 8) =
-                        mx_pack4(acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]);
-              }
-              wave_lds_fence();
-              u32x4_t v[2];
+            for (int kk = 0; kk < 4; ++kk)
+              v[kk] = *reinterpret_cast<const u32x4_t*>((kk < 2 ? stg : s_stage[wave - 4]) +
+                                                        stg128(8 * (kk & 1) + (lane >> 3), lane & 7));
+            wave_lds_fence();
 #pragma unroll
-              for (int kk = 0; kk < 2; ++kk) v[kk] = *reinterpret_cast<const u32x4_t*>(stg + stg128(8 * kk + (lane >> 3), lane & 7));
-              wave_lds_fence();
-#pragma unroll
-              for (int kk = 0; kk < 2; ++kk) {
-                const int m = m0r + 16 * hf + 8 * kk + (lane >> 3), c = lane & 7;
-                if (m < cm_end && c < valid) sto(p.C + (int64_t)m * p.N + n0w + c * 8, v[kk]);
-              }
+            for (int kk = 0; kk < 4; ++kk) {
+              const int m = m0r + 8 * kk + (lane >> 3), c = lane & 7;
+              if (m < cm_end && c < valid) sto(p.C + (int64_t)m * p.N + n0w + c * 8, v[kk]);
             }
           }
         }
