@@ -219,6 +219,10 @@ __device__ __forceinline__ void route_topk16(float* s_l, int64_t T, int64_t t0, 
         }
       }
     }
+    // lane r reads back pick r, which another lane of the wave may have written (the wave's
+    // LDS accesses run in order; the fence keeps the compiler from reusing lane r's earlier
+    // read of that address, its logit)
+    wave_lds_fence();
 #pragma unroll
     for (int u = 0; u < NG; ++u) {
       const float ex = r < k ? expf(my_l[u] - l0[u]) : 0.0f;
