@@ -220,8 +220,8 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
   const int tid = opaque((int)threadIdx.x), lane = tid & 63, wave = tid >> 6;
   // Wave w owns rows 128 * (w / 4) and columns 64 * (w % 4) of the tile
   // (wave-to-SIMD placement is w % 4), so every SIMD holds one wave of each
-  // row half; a wave whose 128 rows all lie past the group end skips its
-  // MFMAs, which halves the matrix work of each SIMD on such a tile.
+  // row half; a wave multiplies only its 32-row blocks that hold a row before
+  // the group end, and one whose 128 rows all lie past it skips its MFMAs.
   const int wm = wave >> 2, wn = wave & 3;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   // Roles (every epilogue but the SwiGLU backward, which copies h through the
@@ -357,8 +357,8 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
         for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
 
     bf16x8_t af[2][4], bf[2][2];
-    // NI: the 32-row blocks of the wave that are multiplied (4, or 2 when the
-    // wave's rows past the first 64 are all past the group end)
+    // NI: the 32-row blocks of the wave that are multiplied, those holding a
+    // row before the group end (1 to 4)
     auto read_frags = [&](auto NIc, int stage, int ks, int set) {
       constexpr int NI = decltype(NIc)::value;
       const uint8_t* As = As0 + stage * kOpStage;
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
 #pragma unroll
       for (int j = 0; j < 2 * NI; ++j) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, NI == 4 ? 1 : 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, NI >= 3 ? 1 : (NI == 2 ? 2 : 3), 0);
       }
     };
 
@@ -399,7 +399,9 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
     // rows of this tile that count for the multiply, from this wave's first row (wave-uniform)
     const int wrows = m_cls - (m0 + (wave_u >> 2) * 128);
     using NI4 = std::integral_constant<int, 4>;
+    using NI3 = std::integral_constant<int, 3>;
     using NI2 = std::integral_constant<int, 2>;
+    using NI1 = std::integral_constant<int, 1>;
     // k-slice kt on stage kt % NST. On entry its first 16-wide sub-slice is in
     // fragment set 0. The barrier sits before the second sub-slice: every wave
     // then holds all of stage kt % NST in registers, so the loads of k-slice
@@ -450,9 +452,10 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
         }
         if (cp && i < LPW) g2lds16(Ak, a_off[i], lds_a + cst + i * 1024);
       }
-      if (NI == 2) {
-        if (OP == OP_NT) bf[0][1] = frag_k4(Bs, lane, 0, frag_col8<EPI>(wn, 1));
-        else bf[0][1] = frag_tr(Bs, lane, 0, frag_col8<EPI>(wn, 1));
+#pragma unroll
+      for (int f = NI / 2; f < 2; ++f) {  // the B fragments not read between the MFMAs
+        if (OP == OP_NT) bf[0][f] = frag_k4(Bs, lane, 0, frag_col8<EPI>(wn, f));
+        else bf[0][f] = frag_tr(Bs, lane, 0, frag_col8<EPI>(wn, f));
       }
       if (cp) {
 #pragma unroll
@@ -472,10 +475,14 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
         second_half(NIc, kt);
       }
     };
-    if (wrows > 64) {
+    if (wrows > 96) {
       kloop(NI4{});
+    } else if (wrows > 64) {
+      kloop(NI3{});  // blocks from NI on keep their zero accumulators; their rows are not stored
+    } else if (wrows > 32) {
+      kloop(NI2{});
     } else if (wrows > 0) {
-      kloop(NI2{});  // blocks 2 and 3 keep their zero accumulators; their rows are not stored
+      kloop(NI1{});
     } else {
       // no output rows: keep the copies and barriers of the k-loop only
       for (int kt = 0; kt < nk; ++kt) {
