@@ -297,8 +297,8 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
       }
       if (kt + MXN < nk) issue_loads(kt + MXN);
     };
-    // NI: the 32-row blocks of the wave that are multiplied (4, or 2 when its
-    // rows past the first 64 are all past the group end)
+    // NI: the 32-row blocks of the wave that are multiplied, those holding a
+    // row before the group end (1 to 4)
     auto kloop = [&](auto NIc) {
       constexpr int NI = decltype(NIc)::value;
       for (int kt = 0; kt < nk; ++kt) {
@@ -332,10 +332,14 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
     };
     // rows of this tile that hold outputs, from this wave's first row (wave-uniform)
     const int wrows = m_cls - (m0 + (wave_u >> 2) * 128);
-    if (wrows > 64) {
+    if (wrows > 96) {
       kloop(std::integral_constant<int, 4>{});
+    } else if (wrows > 64) {
+      kloop(std::integral_constant<int, 3>{});  // blocks from NI on keep zero accumulators; their rows are not stored
+    } else if (wrows > 32) {
+      kloop(std::integral_constant<int, 2>{});
     } else if (wrows > 0) {
-      kloop(std::integral_constant<int, 2>{});  // blocks 2 and 3 keep zero accumulators; their rows are not stored
+      kloop(std::integral_constant<int, 1>{});
     } else {
       for (int kt = 0; kt < nk; ++kt) kwait(kt);  // no output rows: the waits, barriers and copies only
     }
