@@ -117,8 +117,9 @@ def test_grouped_gemm_mx_matches_oracle(M, K, N, E, empty, epi):
 
 
 # Groups whose last 256-row tile ends at every 32-row block boundary of either half of the tile, and just past
-# them, plus an empty group: every k-loop form of the tile (four blocks, two blocks, none).
-MX_PARTIAL_SIZES = [1, 32, 33, 64, 65, 128, 129, 160, 224, 255, 256, 257, 300, 384, 385, 448, 449, 512, 543, 0]
+# them, plus an empty group: every k-loop form of the tile (one to four blocks, none).
+MX_PARTIAL_SIZES = [1, 32, 33, 64, 65, 96, 97, 128, 129, 160, 161, 192, 193, 224, 225, 255, 256, 257, 300, 384, 385,
+                    448, 449, 512, 543, 0]
 
 
 @pytest.mark.parametrize("epi", ["none", "swiglu"])

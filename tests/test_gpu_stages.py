@@ -286,9 +286,10 @@ def test_grouped_gemm_nt_swiglu_bwd(M, K, N, E, empty):
 
 # Groups whose last 256-row tile ends at every 32-row block boundary of either half of the tile, and just past
 # it (a tile multiplies only its blocks that hold rows of the group); groups of 257-512 rows, which run as two
-# halves multiplied as ceil(n/2) rows, with halves at and just past the 64- and 128-row wave boundaries
-# (384/385, 448/449, 512); and an empty group.
-PARTIAL_SIZES = [1, 32, 33, 64, 65, 128, 129, 160, 224, 255, 256, 257, 300, 384, 385, 448, 449, 512, 543, 0]
+# halves multiplied as ceil(n/2) rows, whose second row half ends at and just past its 64- and 96-row block
+# boundaries (384/385, 448/449) or fills it (512); and an empty group.
+PARTIAL_SIZES = [1, 32, 33, 64, 65, 96, 97, 128, 129, 160, 161, 192, 193, 224, 225, 255, 256, 257, 300, 384, 385,
+                 448, 449, 512, 543, 0]
 
 
 @pytest.mark.parametrize("op,epi", [("nn", "none"), ("nn", "swiglu"), ("nt", "none"), ("nt", "swiglu_bwd")])
