@@ -454,7 +454,10 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         try:
             tr = json.load(open(TRAFFIC_FILE))
-            ent = None if mx else tr.get(args.workload, {}).get("gemm1_swiglu")
+            # counters of the training step are filed under "<workload>:backward"; its GEMM 1 is the
+            # plain-row kernel, the inference forward's the row-gather one
+            key = args.workload + (":backward" if bwd else "")
+            ent = None if mx else tr.get(key, {}).get("gemm1_swiglu")
             if ent and ent.get("source_sha") == source_hash(GEMM_SRC):
                 traffic = ent["bytes_per_launch"]
         except Exception:
