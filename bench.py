@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gemma4_class]
                     [--backward [--recompute-h] | --mxfp8] [--no-cpu-baseline] [--no-configs]
-                    [--stage-json PATH]
+                    [--no-vendor-yardstick] [--stage-json PATH]
 
 One step = one pass of the whole forward hot path over one batch: route,
 permute, grouped GEMM 1 (prefused wi, SwiGLU epilogue), grouped GEMM 2 (wo),
@@ -27,6 +27,10 @@ expert weights are quantized beforehand (weight preparation, outside the
 timed step).
 With --recompute-h the forward keeps no fp32 gate/up values and the backward
 recomputes them with one more GEMM1 (the saved bytes are reported).
+
+The bf16 forward line also carries `vendor_dense_gemm`: the vendor library's
+dense GEMM of the same size and FLOPs as each grouped GEMM, timed after the
+step as context for the roofline fraction (skip with --no-vendor-yardstick).
 
 Unless --no-configs is given, the line also carries `configs`: the other
 workloads measured the same way after the headline one (tiny, mid_skewed, the
@@ -72,6 +76,8 @@ def parse():
                     help="with --backward: the forward keeps no h and the backward recomputes it (full remat)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="measure the headline workload only")
+    ap.add_argument("--no-vendor-yardstick", action="store_true",
+                    help="skip timing the vendor library's dense GEMMs of the same sizes")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--stage-json", default=None, help="also write per-stage details to this file")
     return ap.parse_args()
@@ -405,6 +411,39 @@ def measure(wl, dev, steps, warmup, bwd=False, remat=False, mx=False, flush_comb
                 else None)
 
 
+def vendor_dense_gemm(wl, dev, iters=10):
+    """Yardstick, not part of the step: the vendor library's dense bf16 GEMM (hipBLASLt through
+    torch.matmul, contiguous 2-D operands) of the same total size and FLOPs as each grouped GEMM,
+    [S, emb] x [emb, 2 mlp] and [S, mlp] x [mlp, emb], without SwiGLU or ragged groups."""
+    import torch
+
+    S = wl.T * wl.k
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    out = {"library": "hipBLASLt via torch.matmul (dense bf16, fp32 accumulate)",
+           "note": "the same FLOPs as the grouped GEMM, as one dense GEMM; context for the roofline fraction"}
+    for name, (m, kk, n) in (("gemm1", (S, wl.emb, 2 * wl.mlp)), ("gemm2", (S, wl.mlp, wl.emb))):
+        a = torch.randn((m, kk), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        b = (torch.randn((kk, n), generator=g, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+        c = torch.empty((m, n), device=dev, dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a, b, out=c)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(iters):
+            torch.matmul(a, b, out=c)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / iters
+        flop = 2.0 * m * kk * n
+        out[name] = {"m_k_n": [m, kk, n], "ms": round(ms, 5), "tflops": round(tf(flop, ms), 1),
+                     "frac": round(tf(flop, ms) / PEAK_BF16_TFLOPS, 4)}
+        del a, b, c
+        torch.cuda.empty_cache()
+    return out
+
+
 def _round(d):
     return {k_: ({kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                  if isinstance(v, dict) else (round(v, 5) if isinstance(v, float) else v)) for k_, v in d.items()}
@@ -470,6 +509,10 @@ def main():
                 "frac": round(g1["frac"], 4), "traffic": traffic,
                 "per_launch_flop": r["g1_flop"], "avg_launch_ms": round(g1["ms"], 5)}
 
+    vendor = None
+    if not (mx or bwd or args.no_vendor_yardstick):
+        vendor = vendor_dense_gemm(wl, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(r["inp"], wl, args.cpu_seconds)
@@ -515,6 +558,7 @@ def main():
         "saved_bytes": r["saved_bytes"],
         "stages": {k_: _round(v) for k_, v in stages.items()},
         "roofline": roofline,
+        "vendor_dense_gemm": vendor,
         "cpu_baseline": cpu,
         "configs": configs,
     }
