@@ -14,7 +14,8 @@
  *    stated. bf16 tensors are passed as raw 16-bit patterns (moe_bf16_t).
  *    Every pointer must be 16-byte aligned.
  *  - The caller owns all memory, the workspace included. The library never
- *    allocates, frees, synchronises or copies between host and device.
+ *    allocates, frees, synchronises or copies between host and device. A
+ *    workspace whose required size is 0 (no tokens) may be NULL.
  *  - Calls only enqueue work on `stream` (a hipStream_t; NULL = the null
  *    stream) and return. Results are ready when the stream reaches them.
  *  - Arguments are validated before anything is enqueued. A call that

@@ -57,6 +57,15 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
   do {                                                                \
     if ((p) && !aligned16(p)) return fail(MOE_ERR_ALIGN, "argument %s is not 16-byte aligned", #p); \
   } while (0)
+// The workspace `ws` of `ws_bytes` must hold `n` bytes; it may be NULL when the call needs none
+// (no tokens).
+#define NEED_WS(n)                                                                                   \
+  do {                                                                                               \
+    const size_t need_ = (n);                                                                        \
+    if (need_ > 0) NEED(ws);                                                                         \
+    else MAYBE(ws);                                                                                  \
+    if (ws_bytes < need_) return fail(MOE_ERR_WORKSPACE, "need %zu workspace bytes", need_);         \
+  } while (0)
 
 constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -250,8 +259,7 @@ int moe_permute(const moe_shape_t* s, const moe_bf16_t* x, const int32_t* topk_i
     MAYBE(xs);  // NULL: index only, the rows are not copied
     if (xs) NEED(x);
   }
-  NEED(ws);
-  if (ws_bytes < permute_ws(s)) return fail(MOE_ERR_WORKSPACE, "need %zu workspace bytes", permute_ws(s));
+  NEED_WS(permute_ws(s));
   char* w = static_cast<char*>(ws);
   uint64_t* masks = reinterpret_cast<uint64_t*>(w);
   int32_t* base = reinterpret_cast<int32_t*>(w + masks_bytes(s));
@@ -444,8 +452,7 @@ int moe_route_bwd(const moe_shape_t* s, const moe_bf16_t* x, const float* wr, co
     NEED(sorted_slot);
     MAYBE(dx);
   }
-  NEED(ws);
-  if (ws_bytes < route_bwd_ws(s)) return fail(MOE_ERR_WORKSPACE, "need %zu workspace bytes", route_bwd_ws(s));
+  NEED_WS(route_bwd_ws(s));
   Carver c{static_cast<char*>(ws)};
   float* dl = c.take<float>(s->T * s->k);
   float* dls = c.take<float>(s->T * s->k);
@@ -556,8 +563,7 @@ int moe_ffn_fwd_mx(const moe_shape_t* s, const moe_bf16_t* x, const float* wr, c
     NEED(wr);
     MAYBE(bias);
   }
-  NEED(ws);
-  if (ws_bytes < fwd_mx_ws(s)) return fail(MOE_ERR_WORKSPACE, "need %zu workspace bytes", fwd_mx_ws(s));
+  NEED_WS(fwd_mx_ws(s));
   if (!any) return MOE_OK;
   const int64_t T = s->T, S = T * s->k;
   const int emb = s->emb, mlp = s->mlp, E = s->E, k = s->k;
@@ -618,8 +624,7 @@ int moe_ffn_fwd(const moe_shape_t* s, const moe_bf16_t* x, const float* wr, cons
     NEED(wr);
     MAYBE(bias);
   }
-  NEED(ws);
-  if (ws_bytes < fwd_ws(s)) return fail(MOE_ERR_WORKSPACE, "need %zu workspace bytes", fwd_ws(s));
+  NEED_WS(fwd_ws(s));
   if (saved) {
     NEED(saved->group_sizes);
     NEED(saved->group_offsets);
@@ -699,10 +704,8 @@ int moe_ffn_bwd(const moe_shape_t* s, const moe_bf16_t* dy, const moe_saved_t* s
   MAYBE(dwi);
   MAYBE(dwo);
   MAYBE(dtopk_w);
-  NEED(ws);
   const bool remat = saved->h == nullptr;
-  const size_t need_ws = remat ? bwd_remat_ws(s) : bwd_ws(s);
-  if (ws_bytes < need_ws) return fail(MOE_ERR_WORKSPACE, "need %zu workspace bytes", need_ws);
+  NEED_WS(remat ? bwd_remat_ws(s) : bwd_ws(s));
   const int64_t T = s->T, S = T * s->k;
   const int emb = s->emb, mlp = s->mlp, E = s->E, k = s->k;
   const hipStream_t st = (hipStream_t)stream;

@@ -153,6 +153,33 @@ def test_layer_backward_every_token_and_expert():
     assert torch.equal(g2["dx"].view(torch.int16), g["dx"].view(torch.int16))
 
 
+@pytest.mark.parametrize("T,emb,mlp,E,k", [(1, 64, 64, 4, 2), (100, 128, 64, 2, 2), (257, 256, 128, 64, 8),
+                                           (0, 128, 128, 8, 2)])
+def test_layer_backward_edge_shapes(T, emb, mlp, E, k):
+    """One token (two of its four experts get no rows); k = E; 64 experts of about 32 rows each (every row
+    block partial); no tokens at all. Every gradient on every token and expert against the oracle, and an
+    expert with no rows gets dW exactly 0."""
+    wl = workloads.custom(T, emb, mlp, E, k, seed=T + 3 * E, sigma_w=0.05, backward=True)
+    h = workloads.make_inputs(wl)
+    d = _dev(h)
+    y, saved = _fwd(d)
+    g = moe.ffn_bwd(d["dy"], saved, d["wi"], d["wo"], k)
+    assert tuple(g["dx"].shape) == (T, emb) and tuple(g["dtopk_w"].shape) == (T, k)
+    gs = saved["group_sizes"].cpu().numpy()
+    for e in np.flatnonzero(gs == 0):
+        assert not g["dwi"][e].any() and not g["dwo"][e].any(), f"expert {e} has no rows but a nonzero dW"
+    if T == 0:
+        return
+    r_idx, r_w, *_ = _check_routing_and_permute(saved, h)
+    x, wi, wo, dy = bits(h["x"]), bits(h["wi"]), bits(h["wo"]), bits(h["dy"])
+    dx, dtw = oracle.ffn_bwd_tokens(x, r_idx, r_w, wi, wo, dy, stored_bf16=True)
+    assert_close(to_np(g["dx"]), dx, "dx")
+    assert_close(g["dtopk_w"].cpu().numpy(), dtw, "dtopk_w")
+    ref = oracle.ffn_wgrad_experts(x, r_idx, r_w, wi, wo, dy, range(E), stored_bf16=True)
+    assert_close_bf16_out(to_np(g["dwi"]), np.stack([ref[e][0] for e in range(E)]), "dwi")
+    assert_close_bf16_out(to_np(g["dwo"]), np.stack([ref[e][1] for e in range(E)]), "dwo")
+
+
 @pytest.mark.parametrize("T,emb,mlp,E,k", [(384, 256, 128, 8, 2), (300, 128, 256, 6, 3)])
 def test_layer_backward_recomputing_h_equals_kept_h_bitwise(T, emb, mlp, E, k):
     """Full rematerialisation of h: the forward keeps no h and the backward recomputes it with the forward's

@@ -210,7 +210,7 @@ import workloads  # noqa: E402
 
 
 def _mx_layer_inputs(name):
-    h = workloads.make_inputs(workloads.WORKLOADS[name])
+    h = workloads.make_inputs(workloads.WORKLOADS[name] if isinstance(name, str) else name)
     d = {kk: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for kk, v in h.items()}
     return h, d
 
@@ -236,7 +236,13 @@ def test_ffn_fwd_mx_equals_its_stages_bitwise(name):
     assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
 
 
-@pytest.mark.parametrize("name", ["tiny", "mid_skewed"])
+# one token (two of its four experts get no rows); k = E; 64 experts of about 32 rows each (every row block partial)
+MX_EDGE = [workloads.custom(1, 64, 64, 4, 2, seed=5, sigma_w=0.05),
+           workloads.custom(100, 128, 64, 2, 2, seed=6, sigma_w=0.05),
+           workloads.custom(257, 256, 128, 64, 8, seed=7, sigma_w=0.05)]
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid_skewed"] + MX_EDGE, ids=lambda n: n if isinstance(n, str) else n.name)
 def test_ffn_fwd_mx_matches_the_oracle_composition(name):
     """Each stage from the oracle: routing, token quantization, float64 GEMM 1 on the dequantized operands,
     SwiGLU rounded to bf16 and quantized, float64 GEMM 2, bf16 rounding, combine. The device and the oracle
