@@ -38,7 +38,14 @@ __global__ __launch_bounds__(256) void combine_kernel(int64_t T, int emb, int k,
     }
   }
   const int nch = emb >> 3;
-  for (int c = lane; c < nch; c += 64) {
+  // Pick j lives in lane j, and the shuffles below read it from there. A shuffle does not return
+  // the value of a lane outside the active set, so the chunk loop is wave-uniform and only the
+  // loads and the store are masked: with a per-lane loop, a row of fewer than 64 chunks (or the
+  // last, partial round of a longer one) left the lanes past its end, and with them every pick
+  // held there when k exceeded the active lanes, out of the sum.
+  for (int c0 = 0; c0 < nch; c0 += 64) {
+    const int c = c0 + lane;
+    const bool on = c < nch;
     float acc[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc[u] = 0.0f;
@@ -50,7 +57,7 @@ __global__ __launch_bounds__(256) void combine_kernel(int64_t T, int emb, int k,
       for (int u = 0; u < kJB; ++u) {
         rr[u] = __shfl(my_r, (j0 + u) & 63);
         ww[u] = __shfl(my_w, (j0 + u) & 63);
-        if (j0 + u >= k) rr[u] = -1;
+        if (j0 + u >= k || !on) rr[u] = -1;
       }
 #pragma unroll
       for (int u = 0; u < kJB; ++u)
@@ -65,6 +72,7 @@ __global__ __launch_bounds__(256) void combine_kernel(int64_t T, int emb, int k,
         }
       }
     }
+    if (!on) continue;
     u32x4_t o;
 #pragma unroll
     for (int m = 0; m < 4; ++m) o[m] = pack_bf16x2(acc[2 * m], acc[2 * m + 1]);

@@ -35,7 +35,9 @@ def _route_case(T, emb, E, k, seed, bias=None):
                                             (130, 64, 256, 8, 4), (77, 128, 192, 6, 8), (70, 128, 5, 5, 5),
                                             (17, 64, 64, 1, 6), (0, 64, 8, 2, 7),
                                             # k > 16: one token per wave in the top-k (E % 4 != 0: register-staged kernel)
-                                            (100, 128, 64, 20, 9), (50, 64, 256, 24, 10), (40, 64, 37, 17, 11)])
+                                            (100, 128, 64, 20, 9), (50, 64, 256, 24, 10), (40, 64, 37, 17, 11),
+                                            # the largest k: every expert (k = E = 64), and 64 of 256
+                                            (40, 64, 64, 64, 12), (30, 128, 256, 64, 13)])
 def test_route_bit_exact(T, emb, E, k, seed):
     x, wr, _ = _route_case(T, emb, E, k, seed)
     idx, w = moe.route(k, x=x.to(DEV), wr=wr.to(DEV))
@@ -168,7 +170,10 @@ def _combine_bound(exact, mag, k):
     return chain + 0.5 * ulp
 
 
-@pytest.mark.parametrize("T,emb,k", [(64, 128, 2), (777, 1024, 4), (300, 2048, 8), (5, 7168, 8)])
+# the last two: more picks than 16-byte chunks in a row (emb 64, k 64) and in its last round of
+# chunks (emb 576: 72 chunks, a round of 64 and one of 8, with k 16)
+@pytest.mark.parametrize("T,emb,k", [(64, 128, 2), (777, 1024, 4), (300, 2048, 8), (5, 7168, 8), (40, 64, 64),
+                                     (50, 576, 16)])
 def test_combine_within_rounding_bound_of_exact_sum(T, emb, k):
     E = max(8, k)
     rng = np.random.default_rng(T)
@@ -185,17 +190,17 @@ def test_combine_within_rounding_bound_of_exact_sum(T, emb, k):
     assert_close(bf16_values(bits(y)), exact, "y")
 
 
-@pytest.mark.parametrize("k", [2, 3, 4, 8])
+@pytest.mark.parametrize("k", [2, 3, 4, 8, 16, 64])
 def test_combine_of_permute_with_unit_weights_is_k_x(k):
     """permute then combine with unit weights: y == bf16(k * x) exactly (exact for k a power of two)."""
-    T, emb, E = 513, 256, 16
+    T, emb, E = 513, 256, max(16, k)
     x = torch.randn((T, emb)).to(torch.bfloat16)
     idx = torch.from_numpy(_random_idx(T, E, k, k)).to(DEV)
     out = moe.permute(x.to(DEV), idx, E)
     y = moe.combine(out["xs"], out["slot_row"], None, T, k)
     want = (x.float() * k).to(torch.bfloat16)
     assert np.array_equal(bits(y), bits(want))
-    if k in (2, 4, 8):
+    if k in (2, 4, 8, 16, 64):
         assert np.array_equal(bf16_values(bits(y)), k * bf16_values(bits(x)))
 
 
