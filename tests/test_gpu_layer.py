@@ -70,7 +70,8 @@ def test_layer_forward_every_token(name):
 
 
 @pytest.mark.parametrize("T,emb,mlp,E,k", [(1, 64, 64, 4, 2), (300, 192, 320, 12, 3), (257, 256, 128, 64, 8),
-                                           (100, 128, 64, 2, 2), (0, 128, 128, 8, 2), (20, 64, 64, 64, 64)])
+                                           (100, 128, 64, 2, 2), (0, 128, 128, 8, 2), (20, 64, 64, 64, 64),
+                                           (200, 192, 320, 37, 3)])
 def test_layer_forward_edge_shapes(T, emb, mlp, E, k):
     wl = workloads.custom(T, emb, mlp, E, k, seed=T + E, sigma_w=0.05)
     h = workloads.make_inputs(wl)
@@ -154,10 +155,12 @@ def test_layer_backward_every_token_and_expert():
 
 
 @pytest.mark.parametrize("T,emb,mlp,E,k", [(1, 64, 64, 4, 2), (100, 128, 64, 2, 2), (257, 256, 128, 64, 8),
-                                           (0, 128, 128, 8, 2), (20, 64, 64, 64, 64)])
+                                           (0, 128, 128, 8, 2), (20, 64, 64, 64, 64), (200, 192, 320, 37, 3)])
 def test_layer_backward_edge_shapes(T, emb, mlp, E, k):
     """One token (two of its four experts get no rows); k = E; 64 experts of about 32 rows each (every row
-    block partial); no tokens at all; the largest k (every token picks all 64 experts). Every gradient on every token and expert against the oracle, and an
+    block partial); no tokens at all; the largest k (every token picks all 64 experts); 37 experts (not a
+    multiple of the 8 XCDs the weight-gradient tiles are dealt over) with emb and mlp that leave partial
+    tiles in every weight-gradient dimension. Every gradient on every token and expert against the oracle, and an
     expert with no rows gets dW exactly 0."""
     wl = workloads.custom(T, emb, mlp, E, k, seed=T + 3 * E, sigma_w=0.05, backward=True)
     h = workloads.make_inputs(wl)

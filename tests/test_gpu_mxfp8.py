@@ -236,10 +236,12 @@ def test_ffn_fwd_mx_equals_its_stages_bitwise(name):
     assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
 
 
-# one token (two of its four experts get no rows); k = E; 64 experts of about 32 rows each (every row block partial)
+# one token (two of its four experts get no rows); k = E; 64 experts of about 32 rows each (every row block
+# partial); the largest k (every token picks all 64 experts)
 MX_EDGE = [workloads.custom(1, 64, 64, 4, 2, seed=5, sigma_w=0.05),
            workloads.custom(100, 128, 64, 2, 2, seed=6, sigma_w=0.05),
-           workloads.custom(257, 256, 128, 64, 8, seed=7, sigma_w=0.05)]
+           workloads.custom(257, 256, 128, 64, 8, seed=7, sigma_w=0.05),
+           workloads.custom(20, 64, 64, 64, 64, seed=8, sigma_w=0.05)]
 
 
 @pytest.mark.parametrize("name", ["tiny", "mid_skewed"] + MX_EDGE, ids=lambda n: n if isinstance(n, str) else n.name)

@@ -421,7 +421,8 @@ def _check_route_bwd(x, wr, idx, w, g, perm, dx0, out, dx, want_dx=True):
 
 @pytest.mark.parametrize("T,emb,E,k,seed,empty", [(300, 256, 16, 4, 1, ()), (129, 64, 256, 8, 2, (3, 77)),
                                                   (1000, 1024, 128, 8, 3, (0,)), (77, 7168, 200, 6, 4, ()),
-                                                  (50, 128, 8, 8, 5, ())])
+                                                  (50, 128, 8, 8, 5, ()), (40, 64, 64, 64, 6, ()),
+                                                  (60, 128, 37, 5, 7, (36,))])
 def test_route_bwd_matches_oracle(T, emb, E, k, seed, empty):
     x, wr, idx, w, g, perm, dx0 = _route_bwd_case(T, emb, E, k, seed, empty)
     dx = dx0.clone()
