@@ -6,7 +6,10 @@ forward+backward) are generated on the device; routing, group sizes, sort
 order and the permuted rows are compared bit for bit on every token. The
 forward output of the Gemma4-class layer and of the sweep is compared on
 every token; the DeepSeek-V3-shaped output and gradients on 64 sampled tokens
-and nine experts that the oracle computes one by one.
+and nine experts that the oracle computes one by one. At the largest token count
+the boundary takes (T * emb just under 2^31) routing and the sort order are
+compared on every token and the output on sampled ones, the last tokens among
+them.
 """
 import numpy as np
 import pytest
@@ -245,6 +248,36 @@ def test_full_size_forward_every_token(name, chunk):
     toks = np.arange(chunk * CHUNK, min(T, (chunk + 1) * CHUNK), dtype=np.int64)
     ref = oracle.ffn_fwd_tokens(bits(h["x"]), r_idx, r_w, bits(h["wi"]), bits(h["wo"]), tokens=toks)
     assert_close(y[toks], ref, f"{name} y[{toks[0]}:{toks[-1] + 1}]")
+
+
+@pytest.mark.slow
+def test_layer_forward_at_the_largest_token_count():
+    """The largest T * emb the boundary takes: token rows are gathered through 32-bit byte offsets, so
+    T * emb < 2^31. 33,554,431 tokens of width 64, 4 experts, top-2, in the inference launch configuration:
+    GEMM 1 gathers the rows of x in place, the last ones almost 4 GiB into it. Routing and the sort order
+    are compared with the oracle bit for bit on every token, y on sampled tokens, the last 64 among them."""
+    T, emb, mlp, E, k = (2 ** 31 - 1) // 64, 64, 64, 4, 2
+    d = workloads.make_inputs(workloads.custom(T, emb, mlp, E, k, seed=4242, sigma_w=0.05), device=DEV)
+    y, _ = _fwd(d, save=False)
+    idx_d, w_d = moe.route(k, x=d["x"], wr=d["wr"])
+    perm = moe.permute(d["x"], idx_d, E, rows=False)
+    torch.cuda.synchronize()
+    xb = bits(d["x"])
+    idx, w, _ = oracle.route(xb, d["wr"].cpu().numpy(), None, k)
+    assert np.array_equal(idx_d.cpu().numpy(), idx), "topk_idx differs"
+    assert np.abs(w_d.cpu().numpy() - w).max() <= W_ABS
+    gs, go, ss, sr = oracle.dispatch(idx, E)
+    assert np.array_equal(perm["group_sizes"].cpu().numpy(), gs)
+    assert np.array_equal(perm["group_offsets"].cpu().numpy(), go)
+    assert np.array_equal(perm["sorted_slot"].cpu().numpy(), ss)
+    assert np.array_equal(perm["slot_row"].cpu().numpy(), sr)
+    toks = np.unique(np.concatenate([np.arange(T - 64, T), [0, T // 2],
+                                     np.random.default_rng(1).choice(T, 62, replace=False)])).astype(np.int64)
+    ref = oracle.ffn_fwd_tokens(np.ascontiguousarray(xb[toks]), np.ascontiguousarray(idx[toks]),
+                                np.ascontiguousarray(w[toks]), bits(d["wi"]), bits(d["wo"]))
+    assert_close(to_np(y[torch.from_numpy(toks).to(DEV)]), ref, "y (sampled, the last 64 tokens among them)")
+    del d, y, idx_d, w_d, perm
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.slow
