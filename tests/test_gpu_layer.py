@@ -281,6 +281,24 @@ def test_layer_forward_at_the_largest_token_count():
 
 
 @pytest.mark.slow
+def test_layer_forward_at_the_largest_expert_weight():
+    """The largest expert weight the boundary takes: emb * 2 * mlp < 2^31 elements, so that offsets inside one
+    expert's weight fit 32 bits. emb 16384, mlp 65472 (a 4.3 GB prefused wi, a partial SwiGLU column tile,
+    GEMM 2 contracting over 65472), 16 tokens, every output element against the oracle."""
+    T, emb, mlp, E, k = 16, 16384, 65472, 1, 1
+    assert emb * 2 * mlp < 2 ** 31 and emb * 2 * (mlp + 64) >= 2 ** 31
+    h = workloads.make_inputs(workloads.custom(T, emb, mlp, E, k, seed=77, sigma_w=0.004), device=DEV)
+    y, _ = _fwd(h, save=False)
+    torch.cuda.synchronize()
+    idx = np.zeros((T, 1), np.int32)
+    w = np.ones((T, 1), np.float32)
+    ref = oracle.ffn_fwd_tokens(bits(h["x"]), idx, w, bits(h["wi"]), bits(h["wo"]))
+    assert_close(to_np(y), ref, "y")
+    del h, y
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.slow
 def test_full_size_deepseek_v3_shape_forward_backward_sampled():
     d = workloads.make_inputs("deepseek_v3_shape", device=DEV)
     wl = d["workload"]
