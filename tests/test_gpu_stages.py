@@ -490,3 +490,89 @@ def test_swiglu_epilogues_with_saturating_gates(op, epi):
     assert rel <= 1e-2, rel
     # elementwise: one bf16 rounding of the result, plus the fp32 sums' own error
     assert np.all(np.abs(g - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-3 * np.abs(ref).max()), np.abs(g - ref).max()
+
+
+# ---------------------------------------------------------------- index data out of range
+
+def test_out_of_range_index_data_never_leaves_the_buffers():
+    """Index data made on the device is not checked on the host: out-of-range values give unspecified
+    results, but no kernel reads or writes outside the buffers. Expert ids out of range and repeated within
+    a token (permute), group offsets past M, negative and decreasing (grouped GEMM, weight gradient, router
+    backward), rows out of range (combine and its backward, the GEMM's row gather) and sorted slots out of
+    range (router backward): every output and workspace sits at the start of a larger allocation whose
+    tail must come back untouched."""
+    import ctypes as C
+
+    from mixture_experts_ffn_group_amd import _lib
+
+    L = _lib.lib()
+    st = torch.cuda.current_stream().cuda_stream
+    fills = {torch.int16: 0x2EAD, torch.int32: 0x2EADBEEF, torch.uint8: 0x5A}
+    guards = []
+
+    def guarded(shape, dtype, init=None):
+        n = int(np.prod(shape))
+        raw = {torch.bfloat16: torch.int16, torch.float32: torch.int32}.get(dtype, dtype)
+        buf = torch.full((n + 4096,), fills[raw], dtype=raw, device=DEV)
+        view = buf[:n].view(dtype).view(shape)
+        if init is not None:
+            view.copy_(init)
+        guards.append((buf, n, fills[raw]))
+        return view
+
+    def p(t):
+        return C.c_void_p(t.data_ptr())
+
+    rng = np.random.default_rng(5)
+    T, emb, E, k = 300, 128, 16, 4
+    S = T * k
+    s = _lib.shape(T, emb, 64, E, k)
+    x = _bf16_dev(rng.standard_normal((T, emb)))
+    bad_idx = torch.from_numpy(_random_idx(T, E, k, 5)).to(DEV)
+    bad_idx[::7, 0] = -1
+    bad_idx[1::7, 1] = E
+    bad_idx[2::7, 2] = 100000
+    bad_idx[3::7, 3] = bad_idx[3::7, 0]  # the same expert twice in one token
+    gs, go = guarded((E,), torch.int32), guarded((E + 1,), torch.int32)
+    ss, sr = guarded((S,), torch.int32), guarded((S,), torch.int32)
+    xs = guarded((S, emb), torch.bfloat16)
+    ws_n = int(L.moe_permute_workspace_bytes(C.byref(s)))
+    ws = guarded((ws_n,), torch.uint8)
+    _lib.check(L.moe_permute(C.byref(s), p(x), p(bad_idx), p(gs), p(go), p(ss), p(sr), p(xs), p(ws), ws_n, st),
+               "moe_permute")
+
+    row = torch.from_numpy(rng.integers(0, S, S).astype(np.int32)).to(DEV)
+    row[::5] = -3
+    row[1::5] = S
+    row[2::5] = 2 ** 31 - 1
+    ys = _bf16_dev(rng.standard_normal((S, emb)))
+    dy = _bf16_dev(rng.standard_normal((T, emb)))
+    w = torch.rand((T, k), device=DEV)
+    y = guarded((T, emb), torch.bfloat16)
+    _lib.check(L.moe_combine(C.byref(s), p(ys), p(row), p(w), p(y), st), "moe_combine")
+    dys, dtw = guarded((S, emb), torch.bfloat16), guarded((T, k), torch.float32)
+    _lib.check(L.moe_combine_bwd(C.byref(s), p(dy), p(ys), p(row), p(w), p(dys), p(dtw), st), "moe_combine_bwd")
+
+    M, K, N, Eg = 300, 128, 256, 6
+    off = torch.tensor([0, 120, 80, 400, -20, 290, 10 ** 6], dtype=torch.int32, device=DEV)
+    A = _bf16_dev(rng.standard_normal((M, K)))
+    B = _bf16_dev(rng.standard_normal((Eg, K, N)) * 0.05)
+    moe.grouped_gemm(A, B, off, out=guarded((M, N), torch.bfloat16))
+    moe.grouped_gemm(A, B, off, out=guarded((M, N), torch.bfloat16), row_slot=row[:M].contiguous())
+    D = _bf16_dev(rng.standard_normal((M, N)))
+    cw = guarded((Eg, K, N), torch.bfloat16)
+    _lib.check(L.moe_grouped_gemm_wgrad(p(A), p(D), p(off), Eg, M, K, N, p(cw), st), "moe_grouped_gemm_wgrad")
+
+    wr = torch.from_numpy((rng.standard_normal((emb, E)) * 0.05).astype(np.float32)).to(DEV)
+    g = torch.from_numpy(rng.standard_normal((T, k)).astype(np.float32)).to(DEV)
+    go_bad = torch.tensor([0, 500, 100, -7] + [S + 99] * (E - 3), dtype=torch.int32, device=DEV)
+    dwr, dbias = guarded((emb, E), torch.float32), guarded((E,), torch.float32)
+    dx = guarded((T, emb), torch.bfloat16, init=dy)
+    rb_n = int(L.moe_route_bwd_workspace_bytes(C.byref(s)))
+    rb_ws = guarded((rb_n,), torch.uint8)
+    _lib.check(L.moe_route_bwd(C.byref(s), p(x), p(wr), p(bad_idx), p(w), p(g), p(row), p(go_bad), p(dwr),
+                               p(dbias), p(dx), p(rb_ws), rb_n, st), "moe_route_bwd")
+
+    torch.cuda.synchronize()
+    for i, (buf, n, fill) in enumerate(guards):
+        assert torch.equal(buf[n:], torch.full_like(buf[n:], fill)), f"guarded buffer {i}: tail overwritten"
