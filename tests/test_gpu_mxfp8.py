@@ -244,7 +244,24 @@ MX_EDGE = [workloads.custom(1, 64, 64, 4, 2, seed=5, sigma_w=0.05),
            workloads.custom(20, 64, 64, 64, 64, seed=8, sigma_w=0.05)]
 
 
-@pytest.mark.parametrize("name", ["tiny", "mid_skewed"] + MX_EDGE, ids=lambda n: n if isinstance(n, str) else n.name)
+def _mx_random(n=6, seed=77):
+    """Seeded random shapes across the supported range (emb and mlp multiples of 64 up to 1024, E up to 256,
+    k up to 64), the oracle's work bounded."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        emb, mlp = 64 * int(rng.integers(1, 17)), 64 * int(rng.integers(1, 17))
+        E = int(rng.integers(1, 17)) if rng.random() < 0.5 else int(rng.integers(17, 257))
+        k = int(min(E, rng.choice([1, 2, 3, 4, 6, 8])))
+        if E > 8 and rng.random() < 0.35:
+            k = int(rng.integers(9, min(E, 64) + 1))
+        T = int(min(2000, rng.integers(1, max(2, int(2e8 / (k * emb * mlp))) + 1)))
+        out.append(workloads.custom(T, emb, mlp, E, k, seed=7100 + i, sigma_w=0.5 / np.sqrt(max(emb, mlp))))
+    return out
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid_skewed"] + MX_EDGE + _mx_random(),
+                         ids=lambda n: n if isinstance(n, str) else n.name)
 def test_ffn_fwd_mx_matches_the_oracle_composition(name):
     """Each stage from the oracle: routing, token quantization, float64 GEMM 1 on the dequantized operands,
     SwiGLU rounded to bf16 and quantized, float64 GEMM 2, bf16 rounding, combine. The device and the oracle

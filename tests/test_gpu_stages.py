@@ -419,7 +419,25 @@ def _check_route_bwd(x, wr, idx, w, g, perm, dx0, out, dx, want_dx=True):
         assert np.all(np.abs(to_np(dx) - exact) <= _combine_bound(exact, mag, k + 1) + ddl @ wra.T + 1e-30)
 
 
-@pytest.mark.parametrize("T,emb,E,k,seed,empty", [(300, 256, 16, 4, 1, ()), (129, 64, 256, 8, 2, (3, 77)),
+def _rb_random(n=6, seed=91):
+    """Seeded random router-backward shapes: emb up to 1024, E up to 256, k up to 64, up to two experts
+    that no token picks."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        emb = 64 * int(rng.integers(1, 17))
+        E = int(rng.integers(1, 17)) if rng.random() < 0.5 else int(rng.integers(17, 257))
+        k = int(min(E, rng.choice([1, 2, 3, 4, 6, 8])))
+        if E > 8 and rng.random() < 0.35:
+            k = int(rng.integers(9, min(E, 64) + 1))
+        T = int(rng.integers(1, 1500))
+        empty = tuple(int(e) for e in rng.choice(E, min(E - k, int(rng.integers(0, 3))), replace=False)) \
+            if E > k else ()
+        out.append((T, emb, E, k, 100 + i, empty))
+    return out
+
+
+@pytest.mark.parametrize("T,emb,E,k,seed,empty", _rb_random() + [(300, 256, 16, 4, 1, ()), (129, 64, 256, 8, 2, (3, 77)),
                                                   (1000, 1024, 128, 8, 3, (0,)), (77, 7168, 200, 6, 4, ()),
                                                   (50, 128, 8, 8, 5, ()), (40, 64, 64, 64, 6, ()),
                                                   (60, 128, 37, 5, 7, (36,))])
