@@ -469,9 +469,9 @@ __global__ __launch_bounds__(MXT, 1) void mx_gemm_kernel(MxGemmP p) {
           const int sc = mx_e8m0_code(am);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) word |= mx_e4m3_code(ldexpf(v[4 * q + u], 127 - sc)) << (8 * u);
+            const int ex = 127 - sc;
+            const uint32_t word = mx_e4m3_x4(ldexpf(v[4 * q], ex), ldexpf(v[4 * q + 1], ex), ldexpf(v[4 * q + 2], ex),
+                                             ldexpf(v[4 * q + 3], ex));
             *reinterpret_cast<uint32_t*>(stg + 1024 + r * 32 + 8 * q + 4 * hh) = word;  // [32 rows][32 codes]
           }
           wave_lds_fence();

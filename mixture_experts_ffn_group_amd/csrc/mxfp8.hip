@@ -50,14 +50,10 @@ __global__ __launch_bounds__(256) void mxq_rows_kernel(const uint16_t* __restric
   am = max(am, (uint32_t)__shfl_xor((int)am, 1));
   am = max(am, (uint32_t)__shfl_xor((int)am, 2));
   const int sc = mx_e8m0_code(am);
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) lo |= mx_e4m3_code(ldexpf(x[i], 127 - sc)) << (8 * i);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) hi |= mx_e4m3_code(ldexpf(x[4 + i], 127 - sc)) << (8 * i);
+  const int ex = 127 - sc;
   u32x2_t out;
-  out[0] = lo;
-  out[1] = hi;
+  out[0] = mx_e4m3_x4(ldexpf(x[0], ex), ldexpf(x[1], ex), ldexpf(x[2], ex), ldexpf(x[3], ex));
+  out[1] = mx_e4m3_x4(ldexpf(x[4], ex), ldexpf(x[5], ex), ldexpf(x[6], ex), ldexpf(x[7], ex));
   *reinterpret_cast<u32x2_t*>(codes + r * K + (int64_t)c8 * 8) = out;
   const int sc_odd = __shfl_xor(sc, 4);  // the other block of this 64-element slice
   if ((c8 & 7) == 0) {
@@ -97,10 +93,9 @@ __global__ __launch_bounds__(256) void mxq_weight_kernel(const uint16_t* __restr
       u32x4_t o;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) word |= mx_e4m3_code(ldexpf(x[16 * g + 4 * d + i], 127 - sc)) << (8 * i);
-        o[d] = word;
+        const float* xv = x + 16 * g + 4 * d;
+        const int ex = 127 - sc;
+        o[d] = mx_e4m3_x4(ldexpf(xv[0], ex), ldexpf(xv[1], ex), ldexpf(xv[2], ex), ldexpf(xv[3], ex));
       }
       st16(dst + 32 * b + 16 * g, o);
     }
