@@ -182,7 +182,10 @@ __device__ __forceinline__ bf16x8_t frag_k4(const uint8_t* tile, int lane, int k
 }
 __device__ __forceinline__ void wait_vm_4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
 
-template <int OP, int EPI, bool GATHER>
+// GATHER: the A rows are read in place through p.row_slot. SCALE: every output row is scaled by
+// p.slot_scale (indexed through p.row_slot with GATHER, else by the row). Separate instances, so that a
+// scale without a gather never touches p.row_slot and a gather without a scale multiplies by nothing.
+template <int OP, int EPI, bool GATHER, bool SCALE>
 __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kGemmLds];
   // Output staging: 2 KB per wave, 32 rows x 64 bytes of the wave's output at a time.
@@ -496,11 +499,11 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
     // optional per-row fp32 scale (the top-k weight of the row's slot), applied as values are read;
     // fetched before the prefetch so that its wait does not cover the next tile's loads
     float sc4[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-    if (GATHER && p.slot_scale) {  // the four indices, then the four scales: two round trips
+    if (SCALE) {  // the four indices, then the four scales: two round trips
       int si[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) si[i] = min(cm0 + wm * 128 + i * 32 + (lane & 31), cm_end - 1);
-      if (p.row_slot) {
+      if (GATHER) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) si[i] = p.row_slot[si[i]];
 #pragma unroll
@@ -513,7 +516,7 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
     // compiler does not count, so a first use in the epilogue would carry a vmcnt wait sized for the
     // compiler's own loads, covering the copies too; and since the loads are conditional, that wait
     // (and any reuse of their registers, even in the next k-loop) was kept on both paths.
-    if (GATHER) {
+    if (SCALE) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(sc4[i]));
     }
@@ -1054,10 +1057,12 @@ hipError_t launch_grouped_gemm(int op, int epi, const uint16_t* A, const uint16_
   GemmP p{A, B, aux_in, aux_out, C, group_offsets, row_slot, slot_scale, E, (int)M, K, N,
           row_slot ? n_slots : (int)M, slot_div > 0 ? slot_div : 1};
   const dim3 grid(grid_size > 0 ? grid_size : persistent_grid()), block(GTHR);
-  const bool g = row_slot != nullptr || slot_scale != nullptr;
+  const bool g = row_slot != nullptr, sc = slot_scale != nullptr;
 #define MOE_GEMM_LAUNCH(O, P)                                                           \
-  if (g) gemm_kernel<O, P, true><<<grid, block, 0, stream>>>(p);                        \
-  else gemm_kernel<O, P, false><<<grid, block, 0, stream>>>(p);
+  if (g && sc) gemm_kernel<O, P, true, true><<<grid, block, 0, stream>>>(p);            \
+  else if (g) gemm_kernel<O, P, true, false><<<grid, block, 0, stream>>>(p);            \
+  else if (sc) gemm_kernel<O, P, false, true><<<grid, block, 0, stream>>>(p);           \
+  else gemm_kernel<O, P, false, false><<<grid, block, 0, stream>>>(p);
   if (op == OP_NN && epi == EPI_NONE) { MOE_GEMM_LAUNCH(OP_NN, EPI_NONE) }
   else if (op == OP_NN && epi == EPI_SWIGLU) { MOE_GEMM_LAUNCH(OP_NN, EPI_SWIGLU) }
   else if (op == OP_NT && epi == EPI_NONE) { MOE_GEMM_LAUNCH(OP_NT, EPI_NONE) }

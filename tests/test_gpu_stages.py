@@ -338,6 +338,29 @@ def test_grouped_gemm_row_gather_and_row_scale(op, epi):
     assert_close(to_np(got), ref, f"{op}/{epi}")
 
 
+@pytest.mark.parametrize("op,epi", [("nn", "none"), ("nn", "swiglu"), ("nt", "none"), ("nt", "swiglu_bwd")])
+def test_grouped_gemm_row_scale_without_gather(op, epi):
+    """A per-row fp32 scale with no row gather (slot_scale indexed by the output row, A read as it is):
+    equal to the oracle GEMM on the scaled rows."""
+    M, K, N, E = 700, 256, 320, 5
+    rng = np.random.default_rng(23)
+    sizes = rng.multinomial(M, np.ones(E) / E)
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    A = _bf16_dev(rng.standard_normal((M, K)))
+    Nb = 2 * N if epi == "swiglu" else N
+    B = _bf16_dev(rng.standard_normal((E, K, Nb) if op == "nn" else (E, Nb, K)) * (0.5 / np.sqrt(K)))
+    w = rng.random(M).astype(np.float32)
+    h = (rng.standard_normal((M, 2 * N)) * 0.5).astype(np.float32)
+    got = moe.grouped_gemm(A, B, torch.from_numpy(off).to(DEV), op=op, epilogue=epi,
+                           aux_in=torch.from_numpy(h).to(DEV) if epi == "swiglu_bwd" else None,
+                           slot_scale=torch.from_numpy(w).to(DEV))
+    A_rows = bf16_values(bits(A)) * w.astype(np.float64)[:, None]
+    ref = oracle.grouped_gemm(0 if op == "nn" else 1, {"none": 0, "swiglu": 1, "swiglu_bwd": 2}[epi],
+                              np.ascontiguousarray(A_rows), bits(B), off, aux=h if epi == "swiglu_bwd" else None,
+                              real="f64")
+    assert_close(to_np(got), ref, f"{op}/{epi}")
+
+
 def test_grouped_gemm_rows_past_last_group_untouched():
     M, K, N, E = 600, 128, 256, 3
     off = np.array([0, 100, 100, 450], np.int32)  # rows 450.. belong to no group
