@@ -382,7 +382,7 @@ __global__ __launch_bounds__(GTHR, 1) void gemm_kernel(GemmP p) {
         for (int f = 0; f < 2; ++f) acc[i][f] = mfma(bf[set][f], af[set][i], acc[i][f]);
     };
     // Issue order inside a 16-wide sub-slice: one MFMA, then one LDS read of the
-    // next sub-slice's fragments (two per MFMA with two row blocks).
+    // next sub-slice's fragments (two per MFMA with two row blocks, three with one).
     auto interleave = [&](auto NIc) {
       constexpr int NI = decltype(NIc)::value;
 #pragma unroll
